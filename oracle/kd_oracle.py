@@ -1,0 +1,361 @@
+"""fp64 CPU oracle for full-vocabulary logit distillation from hidden states.
+
+TEST INFRASTRUCTURE. Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import, call or execute anything in
+this directory. The product package never does, and this module imports
+nothing from it: the two share no code.
+
+What is computed follows the plain definitions, written out on materialised
+full logit rows (the GPU path reaches the same numbers by streaming vocabulary
+blocks; chunking and an online log-sum-exp are exact re-associations of these
+sums). Sources, cited by page title and section:
+
+* [Nitrobrew notes]  ricardokevins notes, "Nitrobrew tweet analysis":
+  section "Nitrobrew 的两个动作" (logits z = h W^T rebuilt per vocabulary block,
+  online softmax / log-sum-exp and KL accumulators), "仓库实现" (forward-KL
+  gradient "p - q", reverse-KL gradient "p (log p - log q - KL)", with p the
+  student there), the ``forward_kl`` / ``reverse_kl`` listing under "VeRL PR"
+  (student/teacher hidden states, both unembeddings, temperature; gradients
+  reach the student only).
+* [White-box OPD]  ars-opd-rebuild "03 · 层 2：White-box OPD 基线": section 2.3
+  (the beta table: beta=0 KL(teacher||student), beta=1 KL(student||teacher),
+  0<beta<1 beta*KL(teacher||m) + (1-beta)*KL(student||m) with
+  m = (1-beta)*student + beta*teacher; temperature divides logits before the
+  softmax; log-domain arithmetic, logsumexp for the mixture; per-token mean),
+  section 2.4 (tail bucket log(1 - sum of top-k probabilities)), section 6
+  (CPU test plan).
+* [Top-K KD]  lpnh.cn "Top-K知识蒸馏损失实现详解": section 一.2 (binary KL on the
+  mass inside/outside the top-k set, conditional KL on the renormalised shape
+  inside it, CE anchor on the true token), section 二.1 (bf16 logits, fp32 only
+  for log-sum-exp accumulators), section 二.2 (gather the top-64 in bf16, then
+  upcast only those values).
+
+Readings where the pages leave a step open are marked READING in the
+docstrings; every function carries its pins in tests/test_oracle_*.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "as_f64", "bf16_round", "bf16_neighbours", "logits", "lse", "log_softmax", "divergence",
+    "kd_fwd", "grad_student_logits", "kd_bwd", "topk_order", "topk_three_terms", "kd_topk_fwd",
+    "fp32_dot_error_bound", "svd_teacher", "log1mexp",
+]
+
+_SLAB = 8192  # vocabulary rows converted to fp64 at a time (memory only)
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+def as_f64(x) -> np.ndarray:
+    """Decode an input array to float64 exactly.
+
+    uint16 arrays are bf16 bit patterns (sign, 8 exponent bits, 7 mantissa
+    bits: the upper half of an IEEE float32); float32/float64 are widened."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+_BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+_BF16_MIN_EXP = -133  # exponent of the smallest bf16 subnormal
+
+
+def _bf16_quantum_exp(x: np.ndarray) -> np.ndarray:
+    # bf16 keeps 8 significant bits: a value in [2^(e-1), 2^e) is a multiple of 2^(e-8).
+    _, e = np.frexp(x)
+    return np.maximum(e - 8, _BF16_MIN_EXP)
+
+
+def bf16_round(x) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value (ties to even), directly
+    from float64 (no intermediate float32 rounding, which could round twice).
+    Returns the rounded values as float64. [Top-K KD, 二.1: logits are kept in
+    bf16.]"""
+    x = np.asarray(x, dtype=np.float64)
+    qe = _bf16_quantum_exp(x)
+    r = np.ldexp(np.rint(np.ldexp(x, -qe)), qe)  # scaling by 2^k is exact; rint ties to even
+    # values that round past the largest finite bf16 become infinities
+    limit = _BF16_MAX + 2.0 ** 119  # midpoint between max finite and the next (overflowing) step
+    r = np.where(np.abs(x) >= limit, np.copysign(np.inf, x), r)
+    return r
+
+
+def bf16_neighbours(x):
+    """For each float64 value: the two bf16 values around it and the midpoint
+    between them. Returns (lo, hi, mid) with lo <= x <= hi."""
+    x = np.asarray(x, dtype=np.float64)
+    qe = _bf16_quantum_exp(x)
+    y = np.ldexp(x, -qe)
+    lo = np.ldexp(np.floor(y), qe)
+    hi = np.ldexp(np.ceil(y), qe)
+    hi = np.where(hi == lo, np.ldexp(np.floor(y) + 1.0, qe), hi)
+    return lo, hi, 0.5 * (lo + hi)
+
+
+def fp32_dot_error_bound(h, W, factor: float = 8.0):
+    """A statistical bound on |fp32-accumulated dot - exact dot| for every logit:
+    factor * sqrt(d) * 2^-24 * sum_i |h_i W_i|  ([rows, V] float64).
+
+    READING: the kernel accumulates bf16 products in float32 in an order the
+    pages do not fix, so a logit lying within this distance of a bf16 rounding
+    midpoint may round either way on the GPU; only such logits may make the
+    top-k selection differ from this oracle's."""
+    hh = np.abs(as_f64(h))
+    d = hh.shape[1]
+    out = np.empty((hh.shape[0], W.shape[0]))
+    for v0 in range(0, W.shape[0], _SLAB):
+        out[:, v0:v0 + _SLAB] = hh @ np.abs(as_f64(W[v0:v0 + _SLAB])).T
+    return factor * np.sqrt(d) * 2.0 ** -24 * out
+
+
+# ---------------------------------------------------------------------------
+# logits and log-softmax
+# ---------------------------------------------------------------------------
+def logits(h, W) -> np.ndarray:
+    """z[n, v] = sum_i h[n, i] W[v, i] in float64, over the whole vocabulary.
+
+    [Nitrobrew notes, "Nitrobrew 的两个动作": the logits are h times the
+    unembedding transposed; the method rebuilds them block by block, here all
+    of V is one block.] bf16 x bf16 products are exact in float64 and the
+    sums of at most a few thousand terms carry ~1e-16 relative error."""
+    h64 = as_f64(h)
+    V = W.shape[0]
+    z = np.empty((h64.shape[0], V))
+    for v0 in range(0, V, _SLAB):  # conversion in slabs bounds host memory only
+        z[:, v0:v0 + _SLAB] = h64 @ as_f64(W[v0:v0 + _SLAB]).T
+    return z
+
+
+def lse(x) -> np.ndarray:
+    """Natural-log log-sum-exp over the last axis: max + log sum exp(x - max)."""
+    x = np.asarray(x, dtype=np.float64)
+    m = np.max(x, axis=-1, keepdims=True)
+    return m[..., 0] + np.log(np.sum(np.exp(x - m), axis=-1))
+
+
+def log_softmax(x) -> np.ndarray:
+    """log softmax(x) = x - lse(x) over the last axis. [White-box OPD, 2.3:
+    everything stays in the log domain.]"""
+    x = np.asarray(x, dtype=np.float64)
+    return x - lse(x)[..., None]
+
+
+def log1mexp(a):
+    """log(1 - exp(a)) for a <= 0, in the numerically stable two-branch form
+    (expm1 near 0, log1p far from it); -inf at a == 0."""
+    a = np.asarray(a, dtype=np.float64)
+    with np.errstate(divide="ignore"):
+        return np.where(a > -np.log(2.0), np.log(-np.expm1(a)), np.log1p(-np.exp(a)))
+
+
+# ---------------------------------------------------------------------------
+# divergences (forward pass)
+# ---------------------------------------------------------------------------
+def divergence(s, t, beta: float):
+    """Per-row beta-divergence between the student distribution q = softmax(s)
+    and the teacher distribution p = softmax(t) (s, t: tempered logits).
+
+    [White-box OPD, 2.3, the beta table]
+      beta = 0 : KL(p || q)                       (forward, teacher first)
+      beta = 1 : KL(q || p)                       (reverse, student first)
+      else     : beta KL(p || m) + (1-beta) KL(q || m),  m = beta p + (1-beta) q,
+                 log m taken with logaddexp (log-domain mixture).
+    READING: the endpoints are taken piecewise, as the page's table lists them
+    (the mixture formula itself tends to 0 at both ends).
+
+    Returns (loss, aux): aux is the centring scalar of the gradient:
+    KL(q || m) for 0 < beta < 1, the loss itself otherwise."""
+    lq = log_softmax(s)
+    lp = log_softmax(t)
+    q = np.exp(lq)
+    p = np.exp(lp)
+    if beta == 0.0:
+        loss = np.sum(p * (lp - lq), axis=-1)
+        return loss, loss.copy()
+    if beta == 1.0:
+        loss = np.sum(q * (lq - lp), axis=-1)
+        return loss, loss.copy()
+    if not (0.0 < beta < 1.0):
+        raise ValueError("beta must lie in [0, 1]")
+    lm = np.logaddexp(np.log(beta) + lp, np.log1p(-beta) + lq)
+    kl_pm = np.sum(p * (lp - lm), axis=-1)
+    kl_qm = np.sum(q * (lq - lm), axis=-1)
+    return beta * kl_pm + (1.0 - beta) * kl_qm, kl_qm
+
+
+def kd_fwd(h_s, W_s, h_t, W_t, beta: float, tau: float):
+    """Per-token forward outputs for the rows of h_s / h_t.
+
+    s = z_s / tau, t = z_t / tau ([White-box OPD, 2.3]: the temperature divides
+    the logits before the softmax). READING: no tau^2 factor is applied.
+    Returns dict(loss, lse_s, lse_t, aux) with lse_* = LSE of the tempered
+    logits (natural log)."""
+    if tau <= 0:
+        raise ValueError("tau must be positive")
+    s = logits(h_s, W_s) / tau
+    t = logits(h_t, W_t) / tau
+    loss, aux = divergence(s, t, beta)
+    return dict(loss=loss, lse_s=lse(s), lse_t=lse(t), aux=aux)
+
+
+# ---------------------------------------------------------------------------
+# gradient (backward pass)
+# ---------------------------------------------------------------------------
+def grad_student_logits(s, t, beta: float) -> np.ndarray:
+    """dL/ds for each row, s = tempered student logits.
+
+    Derived from the definitions in ``divergence`` (and pinned by finite
+    differences in the tests); the first two agree with [Nitrobrew notes,
+    "仓库实现"] once its letters are read as p = student, q = teacher:
+      beta = 0 : q - p
+      beta = 1 : q (log q - log p - KL(q||p))
+      else     : (1 - beta) q (log q - log m - KL(q||m))"""
+    lq = log_softmax(s)
+    lp = log_softmax(t)
+    q = np.exp(lq)
+    if beta == 0.0:
+        return q - np.exp(lp)
+    if beta == 1.0:
+        kl = np.sum(q * (lq - lp), axis=-1, keepdims=True)
+        return q * (lq - lp - kl)
+    lm = np.logaddexp(np.log(beta) + lp, np.log1p(-beta) + lq)
+    kl_qm = np.sum(q * (lq - lm), axis=-1, keepdims=True)
+    return (1.0 - beta) * q * (lq - lm - kl_qm)
+
+
+def kd_bwd(h_s, W_s, h_t, W_t, beta: float, tau: float, grad_loss=None) -> np.ndarray:
+    """dL/dh_s[n, :] = grad_loss[n] * sum_v (g[n, v] / tau) W_s[v, :].
+
+    The teacher receives no gradient ([Nitrobrew notes, "仓库实现"]). The
+    chain rule through s = z_s / tau contributes the 1/tau."""
+    s = logits(h_s, W_s) / tau
+    t = logits(h_t, W_t) / tau
+    g = grad_student_logits(s, t, beta) / tau
+    if grad_loss is not None:
+        g = g * np.asarray(grad_loss, dtype=np.float64)[:, None]
+    out = np.zeros((g.shape[0], W_s.shape[1]))
+    for v0 in range(0, W_s.shape[0], _SLAB):
+        out += g[:, v0:v0 + _SLAB] @ as_f64(W_s[v0:v0 + _SLAB])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# top-k three-term decomposition
+# ---------------------------------------------------------------------------
+def topk_order(keys, k: int) -> np.ndarray:
+    """Indices of the k largest keys of each row, ordered by (key descending,
+    vocabulary index ascending). READING: the pages fix no tie rule; bf16
+    keys tie often at the k-th slot, so the lower index wins."""
+    keys = np.asarray(keys, dtype=np.float64)
+    V = keys.shape[-1]
+    idx = np.arange(V)
+    out = np.empty((keys.shape[0], k), dtype=np.int64)
+    for r in range(keys.shape[0]):
+        order = np.lexsort((idx, -keys[r]))  # last key is primary
+        out[r] = order[:k]
+    return out
+
+
+def topk_three_terms(zs_b, zt_b, sel, tau: float, labels=None):
+    """Three-term decomposition given bf16-rounded logits and the selection.
+
+    [Top-K KD, 一.2] binary KL: how much teacher mass falls inside the top-k
+    set versus outside; conditional KL: the shape inside the set after
+    renormalising; CE anchor: cross-entropy of the student on the true token.
+    READING: both KLs are teacher-first (forward), the terms are returned
+    separately, log(1 - P) is taken as log1mexp(LSE_K - LSE_V), and the CE
+    uses the untempered student logits (tau = 1).
+    ``sel`` [rows, k] holds the selected vocabulary indices."""
+    rows = np.arange(zs_b.shape[0])[:, None]
+    s = zs_b / tau
+    t = zt_b / tau
+    L_s = lse(s)
+    L_t = lse(t)
+    sK = s[rows, sel]
+    tK = t[rows, sel]
+    LK_s = lse(sK)
+    LK_t = lse(tK)
+    logP = LK_t - L_t
+    logQ = LK_s - L_s
+    P = np.exp(logP)
+    Q = np.exp(logQ)
+    log1P = log1mexp(np.minimum(logP, 0.0))
+    log1Q = log1mexp(np.minimum(logQ, 0.0))
+    with np.errstate(invalid="ignore"):
+        tail = np.where(1.0 - P > 0.0, (1.0 - P) * (log1P - log1Q), 0.0)
+    binary = P * (logP - logQ) + tail
+    lpK = tK - LK_t[:, None]  # log of the renormalised teacher inside the set
+    lqK = sK - LK_s[:, None]
+    cond = np.sum(np.exp(lpK) * (lpK - lqK), axis=-1)
+    out = dict(binary=binary, cond=cond, p_mass=P, q_mass=Q, lse_s=L_s, lse_t=L_t)
+    if labels is not None:
+        lab = np.asarray(labels, dtype=np.int64)
+        valid = lab != -100
+        L_s1 = lse(zs_b)
+        ce = np.full(zs_b.shape[0], np.nan)
+        ce[valid] = L_s1[valid] - zs_b[np.arange(zs_b.shape[0])[valid], lab[valid]]
+        out["ce"] = ce
+    return out
+
+
+def kd_topk_fwd(h_s, W_s, h_t, W_t, k: int, tau: float, labels=None, with_bound: bool = False):
+    """Top-k three-term KD for the given rows.
+
+    Steps ([Top-K KD, 二.1 and 二.2]): round both models' logits to bf16
+    (straight from the exact value), pick the teacher's top-k by
+    (bf16 key desc, index asc), and evaluate the three terms over full-vocab
+    log-sum-exps of the bf16 logits. Returns the dict of ``topk_three_terms``
+    plus ``idx`` [rows, k], ``val_t`` (the selected bf16 teacher logits) and,
+    with ``with_bound``, the exact teacher logits and their fp32 error bound
+    (for judging selections at bf16 rounding midpoints)."""
+    zs = logits(h_s, W_s)
+    zt = logits(h_t, W_t)
+    zs_b = bf16_round(zs)
+    zt_b = bf16_round(zt)
+    sel = topk_order(zt_b, k)
+    out = topk_three_terms(zs_b, zt_b, sel, tau, labels)
+    rows = np.arange(zt.shape[0])[:, None]
+    out["idx"] = sel
+    out["val_t"] = zt_b[rows, sel]
+    if with_bound:
+        out["zt_exact"] = zt
+        out["zt_bound"] = fp32_dot_error_bound(h_t, W_t)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# rank-r teacher (spectral compression of the hidden state)
+# ---------------------------------------------------------------------------
+def svd_teacher(h_t, W_t, r: int, method: str = "svd"):
+    """Rank-r factorisation of the teacher's logit map.
+
+    [Nitrobrew notes, thread part 6/8: spectral compression sends a rank-k
+    version of the hidden state instead of d_model floats; not lossless.]
+    With W_t = U S V^T (thin SVD), the compressed teacher is
+    W~ = U_r [V, r] and h~ = h_t V_r S_r [N, r], so that h~ W~^T = U_r U_r^T z_t
+    (the teacher logits projected on the top-r left singular subspace).
+
+    ``method="gram"`` takes the same factors from the eigendecomposition of
+    the d x d Gram matrix W^T W = V S^2 V^T and U_r = W V_r S_r^-1 (cheaper for
+    V >> d; adequate for the leading singular values).
+    Returns (h~, W~, singular values in descending order) in float64."""
+    W = as_f64(W_t)
+    if method == "svd":
+        U, S, Vt = np.linalg.svd(W, full_matrices=False)
+        Vr = Vt[:r].T
+        W_r = U[:, :r]
+    elif method == "gram":
+        G = W.T @ W
+        evals, evecs = np.linalg.eigh(G)
+        order = np.argsort(evals)[::-1]
+        S = np.sqrt(np.maximum(evals[order], 0.0))
+        Vr = evecs[:, order[:r]]
+        W_r = (W @ Vr) / S[:r]
+    else:
+        raise ValueError(method)
+    h_r = as_f64(h_t) @ (Vr * S[:r])
+    return h_r, W_r, S
