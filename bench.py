@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused chunked-KL hot path on one MI355X.
+
+One step = kd_fwd + kd_bwd (reverse KL, beta = 1, tau = 2) over one batch of
+the 152k-vocabulary, 32k-token workload (N = 32768 tokens, V = 151936,
+d_s = 2560, d_t = 4096, bf16 inputs, fp32 accumulation), inputs resident in
+HBM. Prints one JSON line with whole-job tokens/s, the MFMA fraction of the
+step, the roofline of the dominant kernel (the forward sweep, timed with HIP
+events on its own stream) and the fp64 CPU oracle timed on a bounded sample
+of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk-v C] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+WORKLOAD = 3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--chunk-v", type=int, default=8192)
+    ap.add_argument("--beta", type=float, default=1.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    return ap.parse_args()
+
+
+def cpu_baseline(w, beta, rows_n):
+    """The fp64 oracle (as it stands) on a bounded row sample of the same
+    workload: forward loss plus dL/dh_s for ``rows_n`` tokens."""
+    import numpy as np
+
+    import kdsynth
+    from oracle import kd_oracle as O
+    rows = kdsynth.sample_rows(w.N, rows_n, seed=99)
+    t0 = time.perf_counter()
+    O.kd_fwd(w.h_s[rows], w.W_s, w.h_t[rows], w.W_t, beta, w.tau)
+    O.kd_bwd(w.h_s[rows], w.W_s, w.h_t[rows], w.W_t, beta, w.tau)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {w.N} tokens of the same workload (fwd loss + dL/dh_s, fp64 numpy/BLAS), "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU: "
+              "no sharding or collectives are built)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import kdsynth
+    import vocab_chunked_kl_amd as kd
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    kd.load_library()
+    torch.cuda.set_device(0)
+    w = kdsynth.make(WORKLOAD)
+    N, V, ds, dt_, tau, beta = w.N, w.V, w.d_s, w.d_t, w.tau, args.beta
+    dev = [to_dev(x) for x in (w.h_s, w.W_s, w.h_t, w.W_t)]
+    stream = torch.cuda.Stream()
+    fws = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt_, kd.KD_BF16, beta=beta)
+    bws = kd.workspace_size(kd.KD_OP_BWD, N, V, ds, dt_, kd.KD_BF16, beta=beta, chunk_V=args.chunk_v)
+    with torch.cuda.stream(stream):
+        ws_f = torch.empty(fws, dtype=torch.uint8, device="cuda")
+        ws_b = torch.empty(bws, dtype=torch.uint8, device="cuda")
+        dh = torch.empty(N, ds, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    base_mem = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        loss, lse_s, lse_t, aux = kd.kd_fwd(*dev, beta, tau, workspace=ws_f, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        kd.kd_bwd(*dev, beta, tau, lse_s, lse_t, aux, chunk_V=args.chunk_v, workspace=ws_b, stream=stream, dh=dh)
+        return loss
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        t_start.record(stream)
+        for i in range(args.steps):
+            loss = step(evs[i])
+        t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    fwd_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    peak_extra = torch.cuda.max_memory_allocated() - base_mem
+    assert np.isfinite(loss.float().cpu().numpy()).all()
+
+    fwd_flops = 2.0 * N * V * (ds + dt_)
+    bwd_flops = 2.0 * N * V * (ds + dt_) + 2.0 * N * V * ds
+    jsd = 0.0 < beta < 1.0
+    step_flops = fwd_flops * (2 if jsd else 1) + bwd_flops
+    tok_s = N / (ms_step / 1e3)
+    achieved = fwd_flops * (2 if jsd else 1) / (fwd_ms / 1e3) / 1e12
+    traffic = None
+    if os.path.exists(args.traffic):
+        try:
+            with open(args.traffic) as f:
+                tr = json.load(f)
+            if tr.get("kernel_source_hash") == kernel_hash():
+                traffic = tr.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+    out = {
+        "metric": "tokens/s + MFMA % of peak for fused chunked KL fwd+bwd, V=151936, N=32k",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: N={N} tokens (B=4 x T=8192), V={V}, d_s={ds}, d_t={dt_}, "
+                               f"beta={beta}, tau={tau}, fwd+bwd (dL/dh_s), chunk_V={args.chunk_v}",
+                   "global_batch": N, "seq_len": 8192, "parallelism": "single GPU"},
+        "mfma_frac_step": round(step_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "step_tflops": round(step_flops / (ms_step / 1e3) / 1e12, 1),
+        "fwd_ms": round(fwd_ms, 3),
+        "bwd_ms": round(ms_step - fwd_ms, 3),
+        "workspace_bytes": {"fwd": fws, "bwd": bws, "peak_alloc_delta": int(peak_extra)},
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"kernel": "fwd_kernel (forward sweep: both logit GEMMs + online LSE/KL)",
+                     "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu:
+        del dev
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(w, beta, args.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+def kernel_hash() -> str:
+    """Hash of the kernel sources; traffic counters are only valid for the
+    sources they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "vocab_chunked_kl_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

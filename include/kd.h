@@ -1,0 +1,164 @@
+/*
+ * kd.h - C ABI of the fused chunked-KL distillation library (libkd.so).
+ *
+ * Full-vocabulary logit distillation computed straight from hidden states:
+ * the library rebuilds the student and teacher logits z = h W^T one
+ * vocabulary tile at a time on the GPU (bf16 MFMA, fp32 accumulation) and
+ * reduces them with online log-sum-exp and divergence accumulators, so no
+ * [tokens, V] logit tensor is ever written to memory.
+ *   Source: ricardokevins notes, "Nitrobrew tweet analysis", section
+ *   "Nitrobrew 的两个动作" (rebuild logits per vocabulary block, update online
+ *   softmax / log-sum-exp accumulators and KL terms, discard the block) and
+ *   the forward_kl / reverse_kl listing under "VeRL PR" (inputs: student and
+ *   teacher hidden states, both unembeddings, temperature, chunk size).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked (device) are device pointers on the current HIP device,
+ *     owned by the caller; the library allocates no device memory. Scratch
+ *     memory is the caller's `workspace`, sized by kd_workspace_size().
+ *   - Layout: row-major and contiguous. h_s [N, d_s], h_t [N, d_t] hold one
+ *     token per row ([B, T, D] flattened); W_s [V, d_s], W_t [V, d_t] hold one
+ *     vocabulary entry per row (the nn.Linear weight layout). Inputs must be
+ *     16-byte aligned and d_s, d_t multiples of 8 (else KD_ERR_UNSUPPORTED).
+ *     V is arbitrary (vocabulary tails are masked, never read as logit 0).
+ *   - dtype: KD_BF16 (uint16 bf16 bit patterns) or KD_F32, for all four of
+ *     h_s, W_s, h_t, W_t alike.
+ *   - Temperature: s = z_s / tau, t = z_t / tau before any softmax; q = softmax(s)
+ *     is the student, p = softmax(t) the teacher. No tau^2 factor is applied.
+ *     (ars-opd-rebuild "03 · 层 2：White-box OPD 基线", section 2.3.)
+ *   - Outputs are per token ("reduction none"); mean/sum over valid tokens is
+ *     the caller's (the same section: a per-token mean over non-ignored labels).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     is asynchronous; nothing blocks the host. Argument checks run on the host
+ *     before any HIP call and return KD_ERR_INVALID_ARG / KD_ERR_UNSUPPORTED /
+ *     KD_ERR_WORKSPACE without touching the GPU; a failed launch returns
+ *     KD_ERR_HIP. Calls on different streams with different workspaces may run
+ *     concurrently; calls sharing a workspace must be ordered by the caller.
+ *   - Results do not depend on chunk_V beyond fp32 rounding.
+ */
+#ifndef KD_H_
+#define KD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KD_OK = 0,
+  KD_ERR_INVALID_ARG = 1, /* null required pointer, N <= 0, V < 2, beta outside [0,1], tau <= 0, ... */
+  KD_ERR_UNSUPPORTED = 2, /* d not a multiple of 8, misaligned pointer, unknown dtype */
+  KD_ERR_WORKSPACE = 3,   /* ws_bytes smaller than kd_workspace_size() */
+  KD_ERR_HIP = 4          /* a HIP launch or runtime call failed */
+} kd_status;
+
+typedef enum { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
+
+typedef enum { KD_OP_FWD = 0, KD_OP_BWD = 1, KD_OP_TOPK = 2 } kd_op;
+
+/* Largest k accepted by kd_topk_fwd. */
+#define KD_TOPK_MAX 128
+
+/*
+ * kd_workspace_size - device workspace (bytes) that `op` needs for this shape.
+ *   op: KD_OP_FWD (kd_fwd), KD_OP_BWD (kd_bwd) or KD_OP_TOPK (kd_topk_fwd).
+ *   beta is read for KD_OP_FWD/KD_OP_BWD, chunk_V for KD_OP_BWD, k for
+ *   KD_OP_TOPK; d_s/d_t/dtype size the backward's per-chunk buffers.
+ *   The backward's workspace is O(N * chunk_V) (the gradient tile G of one
+ *   vocabulary chunk, bf16) plus O(chunk_V * d_s) for one transposed chunk of
+ *   W_s; the forward's is O(N * V / vocab_split) floats of partial statistics.
+ *   Writes the size to *bytes (host pointer). Pure host function.
+ */
+kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t d_t, kd_dtype dtype,
+                            float beta, int32_t chunk_V, int32_t k, size_t* bytes);
+
+/*
+ * kd_fwd - per-token beta-divergence between student and teacher.
+ *   Source: ars-opd-rebuild "03 · 层 2：White-box OPD 基线", section 2.3 (beta
+ *   table): beta = 0 gives KL(p || q) (forward, teacher first), beta = 1 gives
+ *   KL(q || p) (reverse, student first), 0 < beta < 1 gives
+ *   beta KL(p || m) + (1 - beta) KL(q || m) with m = beta p + (1 - beta) q.
+ *   Blockwise online reduction per "Nitrobrew 的两个动作" (Nitrobrew notes).
+ *
+ *   h_s, W_s, h_t, W_t (device, read): inputs as described above.
+ *   N tokens, V vocabulary entries, d_s / d_t hidden sizes.
+ *   beta in [0, 1]; tau > 0.
+ *   loss  (device, [N] fp32, written): the divergence of each token.
+ *   lse_s, lse_t (device, [N] fp32, written): natural-log log-sum-exp of the
+ *         tempered student / teacher logits (kd_bwd consumes them).
+ *   aux   (device, [N] fp32, written; may be NULL when beta == 0): the
+ *         gradient's centring scalar: KL(q || m) for 0 < beta < 1, the loss
+ *         itself for beta == 1.
+ *   workspace (device, >= kd_workspace_size(KD_OP_FWD, ...) bytes): scratch.
+ */
+kd_status kd_fwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
+                 int32_t d_s, int32_t d_t, float beta, float tau, kd_dtype dtype, float* loss, float* lse_s,
+                 float* lse_t, float* aux, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * kd_bwd - gradient of sum_n grad_loss[n] * loss[n] with respect to h_s.
+ *   Source: Nitrobrew notes, "仓库实现": the gradient is recomputed block by
+ *   block instead of storing logits; only the student receives a gradient.
+ *   With g = dloss/ds (s the tempered student logits):
+ *     beta = 0:  g = q - p
+ *     beta = 1:  g = q (log q - log p - KL(q || p))
+ *     else:      g = (1 - beta) q (log q - log m - KL(q || m))
+ *   dh_s[n, :] = grad_loss[n] * sum_v (g[n, v] / tau) W_s[v, :].
+ *
+ *   lse_s, lse_t, aux (device, [N] fp32, read): as written by kd_fwd with the
+ *         same inputs, beta and tau (aux unused when beta == 0, may be NULL).
+ *   grad_loss (device, [N] fp32, read; NULL means all ones).
+ *   chunk_V: vocabulary entries per recompute chunk (a positive multiple of
+ *         256); the workspace holds one [N, chunk_V] bf16 gradient chunk.
+ *   dh_s  (device, [N, d_s] fp32, overwritten).
+ */
+kd_status kd_bwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
+                 int32_t d_s, int32_t d_t, float beta, float tau, kd_dtype dtype, int32_t chunk_V,
+                 const float* lse_s, const float* lse_t, const float* aux, const float* grad_loss, float* dh_s,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * kd_topk_fwd - top-k three-term decomposition over bf16 logits.
+ *   Source: lpnh.cn "Top-K知识蒸馏损失实现详解", section 一.2 (binary KL on the
+ *   teacher mass inside vs outside the top-k set; conditional KL on the shape
+ *   inside the set after renormalising; CE anchor on the true token) and
+ *   sections 二.1 / 二.2 (logits in bf16, fp32 only for the log-sum-exp
+ *   accumulators; the top-64 gathered in bf16 and only those upcast).
+ *   Both models' logits are rounded to bf16 (nearest, ties to even); the
+ *   teacher's top-k is taken by (bf16 logit descending, vocabulary index
+ *   ascending); all sums are fp32 over the bf16 values. Only KD_BF16 inputs.
+ *   With P = sum_K p, Q = sum_K q (tempered):
+ *     binary_kl = P log(P/Q) + (1-P) log((1-P)/(1-Q))
+ *     cond_kl   = sum_K (p/P) (log(p/P) - log(q/Q))
+ *     ce        = logsumexp(z_s) - z_s[label]   (untempered student, bf16)
+ *
+ *   k in [1, min(V, KD_TOPK_MAX)].
+ *   labels   (device, [N] int32, read; may be NULL): -100 marks an ignored
+ *            token (its ce is written as NaN); other values must lie in [0, V).
+ *   topk_idx (device, [N, k] int32, written): the selection, in order.
+ *   topk_val (device, [N, k] fp32, written; may be NULL): the bf16 teacher
+ *            logits (untempered) at topk_idx.
+ *   binary_kl, cond_kl, p_mass, q_mass, lse_s, lse_t (device, [N] fp32,
+ *            written): lse_* over the tempered bf16 logits.
+ *   ce       (device, [N] fp32, written when labels != NULL; may be NULL).
+ */
+kd_status kd_topk_fwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
+                      int32_t d_s, int32_t d_t, int32_t k, float tau, kd_dtype dtype, const int32_t* labels,
+                      int32_t* topk_idx, float* topk_val, float* binary_kl, float* cond_kl, float* ce,
+                      float* p_mass, float* q_mass, float* lse_s, float* lse_t, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/* kd_status_string - a static, human-readable name for a status code. */
+const char* kd_status_string(kd_status s);
+
+/* kd_last_error - a static description of the most recent failure on the
+ * calling thread (argument name or HIP error string); "" if none. */
+const char* kd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KD_H_ */

@@ -1,0 +1,95 @@
+"""The C-ABI library loads, exports every symbol include/kd.h declares, and
+rejects bad arguments on the host before any HIP call (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "vocab_chunked_kl_amd", "libkd.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libkd.so not built (run __graft_entry__.build())")
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "kd.h")).read()
+    return sorted(set(re.findall(r"^(?:kd_status|const char\*)\s+(kd_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_symbols_exported():
+    import vocab_chunked_kl_amd as kd
+    lib = kd.load_library()
+    names = header_symbols()
+    assert set(names) == set(kd.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    import vocab_chunked_kl_amd as kd
+    lib = kd.load_library()
+    assert lib.kd_status_string(0) == b"KD_OK"
+    assert lib.kd_status_string(3) == b"KD_ERR_WORKSPACE"
+
+
+def test_workspace_sizes():
+    import vocab_chunked_kl_amd as kd
+    # backward workspace = one bf16 gradient chunk [N, chunk_V] + one transposed W_s chunk [d_s, chunk_V]
+    N, V, ds, dt = 32768, 151936, 2560, 4096
+    for cv in (2048, 8192):
+        b = kd.workspace_size(kd.KD_OP_BWD, N, V, ds, dt, kd.KD_BF16, chunk_V=cv)
+        assert b == N * cv * 2 + ds * cv * 2
+    f1 = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt, kd.KD_BF16, beta=1.0)
+    f5 = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt, kd.KD_BF16, beta=0.5)
+    assert 0 < f1 < f5 < 64 << 20
+    with pytest.raises(kd.KDError):
+        kd.workspace_size(kd.KD_OP_BWD, N, V, ds, dt, kd.KD_BF16, chunk_V=1000)
+    with pytest.raises(kd.KDError):
+        kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt, kd.KD_BF16, beta=1.5)
+    with pytest.raises(kd.KDError):
+        kd.workspace_size(kd.KD_OP_TOPK, N, V, ds, dt, kd.KD_BF16, k=0)
+
+
+FAKE = 0x10000  # aligned non-null address: never dereferenced, every call below fails validation first
+
+
+def call_fwd(lib, **kw):
+    a = dict(h_s=FAKE, W_s=FAKE, h_t=FAKE, W_t=FAKE, N=8, V=100, d_s=64, d_t=64, beta=1.0, tau=1.0, dtype=1,
+             loss=FAKE, lse_s=FAKE, lse_t=FAKE, aux=FAKE, ws=FAKE, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.kd_fwd(*[a[k] for k in ("h_s", "W_s", "h_t", "W_t", "N", "V", "d_s", "d_t", "beta", "tau", "dtype",
+                                       "loss", "lse_s", "lse_t", "aux", "ws", "ws_bytes", "stream")])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(h_s=None), 1), (dict(N=0), 1), (dict(V=1), 1), (dict(beta=1.5), 1), (dict(beta=-0.1), 1),
+    (dict(tau=0.0), 1), (dict(tau=float("nan")), 1), (dict(d_s=60), 2), (dict(dtype=7), 2),
+    (dict(W_t=FAKE + 2), 2), (dict(loss=None), 1), (dict(aux=None, beta=0.5), 1), (dict(ws_bytes=10), 3),
+    (dict(ws=None, ws_bytes=1 << 30), 3),
+])
+def test_fwd_validation(kw, code):
+    import vocab_chunked_kl_amd as kd
+    lib = kd.load_library()
+    assert call_fwd(lib, **kw) == code
+
+
+def test_bwd_and_topk_validation():
+    import vocab_chunked_kl_amd as kd
+    lib = kd.load_library()
+    args = [FAKE, FAKE, FAKE, FAKE, 8, 100, 64, 64, 1.0, 1.0, 1]
+    # chunk_V not a multiple of 256
+    assert lib.kd_bwd(*args, 300, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None) == 1
+    # workspace too small
+    assert lib.kd_bwd(*args, 256, FAKE, FAKE, FAKE, None, FAKE, FAKE, 16, None) == 3
+    # missing dh
+    assert lib.kd_bwd(*args, 256, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == 1
+    targs = [FAKE, FAKE, FAKE, FAKE, 8, 100, 64, 64]
+    outs = [FAKE] * 9
+    # k out of range, fp32 inputs, labels without ce
+    assert lib.kd_topk_fwd(*targs, 0, 1.0, 1, None, *outs, FAKE, 1 << 40, None) == 1
+    assert lib.kd_topk_fwd(*targs, 200, 1.0, 1, None, *outs, FAKE, 1 << 40, None) == 1
+    assert lib.kd_topk_fwd(*targs, 8, 1.0, 0, None, *outs, FAKE, 1 << 40, None) == 2
+    o = list(outs)
+    o[4] = None  # ce
+    assert lib.kd_topk_fwd(*targs, 8, 1.0, 1, FAKE, *o, FAKE, 1 << 40, None) == 1

@@ -1,0 +1,149 @@
+"""GPU parity of kd_fwd / kd_bwd against the fp64 oracle (through the C ABI).
+
+Small cases compare every row and span several tiles with ragged tails
+(tokens, vocabulary and hidden sizes that are not tile multiples). The
+full-size workloads compare a seeded subset of rows (always the first and
+last) computed one by one by the oracle, in the launch configuration the
+benchmark uses. Tolerances (tests/helpers.py): per-token loss and LSEs
+|d| <= 1e-3 |ref| + 1e-5; dL/dh_s per row cosine >= 0.9999 and
+max|d| / max|ref| <= 2e-2.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import kdsynth
+from oracle import kd_oracle as O
+from tests.helpers import assert_close, assert_grad_rows, grad_floor, to_dev, upload, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _kd():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vocab_chunked_kl_amd as kd
+    kd.load_library()
+    return kd, torch
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(kd, torch, arrays, beta, tau, rows=None, grad=None, chunk_V=2048, check_bwd=True):
+    h_s, W_s, h_t, W_t = arrays
+    dev = [to_dev(x) for x in arrays]
+    loss, lse_s, lse_t, aux = kd.kd_fwd(*dev, beta, tau)
+    g = None if grad is None else torch.from_numpy(grad.astype(np.float32)).cuda()
+    dh = kd.kd_bwd(*dev, beta, tau, lse_s, lse_t, aux, grad_loss=g, chunk_V=chunk_V) if check_bwd else None
+    torch.cuda.synchronize()
+    sel = np.arange(h_s.shape[0]) if rows is None else rows
+    ref = O.kd_fwd(h_s[sel], W_s, h_t[sel], W_t, beta, tau)
+    assert_close("loss", loss.cpu().numpy()[sel], ref["loss"])
+    assert_close("lse_s", lse_s.cpu().numpy()[sel], ref["lse_s"])
+    assert_close("lse_t", lse_t.cpu().numpy()[sel], ref["lse_t"])
+    if beta > 0:
+        assert_close("aux", aux.cpu().numpy()[sel], ref["aux"])
+    if check_bwd:
+        gl = None if grad is None else grad[sel]
+        dref = O.kd_bwd(h_s[sel], W_s, h_t[sel], W_t, beta, tau, grad_loss=gl)
+        scale = 1.0 if gl is None else np.abs(gl)
+        floor = grad_floor(ref["lse_s"], ref["lse_t"], ref["loss"], W_s, tau) * scale
+        assert_grad_rows(dh.cpu().numpy()[sel], dref, floor=floor)
+    return loss, dh
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, 1.0])
+def test_tiny_fp32_workload(beta):
+    kd, torch = _kd()
+    w = workload(1)
+    _say(f"tiny fp32 N={w.N} V={w.V} d={w.d_s} beta={beta}")
+    run_case(kd, torch, (w.h_s, w.W_s, w.h_t, w.W_t), beta, w.tau)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("beta,tau", [(0.0, 1.0), (1.0, 1.0), (1.0, 2.0), (0.3, 1.5), (0.5, 2.0)])
+def test_ragged_small(dtype, beta, tau):
+    kd, torch = _kd()
+    # 3 token tiles (last ragged), 8 vocabulary tiles (last ragged), d_t not a multiple of 64
+    N, V, ds, dt = 300, 1000, 64, 200
+    arrays = kdsynth.small_case(11, N, V, ds, dt, dtype=dtype)
+    grad = np.random.default_rng(3).uniform(-1, 2, size=N)
+    grad[::7] = 0.0
+    _say(f"ragged {dtype} N={N} V={V} d_s={ds} d_t={dt} beta={beta} tau={tau}")
+    run_case(kd, torch, arrays, beta, tau, grad=grad, chunk_V=256)
+
+
+@pytest.mark.parametrize("N,V", [(1, 2), (1, 300), (129, 2), (65, 257)])
+def test_degenerate_shapes(N, V):
+    kd, torch = _kd()
+    arrays = kdsynth.small_case(5, N, V, 32, 48)
+    for beta in (0.0, 0.5, 1.0):
+        _say(f"degenerate N={N} V={V} beta={beta}")
+        run_case(kd, torch, arrays, beta, 1.0, chunk_V=256)
+
+
+def test_identical_distributions_give_zero():
+    kd, torch = _kd()
+    # teacher == student (same hidden state and unembedding): every divergence is 0
+    h, W, _, _ = kdsynth.small_case(6, 200, 3000, 128, 128)
+    dev = [to_dev(x) for x in (h, W, h, W)]
+    for beta in (0.0, 0.5, 1.0):
+        loss, lse_s, lse_t, aux = kd.kd_fwd(*dev, beta, 1.0)
+        torch.cuda.synchronize()
+        assert np.max(np.abs(loss.cpu().numpy())) < 2e-5
+        assert np.array_equal(lse_s.cpu().numpy(), lse_t.cpu().numpy())
+
+
+def test_beta_swap_symmetry_gpu():
+    kd, torch = _kd()
+    h_s, W_s, h_t, W_t = (to_dev(x) for x in kdsynth.small_case(7, 256, 2048, 128, 128))
+    for b in (0.0, 0.25, 0.5):
+        a = kd.kd_fwd(h_s, W_s, h_t, W_t, b, 1.0)[0]
+        c = kd.kd_fwd(h_t, W_t, h_s, W_s, 1.0 - b, 1.0)[0]
+        torch.cuda.synchronize()
+        assert np.allclose(a.cpu().numpy(), c.cpu().numpy(), rtol=2e-4, atol=2e-5)
+
+
+def test_backward_chunk_invariance():
+    kd, torch = _kd()
+    arrays = kdsynth.small_case(8, 384, 5000, 256, 128)
+    dev = [to_dev(x) for x in arrays]
+    loss, lse_s, lse_t, aux = kd.kd_fwd(*dev, 1.0, 1.0)
+    outs = [kd.kd_bwd(*dev, 1.0, 1.0, lse_s, lse_t, aux, chunk_V=c).cpu().numpy() for c in (256, 1024, 8192)]
+    for o in outs[1:]:
+        assert np.allclose(o, outs[0], rtol=1e-4, atol=1e-7)
+
+
+def test_workload_rkl_v152k_n4k_sampled():
+    kd, torch = _kd()
+    w = workload(2)
+    rows = kdsynth.sample_rows(w.N, 48)
+    _say(f"{w.name} N={w.N} V={w.V} rows={len(rows)}")
+    run_case(kd, torch, (w.h_s, w.W_s, w.h_t, w.W_t), 1.0, w.tau, rows=rows, chunk_V=8192)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, 1.0])
+def test_workload_jsd_sweep_v152k_n32k_sampled(beta):
+    kd, torch = _kd()
+    w = workload(3)
+    rows = kdsynth.sample_rows(w.N, 24)
+    _say(f"{w.name} N={w.N} V={w.V} beta={beta} rows={len(rows)}")
+    run_case(kd, torch, (w.h_s, w.W_s, w.h_t, w.W_t), beta, w.tau, rows=rows, chunk_V=8192)
+
+
+def test_workload_heavy_head_v248k_sampled():
+    kd, torch = _kd()
+    w = workload(4)
+    # rows whose argmax is a heavy vocabulary entry are the hardest for the LSE range
+    h = kdsynth.bf16_bits_to_f32(w.h_s[:512]).astype(np.float64)
+    heavy = kdsynth.bf16_bits_to_f32(w.W_s[w.meta["heavy_rows"]]).astype(np.float64)
+    zmax = (h @ heavy.T).max(axis=1)
+    must = np.argsort(zmax)[-4:]
+    rows = kdsynth.sample_rows(w.N, 20, must=must)
+    _say(f"{w.name} N={w.N} V={w.V} rows={len(rows)}")
+    run_case(kd, torch, (w.h_s, w.W_s, w.h_t, w.W_t), 1.0, w.tau, rows=rows, chunk_V=8192)

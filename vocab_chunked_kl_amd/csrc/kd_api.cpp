@@ -1,0 +1,158 @@
+// kd_api.cpp - the C ABI declared in include/kd.h: argument checks, workspace
+// sizing and dispatch to the kernel launchers. Every check runs on the host
+// before any HIP call.
+#include "kd.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kd_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+kd_status fail(kd_status s, const char* what) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s", what);
+  return s;
+}
+
+kd_status hip_fail(hipError_t e, const char* where) {
+  snprintf(g_last_error, sizeof(g_last_error), "%s: %s", where, hipGetErrorString(e));
+  return KD_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+kd_status check_common(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
+                       int32_t d_s, int32_t d_t, kd_dtype dtype) {
+  if (!h_s || !W_s || !h_t || !W_t) return fail(KD_ERR_INVALID_ARG, "null input pointer (h_s, W_s, h_t, W_t)");
+  if (N <= 0) return fail(KD_ERR_INVALID_ARG, "N must be positive");
+  if (V < 2) return fail(KD_ERR_INVALID_ARG, "V must be at least 2");
+  if (d_s <= 0 || d_t <= 0) return fail(KD_ERR_INVALID_ARG, "d_s and d_t must be positive");
+  if (dtype != KD_F32 && dtype != KD_BF16) return fail(KD_ERR_UNSUPPORTED, "unknown dtype");
+  if (d_s % 8 || d_t % 8) return fail(KD_ERR_UNSUPPORTED, "d_s and d_t must be multiples of 8");
+  if (!aligned16(h_s) || !aligned16(W_s) || !aligned16(h_t) || !aligned16(W_t))
+    return fail(KD_ERR_UNSUPPORTED, "inputs must be 16-byte aligned");
+  // token and vocabulary tile indices are 32-bit in the kernels
+  if (N > ((int64_t)1 << 38) || V > ((int64_t)1 << 38)) return fail(KD_ERR_UNSUPPORTED, "N or V too large");
+  const int64_t esz = dtype == KD_BF16 ? 2 : 4;
+  if ((int64_t)d_s * esz > (int64_t)1 << 30 || (int64_t)d_t * esz > (int64_t)1 << 30)
+    return fail(KD_ERR_UNSUPPORTED, "hidden size too large");
+  return KD_OK;
+}
+
+bool bad_beta(float beta) { return !(beta >= 0.f && beta <= 1.f); }
+bool bad_tau(float tau) { return !(tau > 0.f) || !isfinite(tau); }
+
+}  // namespace
+
+extern "C" {
+
+const char* kd_status_string(kd_status s) {
+  switch (s) {
+    case KD_OK: return "KD_OK";
+    case KD_ERR_INVALID_ARG: return "KD_ERR_INVALID_ARG";
+    case KD_ERR_UNSUPPORTED: return "KD_ERR_UNSUPPORTED";
+    case KD_ERR_WORKSPACE: return "KD_ERR_WORKSPACE";
+    case KD_ERR_HIP: return "KD_ERR_HIP";
+  }
+  return "KD_ERR_UNKNOWN";
+}
+
+const char* kd_last_error(void) { return g_last_error; }
+
+kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t d_t, kd_dtype dtype, float beta,
+                            int32_t chunk_V, int32_t k, size_t* bytes) {
+  if (!bytes) return fail(KD_ERR_INVALID_ARG, "bytes is null");
+  if (N <= 0 || V < 2 || d_s <= 0 || d_t <= 0) return fail(KD_ERR_INVALID_ARG, "bad shape");
+  if (dtype != KD_F32 && dtype != KD_BF16) return fail(KD_ERR_UNSUPPORTED, "unknown dtype");
+  const kd::Plan p = kd::make_plan(N, V, d_s, d_t, dtype == KD_BF16);
+  switch (op) {
+    case KD_OP_FWD:
+      if (bad_beta(beta)) return fail(KD_ERR_INVALID_ARG, "beta outside [0, 1]");
+      *bytes = kd::fwd_workspace_bytes(p, beta > 0.f && beta < 1.f);
+      return KD_OK;
+    case KD_OP_BWD:
+      if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
+      *bytes = kd::bwd_workspace_bytes(p, chunk_V);
+      return KD_OK;
+    case KD_OP_TOPK:
+      if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
+      *bytes = kd::topk_workspace_bytes(p, k);
+      return KD_OK;
+  }
+  return fail(KD_ERR_INVALID_ARG, "unknown op");
+}
+
+kd_status kd_fwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
+                 int32_t d_s, int32_t d_t, float beta, float tau, kd_dtype dtype, float* loss, float* lse_s,
+                 float* lse_t, float* aux, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  kd_status s = check_common(h_s, W_s, h_t, W_t, N, V, d_s, d_t, dtype);
+  if (s != KD_OK) return s;
+  if (bad_beta(beta)) return fail(KD_ERR_INVALID_ARG, "beta outside [0, 1]");
+  if (bad_tau(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be positive and finite");
+  if (!loss || !lse_s || !lse_t) return fail(KD_ERR_INVALID_ARG, "null output pointer (loss, lse_s, lse_t)");
+  if (!aux && beta > 0.f) return fail(KD_ERR_INVALID_ARG, "aux may be null only for beta == 0");
+  if (!aligned4(loss) || !aligned4(lse_s) || !aligned4(lse_t) || (aux && !aligned4(aux)))
+    return fail(KD_ERR_UNSUPPORTED, "outputs must be 4-byte aligned");
+  const kd::Plan p = kd::make_plan(N, V, d_s, d_t, dtype == KD_BF16);
+  const size_t need = kd::fwd_workspace_bytes(p, beta > 0.f && beta < 1.f);
+  if (!workspace || ws_bytes < need) return fail(KD_ERR_WORKSPACE, "workspace smaller than kd_workspace_size(FWD)");
+  if (!aligned16(workspace)) return fail(KD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  kd::FwdIO io{h_s, W_s, h_t, W_t, beta, tau, loss, lse_s, lse_t, aux, workspace};
+  hipError_t e = kd::run_fwd(p, io, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KD_OK : hip_fail(e, "kd_fwd launch");
+}
+
+kd_status kd_bwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
+                 int32_t d_s, int32_t d_t, float beta, float tau, kd_dtype dtype, int32_t chunk_V,
+                 const float* lse_s, const float* lse_t, const float* aux, const float* grad_loss, float* dh_s,
+                 void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  kd_status s = check_common(h_s, W_s, h_t, W_t, N, V, d_s, d_t, dtype);
+  if (s != KD_OK) return s;
+  if (bad_beta(beta)) return fail(KD_ERR_INVALID_ARG, "beta outside [0, 1]");
+  if (bad_tau(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be positive and finite");
+  if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
+  if (!lse_s || !lse_t || !dh_s) return fail(KD_ERR_INVALID_ARG, "null pointer (lse_s, lse_t, dh_s)");
+  if (!aux && beta > 0.f) return fail(KD_ERR_INVALID_ARG, "aux may be null only for beta == 0");
+  if (!aligned4(dh_s) || !aligned4(lse_s) || !aligned4(lse_t)) return fail(KD_ERR_UNSUPPORTED, "misaligned float arrays");
+  const kd::Plan p = kd::make_plan(N, V, d_s, d_t, dtype == KD_BF16);
+  const size_t need = kd::bwd_workspace_bytes(p, chunk_V);
+  if (!workspace || ws_bytes < need) return fail(KD_ERR_WORKSPACE, "workspace smaller than kd_workspace_size(BWD)");
+  if (!aligned16(workspace)) return fail(KD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  kd::BwdIO io{h_s, W_s, h_t, W_t, beta, tau, chunk_V, lse_s, lse_t, aux, grad_loss, dh_s, workspace};
+  hipError_t e = kd::run_bwd(p, io, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KD_OK : hip_fail(e, "kd_bwd launch");
+}
+
+kd_status kd_topk_fwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
+                      int32_t d_s, int32_t d_t, int32_t k, float tau, kd_dtype dtype, const int32_t* labels,
+                      int32_t* topk_idx, float* topk_val, float* binary_kl, float* cond_kl, float* ce,
+                      float* p_mass, float* q_mass, float* lse_s, float* lse_t, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  g_last_error[0] = 0;
+  kd_status s = check_common(h_s, W_s, h_t, W_t, N, V, d_s, d_t, dtype);
+  if (s != KD_OK) return s;
+  if (dtype != KD_BF16) return fail(KD_ERR_UNSUPPORTED, "kd_topk_fwd takes bf16 inputs only");
+  if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
+  if (bad_tau(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be positive and finite");
+  if (!topk_idx || !binary_kl || !cond_kl || !p_mass || !q_mass || !lse_s || !lse_t)
+    return fail(KD_ERR_INVALID_ARG, "null output pointer");
+  if (labels && !ce) return fail(KD_ERR_INVALID_ARG, "ce must be given with labels");
+  const kd::Plan p = kd::make_plan(N, V, d_s, d_t, true);
+  const size_t need = kd::topk_workspace_bytes(p, k);
+  if (!workspace || ws_bytes < need) return fail(KD_ERR_WORKSPACE, "workspace smaller than kd_workspace_size(TOPK)");
+  if (!aligned16(workspace)) return fail(KD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  kd::TopkIO io{h_s, W_s, h_t, W_t, k, tau, labels, topk_idx, topk_val, binary_kl, cond_kl, ce, p_mass, q_mass,
+                lse_s, lse_t, workspace};
+  hipError_t e = kd::run_topk(p, io, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KD_OK : hip_fail(e, "kd_topk_fwd launch");
+}
+
+}  // extern "C"

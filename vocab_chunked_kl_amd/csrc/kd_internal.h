@@ -1,0 +1,70 @@
+// kd_internal.h - host-side plan and launcher declarations shared between the
+// C-ABI layer (kd_api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kd {
+
+// Logit tile: 128 vocabulary rows x 128 tokens per workgroup (4 waves, 2 x 2).
+constexpr int kTileV = 128;
+constexpr int kTileT = 128;
+// dh tile: 128 tokens x 128 hidden units.
+constexpr int kTileDhT = 128;
+constexpr int kTileDhD = 128;
+// Number of token tiles grouped together in the block order (L2 reuse).
+constexpr int kTokGroup = 8;
+// Target number of workgroups for the split-V forward grid.
+constexpr int kFwdTargetBlocks = 2048;
+// Fields of the forward partial statistics.
+constexpr int kFwdFields = 5;  // max_s, sum_s, max_t, sum_t, kl-accumulator
+constexpr int kJsdFields = 2;  // loss sum, aux sum
+
+enum Mode { kModeFKL = 0, kModeRKL = 1, kModeLSE = 2, kModeJSD = 3 };
+
+struct Plan {
+  int64_t N = 0, V = 0;
+  int32_t d_s = 0, d_t = 0;
+  int esz = 2;       // bytes per input element
+  bool bf16 = true;
+  int n_tok_tiles = 0, n_vtiles = 0, n_splits = 0, tiles_per_split = 0;
+};
+
+Plan make_plan(int64_t N, int64_t V, int32_t d_s, int32_t d_t, bool bf16);
+size_t align_up(size_t x, size_t a);
+size_t fwd_workspace_bytes(const Plan& p, bool jsd);
+size_t bwd_workspace_bytes(const Plan& p, int32_t chunk_V);
+
+struct FwdIO {
+  const void *h_s, *W_s, *h_t, *W_t;
+  float beta, tau;
+  float *loss, *lse_s, *lse_t, *aux;
+  void* workspace;
+};
+hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t stream);
+
+struct BwdIO {
+  const void *h_s, *W_s, *h_t, *W_t;
+  float beta, tau;
+  int32_t chunk_V;
+  const float *lse_s, *lse_t, *aux, *grad;
+  float* dh;
+  void* workspace;
+};
+hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t stream);
+
+struct TopkIO {
+  const void *h_s, *W_s, *h_t, *W_t;
+  int32_t k;
+  float tau;
+  const int32_t* labels;
+  int32_t* idx;
+  float *val, *binary, *cond, *ce, *p_mass, *q_mass, *lse_s, *lse_t;
+  void* workspace;
+};
+size_t topk_workspace_bytes(const Plan& p, int32_t k);
+hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t stream);
+
+}  // namespace kd

@@ -1,0 +1,593 @@
+// kd_kernels.hip - forward (divergence) and backward (dL/dh_s) kernels.
+//
+// Forward: one sweep over every (vocabulary tile, token tile): rebuild z_s and
+// z_t for the tile with bf16 MFMA (fp32 accumulation), then fold the tile into
+// per-token online statistics (running max and sum of exp for both models and
+// a KL numerator), exactly the two actions of the Nitrobrew notes ("Nitrobrew
+// 的两个动作": rebuild the logits of a vocabulary block, update the online
+// softmax / log-sum-exp accumulators and the KL terms, discard the block).
+// The vocabulary is split across workgroups; each writes one partial record
+// per token and a merge kernel combines them (a log-sum-exp merge).
+//
+// The beta family follows the beta table of ars-opd-rebuild "03 · 层 2：
+// White-box OPD 基线" (section 2.3): beta = 0 forward KL, beta = 1 reverse KL,
+// both done in one sweep through the identity
+//   KL(q||p) = sum_v q_v (s_v - t_v) - LSE(s) + LSE(t)     (and its mirror),
+// and 0 < beta < 1, whose log-mixture needs the final log-sum-exps, in two
+// sweeps (LSEs, then the mixture sums).
+//
+// Backward (Nitrobrew notes, "仓库实现": recompute per vocabulary block
+// instead of storing logits): per vocabulary chunk, recompute the tile logits,
+// form g = dloss/ds scaled by grad/tau and store it as bf16 [N, chunk]; then
+// dh_s += G . W_s[chunk] with W_s[chunk] transposed once per chunk.
+//
+// All exponentials and logarithms are base 2 (v_exp_f32 / v_log_f32) on
+// logits prescaled by log2(e)/tau; the per-token results are converted back
+// to natural logarithms in the merge.
+#include <math.h>
+
+#include "kd_internal.h"
+#include "kd_sweep.hpp"
+
+namespace kd {
+
+namespace {
+
+constexpr float kNegInf = -INFINITY;
+
+struct LogitArgs {
+  PairDesc ps, pt;   // (W_s, h_s) and (W_t, h_t)
+  int64_t N, V;
+  float c2;          // log2(e) / tau
+  float inv_tau;
+  float beta;
+  int n_tok_tiles, n_splits, tiles_per_split, n_vtiles;
+  int vt_offset;     // first vocabulary tile of the grid (backward chunks)
+  float* part;       // forward partial statistics
+  const float *lse_s, *lse_t, *aux, *grad;
+  char* G;           // backward gradient chunk
+  int64_t ldg;       // G row pitch in bytes
+  int64_t g_col0;    // vocabulary index of G's column 0
+};
+
+// Block -> (token tile, vocabulary split): groups of kTokGroup token tiles
+// visit every split before the next group starts, so that the blocks of one
+// XCD (a contiguous logical range after xcd_remap) share both W and h rows.
+__device__ __forceinline__ void block_coords(int L, int n_tok_tiles, int n_splits, int& tt, int& sp) {
+  const int per_group = kTokGroup * n_splits;
+  const int group = L / per_group;
+  const int within = L - group * per_group;
+  const int rest = n_tok_tiles - group * kTokGroup;
+  const int g_eff = rest < kTokGroup ? rest : kTokGroup;
+  tt = group * kTokGroup + within % g_eff;
+  sp = within / g_eff;
+}
+
+__device__ __forceinline__ void merge_online(float& m, float& l, float m2, float l2) {
+  const float mm = fmaxf(m, m2);
+  const float f1 = (m == kNegInf) ? 0.f : fast_exp2(m - mm);
+  const float f2 = (m2 == kNegInf) ? 0.f : fast_exp2(m2 - mm);
+  l = l * f1 + l2 * f2;
+  m = mm;
+}
+
+// Merge (ms, ls, mt, lt, acc) with a second record; `acc` is scaled like the
+// student sums for reverse KL and like the teacher sums for forward KL.
+template <int MODE>
+__device__ __forceinline__ void merge_record(float& ms, float& ls, float& mt, float& lt, float& ac, float ms2,
+                                             float ls2, float mt2, float lt2, float ac2) {
+  const float mms = fmaxf(ms, ms2), mmt = fmaxf(mt, mt2);
+  const float fs1 = (ms == kNegInf) ? 0.f : fast_exp2(ms - mms);
+  const float fs2 = (ms2 == kNegInf) ? 0.f : fast_exp2(ms2 - mms);
+  const float ft1 = (mt == kNegInf) ? 0.f : fast_exp2(mt - mmt);
+  const float ft2 = (mt2 == kNegInf) ? 0.f : fast_exp2(mt2 - mmt);
+  ls = ls * fs1 + ls2 * fs2;
+  lt = lt * ft1 + lt2 * ft2;
+  if (MODE == kModeRKL) ac = ac * fs1 + ac2 * fs2;
+  if (MODE == kModeFKL) ac = ac * ft1 + ac2 * ft2;
+  ms = mms;
+  mt = mmt;
+}
+
+// ---------------------------------------------------------------------------
+// Forward sweep. MODE: kModeFKL / kModeRKL (loss in one sweep), kModeLSE (only
+// the log-sum-exps, first JSD sweep), kModeJSD (mixture sums given the LSEs).
+// ---------------------------------------------------------------------------
+template <bool kBf16, int MODE>
+__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(LogitArgs a) {
+  constexpr int TM = kTileV, TN = kTileT, MB = TM / 64, NB = TN / 64;
+  __shared__ SweepLds<TM, TN> lds;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  int tt, sp;
+  block_coords(L, a.n_tok_tiles, a.n_splits, tt, sp);
+  const int vt0 = sp * a.tiles_per_split;
+  const int vt1 = min(vt0 + a.tiles_per_split, a.n_vtiles);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  const int64_t tok0 = (int64_t)tt * TN + wn * (TN / 2);
+  const float c2 = a.c2;
+
+  float ms[NB], ls[NB], mt[NB], lt[NB], ac[NB];
+  float Ls2[NB], Lt2[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    ms[nb] = kNegInf;
+    mt[nb] = kNegInf;
+    ls[nb] = lt[nb] = ac[nb] = 0.f;
+    Ls2[nb] = Lt2[nb] = 0.f;
+    if (MODE == kModeJSD) {
+      const int64_t n = tok0 + nb * 32 + (lane & 31);
+      if (n < a.N) {
+        Ls2[nb] = a.lse_s[n] * kLog2e;
+        Lt2[nb] = a.lse_t[n] * kLog2e;
+      }
+    }
+  }
+  const float beta = a.beta, omb = 1.f - a.beta;
+
+  auto epi = [&](int vt, auto& zs, auto& zt) {
+    const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / 2);
+    const bool full = (int64_t)(vt + 1) * TM <= a.V;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      if constexpr (MODE == kModeJSD) {
+        float sl = 0.f, sx = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool ok = full || (vrow0 + mb * 32 + acc_row(r, lane) < a.V);
+            const float lq2 = fmaf(zs[mb][nb][r], c2, -Ls2[nb]);
+            const float lp2 = fmaf(zt[mb][nb][r], c2, -Lt2[nb]);
+            const float q = fast_exp2(lq2), p = fast_exp2(lp2);
+            const float m = beta * p + omb * q;
+            if (ok && m > 1e-37f) {
+              const float lm2 = fast_log2(m);
+              const float tqm = q * (lq2 - lm2);
+              sl += beta * (p * (lp2 - lm2)) + omb * tqm;
+              sx += tqm;
+            }
+          }
+        ls[nb] += sl;
+        lt[nb] += sx;
+      } else {
+        float mxs = kNegInf, mxt = kNegInf;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool ok = full || (vrow0 + mb * 32 + acc_row(r, lane) < a.V);
+            if (ok) {
+              mxs = fmaxf(mxs, zs[mb][nb][r]);
+              mxt = fmaxf(mxt, zt[mb][nb][r]);
+            }
+          }
+        const float ms_new = fmaxf(ms[nb], mxs * c2);
+        const float mt_new = fmaxf(mt[nb], mxt * c2);
+        if (ms_new == kNegInf) continue;  // no valid row seen yet by this lane
+        const float fs = fast_exp2(ms[nb] - ms_new);
+        const float ft = fast_exp2(mt[nb] - mt_new);
+        float sl = 0.f, tl = 0.f, sa = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool ok = full || (vrow0 + mb * 32 + acc_row(r, lane) < a.V);
+            const float x = zs[mb][nb][r], y = zt[mb][nb][r];
+            float es = fast_exp2(fmaf(x, c2, -ms_new));
+            float et = fast_exp2(fmaf(y, c2, -mt_new));
+            if (!ok) es = et = 0.f;
+            sl += es;
+            tl += et;
+            if (MODE == kModeRKL) sa = fmaf(es, x - y, sa);
+            if (MODE == kModeFKL) sa = fmaf(et, y - x, sa);
+          }
+        ls[nb] = fmaf(ls[nb], fs, sl);
+        lt[nb] = fmaf(lt[nb], ft, tl);
+        if (MODE == kModeRKL) ac[nb] = fmaf(ac[nb], fs, sa);
+        if (MODE == kModeFKL) ac[nb] = fmaf(ac[nb], ft, sa);
+        ms[nb] = ms_new;
+        mt[nb] = mt_new;
+      }
+    }
+  };
+  sweep<kBf16, TM, TN>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+
+  // Lanes l and l ^ 32 hold the same tokens (other vocabulary rows).
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    if constexpr (MODE == kModeJSD) {
+      ls[nb] += __shfl_xor(ls[nb], 32);
+      lt[nb] += __shfl_xor(lt[nb], 32);
+    } else {
+      const float oms = __shfl_xor(ms[nb], 32), ols = __shfl_xor(ls[nb], 32);
+      const float omt = __shfl_xor(mt[nb], 32), olt = __shfl_xor(lt[nb], 32);
+      const float oac = __shfl_xor(ac[nb], 32);
+      merge_record<MODE>(ms[nb], ls[nb], mt[nb], lt[nb], ac[nb], oms, ols, omt, olt, oac);
+    }
+  }
+  // Waves wm = 0 and 1 hold the two vocabulary halves of the same tokens.
+  float* red = reinterpret_cast<float*>(lds.buf[0]);  // [kFwdFields][TN]
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = wn * (TN / 2) + nb * 32 + lane;
+      red[0 * TN + col] = ms[nb];
+      red[1 * TN + col] = ls[nb];
+      red[2 * TN + col] = mt[nb];
+      red[3 * TN + col] = lt[nb];
+      red[4 * TN + col] = ac[nb];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = wn * (TN / 2) + nb * 32 + lane;
+      const int64_t n = (int64_t)tt * TN + col;
+      if constexpr (MODE == kModeJSD) {
+        ls[nb] += red[1 * TN + col];
+        lt[nb] += red[3 * TN + col];
+        if (n < a.N) {
+          a.part[(0 * (int64_t)a.n_splits + sp) * a.N + n] = ls[nb];
+          a.part[(1 * (int64_t)a.n_splits + sp) * a.N + n] = lt[nb];
+        }
+      } else {
+        merge_record<MODE>(ms[nb], ls[nb], mt[nb], lt[nb], ac[nb], red[0 * TN + col], red[1 * TN + col],
+                           red[2 * TN + col], red[3 * TN + col], red[4 * TN + col]);
+        if (n < a.N) {
+          a.part[(0 * (int64_t)a.n_splits + sp) * a.N + n] = ms[nb];
+          a.part[(1 * (int64_t)a.n_splits + sp) * a.N + n] = ls[nb];
+          a.part[(2 * (int64_t)a.n_splits + sp) * a.N + n] = mt[nb];
+          a.part[(3 * (int64_t)a.n_splits + sp) * a.N + n] = lt[nb];
+          a.part[(4 * (int64_t)a.n_splits + sp) * a.N + n] = ac[nb];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Cross-split merge: one thread per token.
+// ---------------------------------------------------------------------------
+template <int MODE>
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part, int n_splits, int64_t N,
+                                                   float inv_tau, float* loss, float* lse_s, float* lse_t,
+                                                   float* aux) {
+  const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  const int64_t S = n_splits;
+  if constexpr (MODE == kModeJSD) {
+    float sl = 0.f, sx = 0.f;
+    for (int s = 0; s < n_splits; ++s) {
+      sl += part[(0 * S + s) * N + n];
+      sx += part[(1 * S + s) * N + n];
+    }
+    loss[n] = sl * kLn2;
+    if (aux) aux[n] = sx * kLn2;
+  } else {
+    float ms = kNegInf, ls = 0.f, mt = kNegInf, lt = 0.f, ac = 0.f;
+    for (int s = 0; s < n_splits; ++s)
+      merge_record<MODE>(ms, ls, mt, lt, ac, part[(0 * S + s) * N + n], part[(1 * S + s) * N + n],
+                         part[(2 * S + s) * N + n], part[(3 * S + s) * N + n], part[(4 * S + s) * N + n]);
+    const float Ls = (ms + log2f(ls)) * kLn2;  // natural-log LSE of the tempered logits
+    const float Lt = (mt + log2f(lt)) * kLn2;
+    lse_s[n] = Ls;
+    lse_t[n] = Lt;
+    if (MODE == kModeRKL || MODE == kModeFKL) {
+      // RKL: sum_v q (s - t) - Ls + Lt,   FKL: sum_v p (t - s) - Lt + Ls
+      const float kl = (MODE == kModeRKL) ? (ac / ls) * inv_tau - Ls + Lt : (ac / lt) * inv_tau - Lt + Ls;
+      loss[n] = kl;
+      if (aux) aux[n] = kl;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward, step 1: G[n, v - c0] = grad[n] / tau * dloss_n / ds_v for one chunk.
+// ---------------------------------------------------------------------------
+template <bool kBf16, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void bwdg_kernel(LogitArgs a) {
+  constexpr int TM = kTileV, TN = kTileT, MB = TM / 64, NB = TN / 64;
+  __shared__ SweepLds<TM, TN> lds;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  int tt, sp;
+  block_coords(L, a.n_tok_tiles, a.n_splits, tt, sp);
+  const int vt0 = a.vt_offset + sp * a.tiles_per_split;
+  const int vt1 = min(vt0 + a.tiles_per_split, a.vt_offset + a.n_vtiles);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  const int64_t tok0 = (int64_t)tt * TN + wn * (TN / 2);
+  const float c2 = a.c2, inv_tau = a.inv_tau, beta = a.beta, omb = 1.f - a.beta;
+
+  float Ls2[NB], Lt2[NB], K1[NB], gsc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int64_t n = tok0 + nb * 32 + (lane & 31);
+    Ls2[nb] = Lt2[nb] = K1[nb] = gsc[nb] = 0.f;
+    if (n < a.N) {
+      const float ls = a.lse_s[n], lt = a.lse_t[n];
+      Ls2[nb] = ls * kLog2e;
+      Lt2[nb] = lt * kLog2e;
+      gsc[nb] = (a.grad ? a.grad[n] : 1.f) * inv_tau;
+      if (MODE == kModeRKL) K1[nb] = ls - lt + a.aux[n];  // log q - log p - KL = (s - t) - K1
+      if (MODE == kModeJSD) K1[nb] = a.aux[n];            // KL(q || m)
+    }
+  }
+
+  auto epi = [&](int vt, auto& zs, auto& zt) {
+    const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / 2);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int64_t n = tok0 + nb * 32 + (lane & 31);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          float g4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = rg * 4 + e;
+            const int64_t v = vrow0 + mb * 32 + acc_row(r, lane);
+            const float x = zs[mb][nb][r], y = zt[mb][nb][r];
+            const float lq2 = fmaf(x, c2, -Ls2[nb]);
+            const float q = fast_exp2(lq2);
+            float g;
+            if constexpr (MODE == kModeRKL) {
+              g = q * fmaf(x - y, inv_tau, -K1[nb]);
+            } else if constexpr (MODE == kModeFKL) {
+              g = q - fast_exp2(fmaf(y, c2, -Lt2[nb]));
+            } else {
+              const float lp2 = fmaf(y, c2, -Lt2[nb]);
+              const float m = beta * fast_exp2(lp2) + omb * q;
+              g = (m > 1e-37f) ? omb * q * fmaf(lq2 - fast_log2(m), kLn2, -K1[nb]) : 0.f;
+            }
+            g4[e] = (v < a.V) ? g * gsc[nb] : 0.f;
+          }
+          if (n < a.N) {
+            const int64_t col = vrow0 + mb * 32 + 8 * rg + 4 * (lane >> 5) - a.g_col0;
+            char* dst = a.G + n * a.ldg;
+            if constexpr (kBf16) {
+              u32x2 w;
+              w.x = f32_to_bf16_bits(g4[0]) | (f32_to_bf16_bits(g4[1]) << 16);
+              w.y = f32_to_bf16_bits(g4[2]) | (f32_to_bf16_bits(g4[3]) << 16);
+              *reinterpret_cast<u32x2*>(dst + col * 2) = w;
+            } else {
+              *reinterpret_cast<floatx4*>(dst + col * 4) = floatx4{g4[0], g4[1], g4[2], g4[3]};
+            }
+          }
+        }
+    }
+  };
+  sweep<kBf16, TM, TN>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+}
+
+// ---------------------------------------------------------------------------
+// Backward, step 2: WsT[d, j] = W_s[c0 + j, d] for j < kcols (zero past V).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ W, T* __restrict__ WT, int64_t V,
+                                                        int32_t d, int64_t c0, int64_t pitch) {
+  __shared__ T tile[64][65];
+  const int64_t j0 = (int64_t)blockIdx.x * 64;
+  const int64_t d0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int jr = i * 4 + ty;
+    const int64_t v = c0 + j0 + jr, dd = d0 + tx;
+    tile[jr][tx] = (v < V && dd < d) ? W[v * d + dd] : T(0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int dr = i * 4 + ty;
+    const int64_t dd = d0 + dr;
+    if (dd < d) WT[dd * pitch + j0 + tx] = tile[tx][dr];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward, step 3: dh[n, d] (+)= sum_j G[n, j] WsT[d, j] over one chunk.
+// ---------------------------------------------------------------------------
+struct DhArgs {
+  PairDesc p;        // A = G (token rows), B = WsT (hidden-unit rows)
+  int64_t N;
+  int32_t d_s;
+  int n_tok_tiles, n_d_tiles;
+  float* dh;
+  int first;         // 1: overwrite dh, 0: accumulate
+};
+
+template <bool kBf16>
+__global__ __launch_bounds__(kThreads, 2) void dh_kernel(DhArgs a) {
+  constexpr int TM = kTileDhT, TN = kTileDhD, MB = TM / 64, NB = TN / 64;
+  __shared__ SweepLds<TM, TN> lds;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  int tt, dt;
+  block_coords(L, a.n_tok_tiles, a.n_d_tiles, tt, dt);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
+  PairDesc none = a.p;
+  none.kbytes = 0;
+  auto epi = [&](int tile, auto& acc, auto&) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int64_t d = (int64_t)dt * TN + wn * (TN / 2) + nb * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t n = (int64_t)tile * TM + wm * (TM / 2) + mb * 32 + acc_row(r, lane);
+          if (n < a.N && d < a.d_s) {
+            float* o = a.dh + n * a.d_s + d;
+            *o = a.first ? acc[mb][nb][r] : *o + acc[mb][nb][r];
+          }
+        }
+      }
+  };
+  sweep<kBf16, TM, TN>(a.p, none, (int64_t)dt * TN, tt, tt + 1, lds, epi);
+}
+
+template <bool kBf16>
+hipError_t launch_fwd_mode(int mode, dim3 grid, const LogitArgs& la, hipStream_t st) {
+  switch (mode) {
+    case kModeFKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeFKL>), grid, dim3(kThreads), 0, st, la); break;
+    case kModeRKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeRKL>), grid, dim3(kThreads), 0, st, la); break;
+    case kModeLSE: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeLSE>), grid, dim3(kThreads), 0, st, la); break;
+    default: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeJSD>), grid, dim3(kThreads), 0, st, la); break;
+  }
+  return hipGetLastError();
+}
+
+template <bool kBf16>
+hipError_t launch_bwdg_mode(int mode, dim3 grid, const LogitArgs& la, hipStream_t st) {
+  switch (mode) {
+    case kModeFKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeFKL>), grid, dim3(kThreads), 0, st, la); break;
+    case kModeRKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeRKL>), grid, dim3(kThreads), 0, st, la); break;
+    default: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeJSD>), grid, dim3(kThreads), 0, st, la); break;
+  }
+  return hipGetLastError();
+}
+
+LogitArgs logit_args(const Plan& p, const void* h_s, const void* W_s, const void* h_t, const void* W_t, float tau,
+                     float beta) {
+  LogitArgs la{};
+  la.ps = PairDesc{static_cast<const char*>(W_s), static_cast<const char*>(h_s), (int64_t)p.d_s * p.esz,
+                   (int64_t)p.d_s * p.esz, p.V, p.N, (int32_t)(p.d_s * p.esz)};
+  la.pt = PairDesc{static_cast<const char*>(W_t), static_cast<const char*>(h_t), (int64_t)p.d_t * p.esz,
+                   (int64_t)p.d_t * p.esz, p.V, p.N, (int32_t)(p.d_t * p.esz)};
+  la.N = p.N;
+  la.V = p.V;
+  la.c2 = kLog2e / tau;
+  la.inv_tau = 1.f / tau;
+  la.beta = beta;
+  la.n_tok_tiles = p.n_tok_tiles;
+  return la;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+Plan make_plan(int64_t N, int64_t V, int32_t d_s, int32_t d_t, bool bf16) {
+  Plan p;
+  p.N = N;
+  p.V = V;
+  p.d_s = d_s;
+  p.d_t = d_t;
+  p.bf16 = bf16;
+  p.esz = bf16 ? 2 : 4;
+  p.n_tok_tiles = (int)((N + kTileT - 1) / kTileT);
+  p.n_vtiles = (int)((V + kTileV - 1) / kTileV);
+  int splits = (kFwdTargetBlocks + p.n_tok_tiles - 1) / p.n_tok_tiles;
+  if (splits < 1) splits = 1;
+  if (splits > p.n_vtiles) splits = p.n_vtiles;
+  p.tiles_per_split = (p.n_vtiles + splits - 1) / splits;
+  p.n_splits = (p.n_vtiles + p.tiles_per_split - 1) / p.tiles_per_split;
+  return p;
+}
+
+size_t fwd_workspace_bytes(const Plan& p, bool jsd) {
+  const size_t rec = (size_t)p.n_splits * (size_t)p.N * sizeof(float);
+  return align_up(kFwdFields * rec, 256) + (jsd ? align_up(kJsdFields * rec, 256) : 0);
+}
+
+size_t bwd_workspace_bytes(const Plan& p, int32_t chunk_V) {
+  return align_up((size_t)p.N * chunk_V * p.esz, 256) + align_up((size_t)p.d_s * chunk_V * p.esz, 256);
+}
+
+hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
+  LogitArgs la = logit_args(p, io.h_s, io.W_s, io.h_t, io.W_t, io.tau, io.beta);
+  la.n_splits = p.n_splits;
+  la.tiles_per_split = p.tiles_per_split;
+  la.n_vtiles = p.n_vtiles;
+  la.vt_offset = 0;
+  la.part = static_cast<float*>(io.workspace);
+  const dim3 grid(p.n_tok_tiles * p.n_splits);
+  const dim3 mgrid((unsigned)((p.N + 255) / 256));
+  hipError_t e;
+  if (io.beta == 0.f || io.beta == 1.f) {
+    const int mode = io.beta == 1.f ? kModeRKL : kModeFKL;
+    e = p.bf16 ? launch_fwd_mode<true>(mode, grid, la, st) : launch_fwd_mode<false>(mode, grid, la, st);
+    if (e != hipSuccess) return e;
+    if (mode == kModeRKL)
+      hipLaunchKernelGGL((merge_kernel<kModeRKL>), mgrid, dim3(256), 0, st, la.part, p.n_splits, p.N, la.inv_tau,
+                         io.loss, io.lse_s, io.lse_t, io.aux);
+    else
+      hipLaunchKernelGGL((merge_kernel<kModeFKL>), mgrid, dim3(256), 0, st, la.part, p.n_splits, p.N, la.inv_tau,
+                         io.loss, io.lse_s, io.lse_t, io.aux);
+    return hipGetLastError();
+  }
+  // 0 < beta < 1: sweep 1 -> LSEs, sweep 2 -> mixture sums.
+  e = p.bf16 ? launch_fwd_mode<true>(kModeLSE, grid, la, st) : launch_fwd_mode<false>(kModeLSE, grid, la, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<kModeLSE>), mgrid, dim3(256), 0, st, la.part, p.n_splits, p.N, la.inv_tau,
+                     io.loss, io.lse_s, io.lse_t, io.aux);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  LogitArgs lj = la;
+  lj.part = reinterpret_cast<float*>(static_cast<char*>(io.workspace) + align_up(
+      kFwdFields * (size_t)p.n_splits * (size_t)p.N * sizeof(float), 256));
+  lj.lse_s = io.lse_s;
+  lj.lse_t = io.lse_t;
+  e = p.bf16 ? launch_fwd_mode<true>(kModeJSD, grid, lj, st) : launch_fwd_mode<false>(kModeJSD, grid, lj, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<kModeJSD>), mgrid, dim3(256), 0, st, lj.part, p.n_splits, p.N, la.inv_tau,
+                     io.loss, io.lse_s, io.lse_t, io.aux);
+  return hipGetLastError();
+}
+
+hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
+  const int mode = io.beta == 1.f ? kModeRKL : (io.beta == 0.f ? kModeFKL : kModeJSD);
+  char* G = static_cast<char*>(io.workspace);
+  char* WsT = G + align_up((size_t)p.N * io.chunk_V * p.esz, 256);
+  LogitArgs la = logit_args(p, io.h_s, io.W_s, io.h_t, io.W_t, io.tau, io.beta);
+  la.lse_s = io.lse_s;
+  la.lse_t = io.lse_t;
+  la.aux = io.aux;
+  la.grad = io.grad;
+  la.G = G;
+  la.ldg = (int64_t)io.chunk_V * p.esz;
+  la.tiles_per_split = 1;
+  const int n_d_tiles = (p.d_s + kTileDhD - 1) / kTileDhD;
+  const int n_tok_tiles_dh = (int)((p.N + kTileDhT - 1) / kTileDhT);
+  hipError_t e;
+  for (int64_t c0 = 0; c0 < p.V; c0 += io.chunk_V) {
+    const int64_t ccols = (p.V - c0 < io.chunk_V) ? p.V - c0 : io.chunk_V;
+    const int ctiles = (int)((ccols + kTileV - 1) / kTileV);
+    const int64_t kcols = (int64_t)ctiles * kTileV;
+    la.vt_offset = (int)(c0 / kTileV);
+    la.n_vtiles = ctiles;
+    la.n_splits = ctiles;
+    la.g_col0 = c0;
+    const dim3 grid(p.n_tok_tiles * ctiles);
+    e = p.bf16 ? launch_bwdg_mode<true>(mode, grid, la, st) : launch_bwdg_mode<false>(mode, grid, la, st);
+    if (e != hipSuccess) return e;
+    const dim3 tgrid((unsigned)(kcols / 64), (unsigned)((p.d_s + 63) / 64));
+    if (p.bf16)
+      hipLaunchKernelGGL(transpose_kernel<uint16_t>, tgrid, dim3(256), 0, st, static_cast<const uint16_t*>(io.W_s),
+                         reinterpret_cast<uint16_t*>(WsT), p.V, p.d_s, c0, (int64_t)io.chunk_V);
+    else
+      hipLaunchKernelGGL(transpose_kernel<float>, tgrid, dim3(256), 0, st, static_cast<const float*>(io.W_s),
+                         reinterpret_cast<float*>(WsT), p.V, p.d_s, c0, (int64_t)io.chunk_V);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    DhArgs da{};
+    da.p = PairDesc{G, WsT, (int64_t)io.chunk_V * p.esz, (int64_t)io.chunk_V * p.esz, p.N, p.d_s,
+                    (int32_t)(kcols * p.esz)};
+    da.N = p.N;
+    da.d_s = p.d_s;
+    da.n_tok_tiles = n_tok_tiles_dh;
+    da.n_d_tiles = n_d_tiles;
+    da.dh = io.dh;
+    da.first = c0 == 0;
+    const dim3 dgrid(n_tok_tiles_dh * n_d_tiles);
+    if (p.bf16)
+      hipLaunchKernelGGL(dh_kernel<true>, dgrid, dim3(kThreads), 0, st, da);
+    else
+      hipLaunchKernelGGL(dh_kernel<false>, dgrid, dim3(kThreads), 0, st, da);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace kd
