@@ -63,22 +63,22 @@ struct Stage {
   static_assert(kChunks >= 1 && ROWS * 8 % kThreads == 0, "tile rows must be a multiple of 32");
   u32x4 v[kChunks];
 
-  // byte offset of chunk i inside the tile at stage byte offset 0
-  __device__ __forceinline__ static int32_t lane_off(int i, int tid, int64_t ld_bytes) {
-    const int c = tid + kThreads * i;
-    return (int32_t)((c >> 3) * ld_bytes + (c & 7) * 16);
+  // byte offset of this thread's chunk 0 inside the tile; chunk i sits
+  // 32 * i rows further down
+  __device__ __forceinline__ static int32_t lane_off(int tid, int64_t ld_bytes) {
+    return (int32_t)((tid >> 3) * ld_bytes + (tid & 7) * 16);
   }
 
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, const int32_t (&off)[kChunks], int32_t kbyte0,
-                                       int32_t kbytes, int tid) {
+  // Branch-free: a lane whose 16 bytes lie at or past the row length (K
+  // tail), or any lane when `valid` is false, reads from an offset past the
+  // resource end, which returns zeros.
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int32_t off0, int32_t row_step, int32_t kbyte0,
+                                       int32_t kbytes, bool valid, int tid) {
+    const bool in = valid && (kbyte0 + (tid & 7) * 16 < kbytes);
 #pragma unroll
-    for (int i = 0; i < kChunks; ++i) v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[i] + kbyte0, 0, 0);
-    if (kbyte0 + kStageBytes > kbytes) {  // partial last stage: zero the K tail
-#pragma unroll
-      for (int i = 0; i < kChunks; ++i) {
-        const int c = tid + kThreads * i;
-        if (kbyte0 + (c & 7) * 16 >= kbytes) v[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < kChunks; ++i) {
+      const int32_t off = in ? off0 + i * row_step + kbyte0 : 0x7FFFFFF0;
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
     }
   }
 
@@ -151,6 +151,9 @@ __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 
 // contiguous run of logical tiles so that blocks sharing operand rows meet in
 // that XCD's L2. Identity when the grid is not a multiple of 8.
 __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
+#ifdef KD_NO_XCD_REMAP
+  return b;
+#endif
   if (nblocks & 7) return b;
   return (b & 7) * (nblocks >> 3) + (b >> 3);
 }

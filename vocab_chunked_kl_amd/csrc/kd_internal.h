@@ -8,16 +8,24 @@
 
 namespace kd {
 
-// Logit tile: 128 vocabulary rows x 128 tokens per workgroup (4 waves, 2 x 2).
-constexpr int kTileV = 128;
+// Logit tile: 256 vocabulary rows x 128 tokens per workgroup (4 waves, 2 x 2).
+constexpr int kTileV = 256;
 constexpr int kTileT = 128;
-// dh tile: 128 tokens x 128 hidden units.
-constexpr int kTileDhT = 128;
+// dh tile: 256 tokens x 128 hidden units.
+constexpr int kTileDhT = 256;
 constexpr int kTileDhD = 128;
 // Number of token tiles grouped together in the block order (L2 reuse).
-constexpr int kTokGroup = 8;
-// Target number of workgroups for the split-V forward grid.
-constexpr int kFwdTargetBlocks = 2048;
+#ifndef KD_TOK_GROUP
+#define KD_TOK_GROUP 8
+#endif
+constexpr int kTokGroup = KD_TOK_GROUP;
+// Vocabulary tiles per forward workgroup (2048 vocabulary entries): blocks
+// that run together finish together, which keeps their shared operand rows
+// in L2; each writes one partial record per token.
+#ifndef KD_FWD_TILES_PER_BLOCK
+#define KD_FWD_TILES_PER_BLOCK 8
+#endif
+constexpr int kFwdTilesPerBlock = KD_FWD_TILES_PER_BLOCK;
 // Fields of the forward partial statistics.
 constexpr int kFwdFields = 5;  // max_s, sum_s, max_t, sum_t, kl-accumulator
 constexpr int kJsdFields = 2;  // loss sum, aux sum

@@ -35,6 +35,13 @@ namespace {
 
 constexpr float kNegInf = -INFINITY;
 
+// The three LDS stage buffers of the sweep ring, as separate objects.
+#define KD_RING_LDS(TM, TN)                                                   \
+  __shared__ __attribute__((aligned(16))) char ring0_[Ring<TM, TN>::kBytes]; \
+  __shared__ __attribute__((aligned(16))) char ring1_[Ring<TM, TN>::kBytes]; \
+  __shared__ __attribute__((aligned(16))) char ring2_[Ring<TM, TN>::kBytes]; \
+  const RingLds<TM, TN> lds{ring0_, ring1_, ring2_}
+
 struct LogitArgs {
   PairDesc ps, pt;   // (W_s, h_s) and (W_t, h_t)
   int64_t N, V;
@@ -94,9 +101,9 @@ __device__ __forceinline__ void merge_record(float& ms, float& ls, float& mt, fl
 // the log-sum-exps, first JSD sweep), kModeJSD (mixture sums given the LSEs).
 // ---------------------------------------------------------------------------
 template <bool kBf16, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void fwd_kernel(LogitArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(LogitArgs a) {
   constexpr int TM = kTileV, TN = kTileT, MB = TM / 64, NB = TN / 64;
-  __shared__ SweepLds<TM, TN> lds;
+  KD_RING_LDS(TM, TN);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
   block_coords(L, a.n_tok_tiles, a.n_splits, tt, sp);
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_kernel(LogitArgs a) {
     }
   }
   // Waves wm = 0 and 1 hold the two vocabulary halves of the same tokens.
-  float* red = reinterpret_cast<float*>(lds.buf[0]);  // [kFwdFields][TN]
+  __shared__ float red[kFwdFields * TN];
   if (wm == 1 && lane < 32) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -288,7 +295,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 template <bool kBf16, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void bwdg_kernel(LogitArgs a) {
   constexpr int TM = kTileV, TN = kTileT, MB = TM / 64, NB = TN / 64;
-  __shared__ SweepLds<TM, TN> lds;
+  KD_RING_LDS(TM, TN);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
   block_coords(L, a.n_tok_tiles, a.n_splits, tt, sp);
@@ -322,6 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwdg_kernel(LogitArgs a) {
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
+          __builtin_amdgcn_sched_barrier(0);  // keep the groups apart: bounds register pressure
           float g4[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -398,9 +406,9 @@ struct DhArgs {
 };
 
 template <bool kBf16>
-__global__ __launch_bounds__(kThreads, 2) void dh_kernel(DhArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
   constexpr int TM = kTileDhT, TN = kTileDhD, MB = TM / 64, NB = TN / 64;
-  __shared__ SweepLds<TM, TN> lds;
+  KD_RING_LDS(TM, TN);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, dt;
   block_coords(L, a.n_tok_tiles, a.n_d_tiles, tt, dt);
@@ -480,10 +488,7 @@ Plan make_plan(int64_t N, int64_t V, int32_t d_s, int32_t d_t, bool bf16) {
   p.esz = bf16 ? 2 : 4;
   p.n_tok_tiles = (int)((N + kTileT - 1) / kTileT);
   p.n_vtiles = (int)((V + kTileV - 1) / kTileV);
-  int splits = (kFwdTargetBlocks + p.n_tok_tiles - 1) / p.n_tok_tiles;
-  if (splits < 1) splits = 1;
-  if (splits > p.n_vtiles) splits = p.n_vtiles;
-  p.tiles_per_split = (p.n_vtiles + splits - 1) / splits;
+  p.tiles_per_split = kFwdTilesPerBlock < p.n_vtiles ? kFwdTilesPerBlock : p.n_vtiles;
   p.n_splits = (p.n_vtiles + p.tiles_per_split - 1) / p.tiles_per_split;
   return p;
 }

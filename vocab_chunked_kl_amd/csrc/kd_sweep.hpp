@@ -11,11 +11,10 @@
 // both for the same (vocabulary, token) tile, as the block logit rebuild of
 // the Nitrobrew notes ("Nitrobrew 的两个动作") needs them side by side.
 //
-// Pipeline: the global->register prefetch of the next stage is in flight
-// while the MFMAs run on the current LDS stage; registers are then written
-// into the other LDS buffer and one barrier per stage publishes it. The
-// epilogue runs between the MFMAs of a tile's last stage and the LDS store of
-// the next tile's first stage, so its VALU/exp work overlaps those loads.
+// Pipeline: a ring of three LDS stage buffers filled by direct-to-LDS buffer
+// loads (no staging registers, no LDS store instructions). While stage i is
+// multiplied, the loads of stages i+1 and i+2 are in flight; one barrier per
+// stage recycles the buffer read in the previous step.
 #pragma once
 
 #include "kd_device.hpp"
@@ -30,112 +29,240 @@ struct PairDesc {
   int32_t kbytes;     // contracted extent in bytes (multiple of 16)
 };
 
+// s_waitcnt immediate that waits until at most `n` vector-memory operations
+// of this wave are outstanding (the LDS and export counters are not waited on).
+__device__ __forceinline__ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Workgroup barrier with the wave's own LDS operations drained first. Written
+// as one asm statement (a "memory" clobber keeps every memory access on its
+// side) so that the compiler does not also drain the direct-to-LDS loads in
+// flight: the stage ring below waits for those itself, one stage at a time.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// sched_group_barrier masks
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
+
+// LDS stage layout: [A tile: TM rows][B tile: TN rows], 128 bytes per row,
+// unpadded, with the 16-byte chunks of row R stored at slot (chunk ^ swz(R)),
+// swz(R) = (R & 7) ^ ((R >> 3) & 3). Direct-to-LDS loads write 64 lanes x 16
+// bytes contiguously (8 rows per instruction), and the XOR spreads the MFMA
+// fragment reads of 16 consecutive rows over all banks.
+__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 3); }
+
 template <int TM, int TN>
-struct SweepLds {
-  char buf[2][(TM + TN) * kPitch];
+struct Ring {
+  static constexpr int kBytes = (TM + TN) * kStageBytes;
+};
+
+// Issue the direct-to-LDS loads of one stage (this wave's share: TM/32 + TN/32
+// instructions of 8 rows each). `a_base` / `b_base`: resources starting at the
+// tile's first row; `lane_row` = (lane >> 3) * ld for each operand; `cterm[i]`:
+// this lane's chunk byte offset for instruction index i & 3. A lane whose
+// chunk lies at or past the row length, or every lane when `valid` is false,
+// reads past the resource end and writes zeros.
+template <int TM, int TN>
+__device__ __forceinline__ void dma_stage(char* dst, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                          int32_t a_lane_row, int32_t b_lane_row, int64_t lda, int64_t ldb,
+                                          int32_t kbyte0, int32_t kbytes, bool valid, int wave, int lane) {
+  constexpr int QA = TM / 32, QB = TN / 32;  // instructions per wave
+  const int c_lo = lane & 7, c_hi = lane >> 3;
+#pragma unroll
+  for (int i = 0; i < QA; ++i) {
+    const int q = wave * QA + i;                 // 8-row group index within the tile
+    const int c = c_lo ^ c_hi ^ (q & 3);         // global chunk this lane moves
+    const bool in = valid && (kbyte0 + c * 16 < kbytes);
+    const int32_t off = in ? a_lane_row + (int32_t)(8 * q * lda) + c * 16 + kbyte0 : 0x7FFFFFF0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(dst + q * 1024), 16, off,
+                                             0, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < QB; ++i) {
+    const int q = wave * QB + i;
+    const int c = c_lo ^ c_hi ^ (q & 3);
+    const bool in = valid && (kbyte0 + c * 16 < kbytes);
+    const int32_t off = in ? b_lane_row + (int32_t)(8 * q * ldb) + c * 16 + kbyte0 : 0x7FFFFFF0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (__attribute__((address_space(3))) void*)(dst + TM * kStageBytes + q * 1024), 16, off, 0, 0, 0);
+  }
+}
+
+// MFMAs of one LDS stage for this wave: four k16 sub-steps, fragments double
+// buffered in registers so the reads of sub-step j+1 overlap the MFMAs of j.
+// a_off / b_off: this lane's row byte offset; colx[j]: its swizzled chunk
+// byte offset for sub-step j.
+template <bool kBf16, int MB, int NB>
+__device__ __forceinline__ void mma_ring_stage(floatx16 (&acc)[MB][NB], const char* cur, int a_off, int b_off,
+                                               const int (&colx)[4]) {
+  u32x4 fa[2][MB], fb[2][NB];
+  auto rd = [&](int s, int j) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+      fa[s][mb] = *reinterpret_cast<const u32x4*>(cur + a_off + colx[j] + mb * 32 * kStageBytes);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+      fb[s][nb] = *reinterpret_cast<const u32x4*>(cur + b_off + colx[j] + nb * 32 * kStageBytes);
+  };
+  auto mm = [&](int s) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (kBf16) {
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[s][mb]),
+                                                                __builtin_bit_cast(bf16x8, fb[s][nb]), acc[mb][nb], 0,
+                                                                0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t ae = fa[s][mb][e], be = fb[s][nb][e];
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, ae),
+                                                               __builtin_bit_cast(float, be), acc[mb][nb], 0, 0, 0);
+          }
+        }
+      }
+  };
+  constexpr int kRd = MB + NB;
+  constexpr int kMf = MB * NB * (kBf16 ? 1 : 4);
+  rd(0, 0);
+  rd(1, 1);
+  mm(0);
+  rd(0, 2);
+  mm(1);
+  rd(1, 3);
+  mm(0);
+  mm(1);
+  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kRd, 0);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+#pragma unroll
+    for (int i = 0; i < kMf; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      if (i < kRd) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMf, 0);
+}
+
+// Shared LDS of the stage ring: three separate objects, so that the compiler
+// sees that reads of one stage never alias the loads landing in another.
+template <int TM, int TN>
+struct RingLds {
+  char* b0;
+  char* b1;
+  char* b2;
 };
 
 template <bool kBf16, int TM, int TN, class Epi>
 __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, int64_t b_row0, int a_tile_begin,
-                                      int a_tile_end, SweepLds<TM, TN>& lds, Epi&& epi) {
+                                      int a_tile_end, const RingLds<TM, TN>& lds, Epi&& epi) {
   constexpr int MB = TM / 64, NB = TN / 64;
-  using SA = Stage<TM>;
-  using SB = Stage<TN>;
+  constexpr int kDma = TM / 32 + TN / 32;  // direct-to-LDS loads per wave per stage
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int a_row0w = (wave & 1) * (TM / 2);
-  const int b_row0w = TM + (wave >> 1) * (TN / 2);  // B rows sit after A rows in an LDS stage
+  const int r32 = lane & 31;
+  const int a_off = ((wave & 1) * (TM / 2) + r32) * kStageBytes;
+  const int b_off = (TM + (wave >> 1) * (TN / 2) + r32) * kStageBytes;
+  int colx[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) colx[j] = ((2 * j + (lane >> 5)) ^ lds_swz(r32)) * 16;
 
   const int ks1 = (p1.kbytes + kStageBytes - 1) / kStageBytes;
   const int ks2 = (p2.kbytes + kStageBytes - 1) / kStageBytes;
   if (a_tile_end <= a_tile_begin || ks1 == 0) return;
 
-  // Per-lane chunk offsets inside a tile (stage 0); constant for the sweep.
-  int32_t oa1[SA::kChunks], ob1[SB::kChunks], oa2[SA::kChunks], ob2[SB::kChunks];
-#pragma unroll
-  for (int i = 0; i < SA::kChunks; ++i) {
-    oa1[i] = SA::lane_off(i, tid, p1.lda);
-    oa2[i] = SA::lane_off(i, tid, p2.lda);
-  }
-#pragma unroll
-  for (int i = 0; i < SB::kChunks; ++i) {
-    ob1[i] = SB::lane_off(i, tid, p1.ldb);
-    ob2[i] = SB::lane_off(i, tid, p2.ldb);
-  }
+  const int32_t la1 = (int32_t)((lane >> 3) * p1.lda), la2 = (int32_t)((lane >> 3) * p2.lda);
+  const int32_t lb1 = (int32_t)((lane >> 3) * p1.ldb), lb2 = (int32_t)((lane >> 3) * p2.ldb);
   const __amdgpu_buffer_rsrc_t rb1 = make_rsrc(p1.B + b_row0 * p1.ldb, (p1.b_rows - b_row0) * p1.ldb);
   const __amdgpu_buffer_rsrc_t rb2 = make_rsrc(p2.B + b_row0 * p2.ldb, (p2.b_rows - b_row0) * p2.ldb);
 
-  SA sa;
-  SB sb;
-  // Fetch stage `s` of pair `pr` of A tile `tile` into registers.
-  auto load = [&](int tile, int pr, int s) {
-    const int64_t a_row0 = (int64_t)tile * TM;
-    if (pr == 0) {
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(p1.A + a_row0 * p1.lda, (p1.a_rows - a_row0) * p1.lda);
-      sa.load(ra, oa1, s * kStageBytes, p1.kbytes, tid);
-      sb.load(rb1, ob1, s * kStageBytes, p1.kbytes, tid);
-    } else {
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(p2.A + a_row0 * p2.lda, (p2.a_rows - a_row0) * p2.lda);
-      sa.load(ra, oa2, s * kStageBytes, p2.kbytes, tid);
-      sb.load(rb2, ob2, s * kStageBytes, p2.kbytes, tid);
+  // Fetch cursor: the stage issued next (tile, pair, stage).
+  int ft = a_tile_begin, fp = 0, fs = 0;
+  auto issue = [&](char* dst) {
+    const bool valid = ft < a_tile_end;
+    const int64_t a_row0 = (int64_t)(valid ? ft : a_tile_begin) * TM;
+    if (fp == 0)
+      dma_stage<TM, TN>(dst, make_rsrc(p1.A + a_row0 * p1.lda, (p1.a_rows - a_row0) * p1.lda), rb1, la1, lb1, p1.lda,
+                        p1.ldb, fs * kStageBytes, p1.kbytes, valid, wave, lane);
+    else
+      dma_stage<TM, TN>(dst, make_rsrc(p2.A + a_row0 * p2.lda, (p2.a_rows - a_row0) * p2.lda), rb2, la2, lb2, p2.lda,
+                        p2.ldb, fs * kStageBytes, p2.kbytes, valid, wave, lane);
+    if (++fs == (fp == 0 ? ks1 : ks2)) {
+      fs = 0;
+      if (fp == 0 && ks2 > 0) {
+        fp = 1;
+      } else {
+        fp = 0;
+        ++ft;
+      }
     }
   };
-  auto store = [&](int b) {
-    sa.store(lds.buf[b], tid);
-    sb.store(lds.buf[b] + TM * kPitch, tid);
+
+  // One ring step on buffer `cur`: wait for its loads (at most the next
+  // stage's loads stay in flight), barrier, refill the buffer read one step
+  // earlier with the stage two ahead, multiply `cur`.
+  auto step = [&](floatx16(&acc)[MB][NB], char* cur, char* refill) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDma));
+    lds_barrier();
+    issue(refill);
+    mma_ring_stage<kBf16>(acc, cur, a_off, b_off, colx);
   };
-  // The stage after (tile, pr, s); false past the end of the sweep.
-  auto next = [&](int& tile, int& pr, int& s) -> bool {
-    ++s;
-    if (pr == 0 && s == ks1) {
-      s = 0;
-      if (ks2 > 0) pr = 1; else ++tile;
-    } else if (pr == 1 && s == ks2) {
-      s = 0;
-      pr = 0;
-      ++tile;
+  // Run `ks` stages into `acc` starting with ring position `rot`.
+  auto run = [&](floatx16(&acc)[MB][NB], int ks, int rot) {
+    char* b[3] = {lds.b0, lds.b1, lds.b2};
+    int s = 0;
+    switch (rot) {
+      case 0:
+        for (; s + 3 <= ks; s += 3) {
+          step(acc, lds.b0, lds.b2);
+          step(acc, lds.b1, lds.b0);
+          step(acc, lds.b2, lds.b1);
+        }
+        if (s < ks) step(acc, lds.b0, lds.b2), ++s;
+        if (s < ks) step(acc, lds.b1, lds.b0), ++s;
+        break;
+      case 1:
+        for (; s + 3 <= ks; s += 3) {
+          step(acc, lds.b1, lds.b0);
+          step(acc, lds.b2, lds.b1);
+          step(acc, lds.b0, lds.b2);
+        }
+        if (s < ks) step(acc, lds.b1, lds.b0), ++s;
+        if (s < ks) step(acc, lds.b2, lds.b1), ++s;
+        break;
+      default:
+        for (; s + 3 <= ks; s += 3) {
+          step(acc, lds.b2, lds.b1);
+          step(acc, lds.b0, lds.b2);
+          step(acc, lds.b1, lds.b0);
+        }
+        if (s < ks) step(acc, lds.b2, lds.b1), ++s;
+        if (s < ks) step(acc, lds.b0, lds.b2), ++s;
+        break;
     }
-    return tile < a_tile_end;
+    (void)b;
   };
 
   floatx16 acc1[MB][NB], acc2[MB][NB];
   zero_acc(acc1);
   zero_acc(acc2);
-
-  int lt = a_tile_begin, lp = 0, ls = 0;  // stage in flight
-  load(lt, lp, ls);
-  store(0);
-  __syncthreads();
-  int buf = 0;
-
+  issue(lds.b0);  // stage 0
+  issue(lds.b1);  // stage 1
+  int rot = 0;
   for (int tile = a_tile_begin; tile < a_tile_end; ++tile) {
-    for (int s = 0; s < ks1; ++s) {
-      const bool more = next(lt, lp, ls);
-      if (more) load(lt, lp, ls);
-      mma_stage<kBf16>(acc1, lds.buf[buf], lds.buf[buf], a_row0w, b_row0w, lane);
-      if (more) store(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
+    run(acc1, ks1, rot);
+    rot = (rot + ks1) % 3;
+    if (ks2 > 0) {
+      run(acc2, ks2, rot);
+      rot = (rot + ks2) % 3;
     }
-    for (int s = 0; s < ks2; ++s) {
-      const bool more = next(lt, lp, ls);
-      if (more) load(lt, lp, ls);
-      mma_stage<kBf16>(acc2, lds.buf[buf], lds.buf[buf], a_row0w, b_row0w, lane);
-      if (s + 1 == ks2) {
-        epi(tile, acc1, acc2);
-        zero_acc(acc1);
-        zero_acc(acc2);
-      }
-      if (more) store(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    }
-    if (ks2 == 0) {
-      epi(tile, acc1, acc2);
-      zero_acc(acc1);
-    }
+    epi(tile, acc1, acc2);
+    zero_acc(acc1);
+    zero_acc(acc2);
   }
+  // drain the loads issued past the end before the LDS is reused
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  lds_barrier();
 }
 
 }  // namespace kd
