@@ -59,7 +59,9 @@ typedef enum { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
 typedef enum { KD_OP_FWD = 0, KD_OP_BWD = 1, KD_OP_TOPK = 2 } kd_op;
 
 /* Largest k accepted by kd_topk_fwd. */
-#define KD_TOPK_MAX 128
+#define KD_TOPK_MAX 64
+/* Largest vocabulary accepted by kd_topk_fwd (8 splits of 65536 entries). */
+#define KD_TOPK_MAX_V 524288
 
 /*
  * kd_workspace_size - device workspace (bytes) that `op` needs for this shape.
@@ -134,11 +136,13 @@ kd_status kd_bwd(const void* h_s, const void* W_s, const void* h_t, const void* 
  *     cond_kl   = sum_K (p/P) (log(p/P) - log(q/Q))
  *     ce        = logsumexp(z_s) - z_s[label]   (untempered student, bf16)
  *
- *   k in [1, min(V, KD_TOPK_MAX)].
+ *   k in [1, min(V, KD_TOPK_MAX)]; V <= KD_TOPK_MAX_V (else KD_ERR_UNSUPPORTED).
  *   labels   (device, [N] int32, read; may be NULL): -100 marks an ignored
  *            token (its ce is written as NaN); other values must lie in [0, V).
  *   topk_idx (device, [N, k] int32, written): the selection, in order.
  *   topk_val (device, [N, k] fp32, written; may be NULL): the bf16 teacher
+ *            logits (untempered) at topk_idx.
+ *   topk_val_s (device, [N, k] fp32, written; may be NULL): the bf16 student
  *            logits (untempered) at topk_idx.
  *   binary_kl, cond_kl, p_mass, q_mass, lse_s, lse_t (device, [N] fp32,
  *            written): lse_* over the tempered bf16 logits.
@@ -146,7 +150,7 @@ kd_status kd_bwd(const void* h_s, const void* W_s, const void* h_t, const void* 
  */
 kd_status kd_topk_fwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
                       int32_t d_s, int32_t d_t, int32_t k, float tau, kd_dtype dtype, const int32_t* labels,
-                      int32_t* topk_idx, float* topk_val, float* binary_kl, float* cond_kl, float* ce,
+                      int32_t* topk_idx, float* topk_val, float* topk_val_s, float* binary_kl, float* cond_kl, float* ce,
                       float* p_mass, float* q_mass, float* lse_s, float* lse_t, void* workspace, size_t ws_bytes,
                       void* stream);
 

@@ -82,3 +82,81 @@ def assert_grad_rows(gpu, ref, name="dh_s", floor=None):
         assert cos >= COS_MIN and mrel <= MAXREL, f"{name} row {i}: cos={cos:.7f} maxrel={mrel:.3g}"
     gcos = float(np.sum(gpu * ref) / (np.linalg.norm(gpu) * np.linalg.norm(ref) + 1e-300))
     assert gcos >= COS_MIN, f"{name}: global cosine {gcos:.7f}"
+
+
+def check_topk_rows(out, h_s, W_s, h_t, W_t, rows, k, tau, labels=None, factor=8.0):
+    """Acceptance of kd_topk_fwd on ``rows`` against the fp64 oracle.
+
+    The kernel rounds fp32-accumulated logits to bf16, the oracle rounds the
+    exact logits; a logit within the fp32 accumulation bound of a bf16
+    rounding midpoint may round either way (``ambiguous``). Per row:
+      * every returned teacher / student value is the oracle's rounding, or the
+        other neighbour for an ambiguous logit;
+      * the list is ordered by (value desc, index asc) and no other vocabulary
+        entry can rank above its last element under any admissible rounding;
+      * the list equals the oracle's own top-k unless an ambiguous logit is
+        involved (returned as ``flagged``);
+      * the three terms and both LSEs match the oracle evaluated on the
+        kernel's own roundings of the selected logits (tolerances above).
+    Returns (exact_rows, flagged_rows)."""
+    from oracle import kd_oracle as O
+    idx = out["idx"].cpu().numpy()[rows]
+    vt = out["val"].cpu().numpy()[rows].astype(np.float64)
+    vs = out["val_s"].cpu().numpy()[rows].astype(np.float64)
+    zt = O.logits(h_t[rows], W_t)
+    zs = O.logits(h_s[rows], W_s)
+    bt = O.fp32_dot_error_bound(h_t[rows], W_t, factor)
+    bs = O.fp32_dot_error_bound(h_s[rows], W_s, factor)
+    exact = flagged = 0
+    for i in range(len(rows)):
+        rt, rs = O.bf16_round(zt[i]), O.bf16_round(zs[i])
+        lo_t, hi_t, mid_t = O.bf16_neighbours(zt[i])
+        lo_s, hi_s, mid_s = O.bf16_neighbours(zs[i])
+        amb_t = np.abs(zt[i] - mid_t) <= bt[i]
+        amb_s = np.abs(zs[i] - mid_s) <= bs[i]
+        alt_t = np.where(rt == lo_t, hi_t, lo_t)
+        alt_s = np.where(rs == lo_s, hi_s, lo_s)
+        sel = idx[i].astype(np.int64)
+        assert len(set(sel.tolist())) == k and sel.min() >= 0 and sel.max() < W_t.shape[0], f"row {i}: bad indices"
+        okt = (vt[i] == rt[sel]) | (amb_t[sel] & (vt[i] == alt_t[sel]))
+        oks = (vs[i] == rs[sel]) | (amb_s[sel] & (vs[i] == alt_s[sel]))
+        assert okt.all(), f"row {i}: teacher values {vt[i][~okt][:4]} vs {rt[sel][~okt][:4]}"
+        assert oks.all(), f"row {i}: student values {vs[i][~oks][:4]} vs {rs[sel][~oks][:4]}"
+        for j in range(k - 1):
+            assert (vt[i][j] > vt[i][j + 1]) or (vt[i][j] == vt[i][j + 1] and sel[j] < sel[j + 1]), f"row {i}: order at {j}"
+        rest = np.ones(W_t.shape[0], bool)
+        rest[sel] = False
+        minkey = np.where(amb_t, np.minimum(rt, alt_t), rt)
+        last_v, last_i = vt[i][-1], sel[-1]
+        v_idx = np.arange(W_t.shape[0])
+        above = rest & ((minkey > last_v) | ((minkey == last_v) & (v_idx < last_i)))
+        assert not above.any(), f"row {i}: entries {v_idx[above][:5]} must outrank the last selected"
+        ref_sel = O.topk_order(rt[None], k)[0]
+        if np.array_equal(ref_sel, sel):
+            exact += 1
+        else:
+            flagged += 1
+            assert (amb_t & ((np.abs(rt - last_v) <= 2 * np.abs(hi_t - lo_t)))).any(), f"row {i}: differs without ambiguity"
+        zt_b, zs_b = rt.copy(), rs.copy()
+        zt_b[sel] = vt[i]
+        zs_b[sel] = vs[i]
+        ref = O.topk_three_terms(zs_b[None], zt_b[None], sel[None], tau)
+        for name, key in (("binary", "binary"), ("cond", "cond"), ("p_mass", "p_mass"), ("q_mass", "q_mass"),
+                          ("lse_s", "lse_s"), ("lse_t", "lse_t")):
+            g = float(out[name].cpu().numpy()[rows[i]])
+            assert_close(f"row {i} {name}", np.array([g]), ref[key])
+        if labels is not None:
+            y = int(labels[rows[i]])
+            g = float(out["ce"].cpu().numpy()[rows[i]])
+            if y == -100:
+                assert np.isnan(g)
+            else:
+                cands = [rs[y]] + ([alt_s[y]] if amb_s[y] else [])
+                oks_ce = []
+                for c in cands:
+                    zz = zs_b.copy()
+                    zz[y] = c
+                    ce_ref = O.lse(zz) - c
+                    oks_ce.append(close(np.array([g]), np.array([ce_ref]))[0])
+                assert any(oks_ce), f"row {i} ce {g} vs {O.lse(zs_b) - rs[y]}"
+    return exact, flagged

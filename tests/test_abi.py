@@ -89,11 +89,14 @@ def test_bwd_and_topk_validation():
     # missing dh
     assert lib.kd_bwd(*args, 256, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == 1
     targs = [FAKE, FAKE, FAKE, FAKE, 8, 100, 64, 64]
-    outs = [FAKE] * 9
+    outs = [FAKE] * 10
     # k out of range, fp32 inputs, labels without ce
     assert lib.kd_topk_fwd(*targs, 0, 1.0, 1, None, *outs, FAKE, 1 << 40, None) == 1
     assert lib.kd_topk_fwd(*targs, 200, 1.0, 1, None, *outs, FAKE, 1 << 40, None) == 1
+    # vocabulary above the top-k limit
+    big = [FAKE, FAKE, FAKE, FAKE, 8, kd.KD_TOPK_MAX_V + 1, 64, 64]
+    assert lib.kd_topk_fwd(*big, 8, 1.0, 1, None, *outs, FAKE, 1 << 40, None) == 2
     assert lib.kd_topk_fwd(*targs, 8, 1.0, 0, None, *outs, FAKE, 1 << 40, None) == 2
     o = list(outs)
-    o[4] = None  # ce
+    o[5] = None  # ce
     assert lib.kd_topk_fwd(*targs, 8, 1.0, 1, FAKE, *o, FAKE, 1 << 40, None) == 1

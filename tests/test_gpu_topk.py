@@ -1,0 +1,78 @@
+"""GPU parity of kd_topk_fwd (top-k three-term KD over bf16 logits) against
+the fp64 oracle, through the C ABI. Selection is compared index for index;
+logits that sit within the fp32 accumulation bound of a bf16 rounding
+midpoint may round either way (tests/helpers.check_topk_rows)."""
+import sys
+
+import numpy as np
+import pytest
+
+import kdsynth
+from oracle import kd_oracle as O
+from tests.helpers import check_topk_rows, to_dev, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _kd():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import vocab_chunked_kl_amd as kd
+    kd.load_library()
+    return kd, torch
+
+
+def _run(kd, torch, arrays, k, tau, labels=None):
+    dev = [to_dev(x) for x in arrays]
+    lab = None if labels is None else torch.from_numpy(labels.astype(np.int32)).cuda()
+    out = kd.kd_topk_fwd(*dev, k, tau, labels=lab)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("k", [1, 8, 64])
+@pytest.mark.parametrize("tau", [1.0, 1.5])
+def test_topk_ragged_small(k, tau):
+    kd, torch = _kd()
+    N, V, ds, dt = 150, 5000, 64, 128  # 2 token tiles (ragged), 20 vocabulary tiles (ragged)
+    arrays = kdsynth.small_case(21, N, V, ds, dt)
+    labels = kdsynth.uniform_labels(5, N, V, ignore_frac=0.2)
+    print(f"topk ragged N={N} V={V} k={k} tau={tau}", flush=True)
+    out = _run(kd, torch, arrays, k, tau, labels)
+    exact, flagged = check_topk_rows(out, *arrays, np.arange(N), k, tau, labels)
+    print(f"exact {exact} flagged {flagged}", flush=True)
+    assert exact >= 0.9 * N
+
+
+def test_topk_multi_split_and_ties():
+    kd, torch = _kd()
+    # three vocabulary splits; small logits -> many bf16 ties at the k-th slot
+    N, V, ds, dt = 64, 150001, 32, 32
+    arrays = kdsynth.small_case(22, N, V, ds, dt, logit_std=0.5)
+    labels = kdsynth.uniform_labels(6, N, V)
+    print(f"topk splits N={N} V={V}", flush=True)
+    out = _run(kd, torch, arrays, 64, 1.0, labels)
+    exact, flagged = check_topk_rows(out, *arrays, np.arange(N), 64, 1.0, labels)
+    print(f"exact {exact} flagged {flagged}", flush=True)
+    assert exact >= 0.8 * N
+
+
+def test_topk_k_equals_v():
+    kd, torch = _kd()
+    N, V = 40, 64
+    arrays = kdsynth.small_case(23, N, V, 16, 16)
+    out = _run(kd, torch, arrays, 64, 1.0)
+    exact, _ = check_topk_rows(out, *arrays, np.arange(N), 64, 1.0)
+    assert np.allclose(out["binary"].cpu().numpy(), 0.0, atol=1e-5)
+
+
+def test_topk_workload_v248k_sampled():
+    kd, torch = _kd()
+    w = workload(5)
+    rows = kdsynth.sample_rows(w.N, 16)
+    print(f"{w.name} N={w.N} V={w.V} rows={len(rows)}", flush=True)
+    out = _run(kd, torch, (w.h_s, w.W_s, w.h_t, w.W_t), w.k, w.tau, w.labels)
+    exact, flagged = check_topk_rows(out, w.h_s, w.W_s, w.h_t, w.W_t, rows, w.k, w.tau, w.labels)
+    print(f"exact {exact} flagged {flagged}", flush=True)
+    assert exact >= len(rows) // 2

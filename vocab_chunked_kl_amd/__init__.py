@@ -35,7 +35,8 @@ LIB_PATH = os.path.join(_HERE, "libkd.so")
 KD_OK, KD_ERR_INVALID_ARG, KD_ERR_UNSUPPORTED, KD_ERR_WORKSPACE, KD_ERR_HIP = range(5)
 KD_F32, KD_BF16 = 0, 1
 KD_OP_FWD, KD_OP_BWD, KD_OP_TOPK = 0, 1, 2
-KD_TOPK_MAX = 128
+KD_TOPK_MAX = 64
+KD_TOPK_MAX_V = 524288
 EXPORTED = ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_status_string", "kd_last_error")
 
 
@@ -64,7 +65,7 @@ def load_library(path: str = LIB_PATH):
     lib.kd_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, f32, f32, ctypes.c_int, i32, vp, vp, vp, vp, vp, vp,
                            sz, vp]
     lib.kd_topk_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, ctypes.c_int, vp, vp, vp, vp, vp, vp,
-                                vp, vp, vp, vp, vp, sz, vp]
+                                vp, vp, vp, vp, vp, vp, sz, vp]
     for fn in ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
@@ -172,6 +173,7 @@ def kd_topk_fwd(h_s, W_s, h_t, W_t, k: int, tau: float, labels=None, workspace=N
     f = lambda: torch.empty(N, dtype=torch.float32, device=dev)  # noqa: E731
     out = dict(idx=torch.empty(N, k, dtype=torch.int32, device=dev),
                val=torch.empty(N, k, dtype=torch.float32, device=dev) if with_values else None,
+               val_s=torch.empty(N, k, dtype=torch.float32, device=dev) if with_values else None,
                binary=f(), cond=f(), ce=f() if labels is not None else None, p_mass=f(), q_mass=f(),
                lse_s=f(), lse_t=f())
     if labels is not None and (labels.dtype != torch.int32 or labels.numel() != N or not labels.is_contiguous()):
@@ -179,7 +181,8 @@ def kd_topk_fwd(h_s, W_s, h_t, W_t, k: int, tau: float, labels=None, workspace=N
     nbytes = workspace_size(KD_OP_TOPK, N, V, d_s, d_t, dt, k=k)
     ws = _workspace(nbytes, dev, workspace)
     _check(lib.kd_topk_fwd(_ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t), N, V, d_s, d_t, int(k), float(tau), dt,
-                           _ptr(labels), _ptr(out["idx"]), _ptr(out["val"]), _ptr(out["binary"]), _ptr(out["cond"]),
+                           _ptr(labels), _ptr(out["idx"]), _ptr(out["val"]), _ptr(out["val_s"]), _ptr(out["binary"]),
+                           _ptr(out["cond"]),
                            _ptr(out["ce"]), _ptr(out["p_mass"]), _ptr(out["q_mass"]), _ptr(out["lse_s"]),
                            _ptr(out["lse_t"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return out

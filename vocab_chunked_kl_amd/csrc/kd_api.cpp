@@ -133,7 +133,7 @@ kd_status kd_bwd(const void* h_s, const void* W_s, const void* h_t, const void* 
 
 kd_status kd_topk_fwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
                       int32_t d_s, int32_t d_t, int32_t k, float tau, kd_dtype dtype, const int32_t* labels,
-                      int32_t* topk_idx, float* topk_val, float* binary_kl, float* cond_kl, float* ce,
+                      int32_t* topk_idx, float* topk_val, float* topk_val_s, float* binary_kl, float* cond_kl, float* ce,
                       float* p_mass, float* q_mass, float* lse_s, float* lse_t, void* workspace, size_t ws_bytes,
                       void* stream) {
   g_last_error[0] = 0;
@@ -142,6 +142,7 @@ kd_status kd_topk_fwd(const void* h_s, const void* W_s, const void* h_t, const v
   if (dtype != KD_BF16) return fail(KD_ERR_UNSUPPORTED, "kd_topk_fwd takes bf16 inputs only");
   if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
   if (bad_tau(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be positive and finite");
+  if (V > KD_TOPK_MAX_V) return fail(KD_ERR_UNSUPPORTED, "V above KD_TOPK_MAX_V for kd_topk_fwd");
   if (!topk_idx || !binary_kl || !cond_kl || !p_mass || !q_mass || !lse_s || !lse_t)
     return fail(KD_ERR_INVALID_ARG, "null output pointer");
   if (labels && !ce) return fail(KD_ERR_INVALID_ARG, "ce must be given with labels");
@@ -149,8 +150,8 @@ kd_status kd_topk_fwd(const void* h_s, const void* W_s, const void* h_t, const v
   const size_t need = kd::topk_workspace_bytes(p, k);
   if (!workspace || ws_bytes < need) return fail(KD_ERR_WORKSPACE, "workspace smaller than kd_workspace_size(TOPK)");
   if (!aligned16(workspace)) return fail(KD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
-  kd::TopkIO io{h_s, W_s, h_t, W_t, k, tau, labels, topk_idx, topk_val, binary_kl, cond_kl, ce, p_mass, q_mass,
-                lse_s, lse_t, workspace};
+  kd::TopkIO io{h_s, W_s, h_t, W_t, k, tau, labels, topk_idx, topk_val, topk_val_s, binary_kl, cond_kl, ce, p_mass,
+                q_mass, lse_s, lse_t, workspace};
   hipError_t e = kd::run_topk(p, io, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KD_OK : hip_fail(e, "kd_topk_fwd launch");
 }

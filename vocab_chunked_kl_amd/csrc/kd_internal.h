@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "kd.h"
+
 namespace kd {
 
 // Logit tile: 256 vocabulary rows x 128 tokens per workgroup (4 waves, 2 x 2).
@@ -69,7 +71,7 @@ struct TopkIO {
   float tau;
   const int32_t* labels;
   int32_t* idx;
-  float *val, *binary, *cond, *ce, *p_mass, *q_mass, *lse_s, *lse_t;
+  float *val, *val_s, *binary, *cond, *ce, *p_mass, *q_mass, *lse_s, *lse_t;
   void* workspace;
 };
 size_t topk_workspace_bytes(const Plan& p, int32_t k);

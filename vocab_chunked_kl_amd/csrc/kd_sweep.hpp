@@ -152,9 +152,10 @@ struct RingLds {
   char* b2;
 };
 
-template <bool kBf16, int TM, int TN, class Epi>
+template <bool kBf16, int TM, int TN, class Epi, int NBUF = 3>
 __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, int64_t b_row0, int a_tile_begin,
                                       int a_tile_end, const RingLds<TM, TN>& lds, Epi&& epi) {
+  static_assert(NBUF == 2 || NBUF == 3, "ring of two or three stage buffers");
   constexpr int MB = TM / 64, NB = TN / 64;
   constexpr int kDma = TM / 32 + TN / 32;  // direct-to-LDS loads per wave per stage
   const int tid = threadIdx.x;
@@ -198,63 +199,77 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
     }
   };
 
-  // One ring step on buffer `cur`: wait for its loads (at most the next
-  // stage's loads stay in flight), barrier, refill the buffer read one step
-  // earlier with the stage two ahead, multiply `cur`.
+  // One ring step on buffer `cur`: wait for its loads (with three buffers the
+  // next stage's loads stay in flight), barrier, refill the buffer read one
+  // step earlier with the stage NBUF-1 ahead, multiply `cur`.
   auto step = [&](floatx16(&acc)[MB][NB], char* cur, char* refill) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDma));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NBUF == 3 ? kDma : 0));
     lds_barrier();
     issue(refill);
     mma_ring_stage<kBf16>(acc, cur, a_off, b_off, colx);
   };
   // Run `ks` stages into `acc` starting with ring position `rot`.
   auto run = [&](floatx16(&acc)[MB][NB], int ks, int rot) {
-    char* b[3] = {lds.b0, lds.b1, lds.b2};
     int s = 0;
-    switch (rot) {
-      case 0:
-        for (; s + 3 <= ks; s += 3) {
-          step(acc, lds.b0, lds.b2);
+    if constexpr (NBUF == 3) {
+      switch (rot) {
+        case 0:
+          for (; s + 3 <= ks; s += 3) {
+            step(acc, lds.b0, lds.b2);
+            step(acc, lds.b1, lds.b0);
+            step(acc, lds.b2, lds.b1);
+          }
+          if (s < ks) step(acc, lds.b0, lds.b2), ++s;
+          if (s < ks) step(acc, lds.b1, lds.b0), ++s;
+          break;
+        case 1:
+          for (; s + 3 <= ks; s += 3) {
+            step(acc, lds.b1, lds.b0);
+            step(acc, lds.b2, lds.b1);
+            step(acc, lds.b0, lds.b2);
+          }
+          if (s < ks) step(acc, lds.b1, lds.b0), ++s;
+          if (s < ks) step(acc, lds.b2, lds.b1), ++s;
+          break;
+        default:
+          for (; s + 3 <= ks; s += 3) {
+            step(acc, lds.b2, lds.b1);
+            step(acc, lds.b0, lds.b2);
+            step(acc, lds.b1, lds.b0);
+          }
+          if (s < ks) step(acc, lds.b2, lds.b1), ++s;
+          if (s < ks) step(acc, lds.b0, lds.b2), ++s;
+          break;
+      }
+    } else {
+      if (rot == 0) {
+        for (; s + 2 <= ks; s += 2) {
+          step(acc, lds.b0, lds.b1);
           step(acc, lds.b1, lds.b0);
-          step(acc, lds.b2, lds.b1);
         }
-        if (s < ks) step(acc, lds.b0, lds.b2), ++s;
-        if (s < ks) step(acc, lds.b1, lds.b0), ++s;
-        break;
-      case 1:
-        for (; s + 3 <= ks; s += 3) {
+        if (s < ks) step(acc, lds.b0, lds.b1);
+      } else {
+        for (; s + 2 <= ks; s += 2) {
           step(acc, lds.b1, lds.b0);
-          step(acc, lds.b2, lds.b1);
-          step(acc, lds.b0, lds.b2);
+          step(acc, lds.b0, lds.b1);
         }
-        if (s < ks) step(acc, lds.b1, lds.b0), ++s;
-        if (s < ks) step(acc, lds.b2, lds.b1), ++s;
-        break;
-      default:
-        for (; s + 3 <= ks; s += 3) {
-          step(acc, lds.b2, lds.b1);
-          step(acc, lds.b0, lds.b2);
-          step(acc, lds.b1, lds.b0);
-        }
-        if (s < ks) step(acc, lds.b2, lds.b1), ++s;
-        if (s < ks) step(acc, lds.b0, lds.b2), ++s;
-        break;
+        if (s < ks) step(acc, lds.b1, lds.b0);
+      }
     }
-    (void)b;
   };
 
   floatx16 acc1[MB][NB], acc2[MB][NB];
   zero_acc(acc1);
   zero_acc(acc2);
-  issue(lds.b0);  // stage 0
-  issue(lds.b1);  // stage 1
+  issue(lds.b0);                    // stage 0
+  if (NBUF == 3) issue(lds.b1);     // stage 1
   int rot = 0;
   for (int tile = a_tile_begin; tile < a_tile_end; ++tile) {
     run(acc1, ks1, rot);
-    rot = (rot + ks1) % 3;
+    rot = (rot + ks1) % NBUF;
     if (ks2 > 0) {
       run(acc2, ks2, rot);
-      rot = (rot + ks2) % 3;
+      rot = (rot + ks2) % NBUF;
     }
     epi(tile, acc1, acc2);
     zero_acc(acc1);

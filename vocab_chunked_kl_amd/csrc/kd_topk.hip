@@ -1,8 +1,487 @@
-// kd_topk.hip - top-k three-term kernels (placeholder until the streaming
-// selection kernel lands).
+// kd_topk.hip - top-k three-term decomposition over bf16 logits.
+//
+// lpnh.cn "Top-K知识蒸馏损失实现详解": section 一.2 splits the top-k KD loss
+// into a binary KL (teacher mass inside vs outside the top-k set), a
+// conditional KL (the shape inside the set, renormalised) and a CE anchor on
+// the true token; section 二.1 keeps the logits in bf16 with fp32 only for
+// the log-sum-exp accumulators; section 二.2 gathers the top-64 in bf16 and
+// upcasts only those values.
+//
+// Sweep kernel (one block per token tile and 65536-entry vocabulary split):
+// rebuild both logit tiles with bf16 MFMA, round them to bf16 (nearest even),
+// fold them into online log-sum-exps of the tempered bf16 logits, and keep a
+// running top-k of the teacher's bf16 logits per token in LDS. Candidates are
+// ordered by one 32-bit word: (order-preserving bf16 key << 16) | (0xFFFF -
+// index within the split), i.e. key descending, then index ascending. Only
+// values above the token's current k-th word enter a small candidate buffer;
+// buffers are merged into the state by ranking (count of larger entries).
+//
+// Merge kernel (one wave per token): merge the per-split log-sum-exps and
+// top-k lists, recompute the student logits at the selected indices and at
+// the label (fp32 dot products, rounded to bf16), and evaluate the terms.
+#include <math.h>
+
 #include "kd_internal.h"
+#include "kd_sweep.hpp"
 
 namespace kd {
-size_t topk_workspace_bytes(const Plan& p, int32_t k) { return 256; }
-hipError_t run_topk(const Plan&, const TopkIO&, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+constexpr float kNegInf = -INFINITY;
+constexpr int kTopkSplit = 65536;  // vocabulary entries per split: the in-split index fits 16 bits
+constexpr int kCandCap = 32;       // candidate buffer entries per token per round
+constexpr int kTopkFields = 6;     // m_s, l_s, m_t, l_t, m_1, l_1 (untempered student)
+
+struct TopkArgs {
+  PairDesc ps, pt;
+  int64_t N, V;
+  int32_t d_s;
+  int k;
+  float c2;       // log2(e) / tau
+  float inv_tau;
+  int n_tok_tiles, n_splits, tiles_per_split, n_vtiles;
+  float* part;     // [kTopkFields][n_splits][N]
+  uint32_t* lists; // [n_splits][N][k] packed words, descending
+};
+
+// Round to bf16 (nearest, ties to even) and return the rounded value as fp32.
+__device__ __forceinline__ float round_bf16(float x) {
+  return __builtin_bit_cast(float, f32_to_bf16_bits(x) << 16);
+}
+
+// Order-preserving 16-bit key of a bf16 value (given as its rounded fp32);
+// -0 and +0 map to the same key.
+__device__ __forceinline__ uint32_t bf16_key(float xb) {
+  uint32_t b = __builtin_bit_cast(uint32_t, xb) >> 16;
+  if (b == 0x8000u) b = 0;
+  return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+}
+
+__device__ __forceinline__ float key_to_f32(uint32_t key) {
+  const uint32_t b = (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
+  return __builtin_bit_cast(float, b << 16);
+}
+
+__device__ __forceinline__ void merge2(float& m, float& l, float m2, float l2) {
+  const float mm = fmaxf(m, m2);
+  const float f1 = (m == kNegInf) ? 0.f : fast_exp2(m - mm);
+  const float f2 = (m2 == kNegInf) ? 0.f : fast_exp2(m2 - mm);
+  l = l * f1 + l2 * f2;
+  m = mm;
+}
+
+#define KD_RING2_LDS(TM, TN)                                                  \
+  __shared__ __attribute__((aligned(16))) char ring0_[Ring<TM, TN>::kBytes]; \
+  __shared__ __attribute__((aligned(16))) char ring1_[Ring<TM, TN>::kBytes]; \
+  const RingLds<TM, TN> lds{ring0_, ring1_, nullptr}
+
+// ---------------------------------------------------------------------------
+// Sweep: per (token tile, vocabulary split) top-k lists and LSE partials.
+// kSep1: also accumulate the untempered student LSE (tau != 1, for the CE).
+// ---------------------------------------------------------------------------
+template <bool kSep1>
+__global__ __launch_bounds__(kThreads, 1) void topk_sweep_kernel(TopkArgs a) {
+  constexpr int TM = kTileV, TN = kTileT, MB = TM / 64, NB = TN / 64;
+  KD_RING2_LDS(TM, TN);
+  __shared__ uint32_t S[TN][KD_TOPK_MAX];  // running top-k words, descending
+  __shared__ uint32_t B[TN][kCandCap];     // candidate buffer
+  __shared__ int cntS[TN], cntB[TN];
+  __shared__ uint32_t theta[TN];           // k-th word once full, else 0
+  __shared__ float red[kTopkFields * TN];
+
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int tt = L % a.n_tok_tiles;
+  const int sp = L / a.n_tok_tiles;
+  const int vt0 = sp * a.tiles_per_split;
+  const int vt1 = min(vt0 + a.tiles_per_split, a.n_vtiles);
+  const int64_t vbase = (int64_t)sp * kTopkSplit;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave & 1, wn = wave >> 1;
+  const int K = a.k;
+  const float c2 = a.c2;
+
+  for (int t = tid; t < TN; t += kThreads) {
+    cntS[t] = 0;
+    cntB[t] = 0;
+    theta[t] = 0u;
+  }
+  __syncthreads();
+
+  float ms[NB], ls[NB], mt[NB], lt[NB], m1[NB], l1[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    ms[nb] = mt[nb] = m1[nb] = kNegInf;
+    ls[nb] = lt[nb] = l1[nb] = 0.f;
+  }
+
+  // merge token t's candidate buffer into its state (one wave)
+  auto merge_token = [&](int t) {
+    const int cs = cntS[t];
+    const int cb = min(cntB[t], kCandCap);
+    const int total = cs + cb;
+    const uint32_t e0 = lane < cs ? S[t][lane] : (lane - cs < cb ? B[t][lane - cs] : 0u);
+    const int j1 = lane + 64;
+    const uint32_t e1 = j1 < cs ? S[t][j1] : (j1 - cs < cb && j1 >= cs ? B[t][j1 - cs] : 0u);
+    int r0 = 0, r1 = 0;
+    for (int i = 0; i < total; ++i) {
+      const uint32_t x = i < cs ? S[t][i] : B[t][i - cs];
+      r0 += x > e0;
+      r1 += x > e1;
+    }
+    if (lane < total && r0 < K) S[t][r0] = e0;
+    if (j1 < total && r1 < K) S[t][r1] = e1;
+    const int ns = min(total, K);
+    if (lane == 0) {
+      cntS[t] = ns;
+      cntB[t] = 0;
+    }
+    const uint32_t th = S[t][K - 1];
+    if (lane == 0) theta[t] = ns == K ? th : 0u;
+  };
+
+  auto epi = [&](int vt, auto& zs, auto& zt) {
+    const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / 2);
+    const bool full = (int64_t)(vt + 1) * TM <= a.V;
+    // 1) round both logit tiles to bf16; 2) online LSEs of the tempered values
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float mxs = kNegInf, mxt = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = full || (vrow0 + mb * 32 + acc_row(r, lane) < a.V);
+          zs[mb][nb][r] = round_bf16(zs[mb][nb][r]);
+          zt[mb][nb][r] = round_bf16(zt[mb][nb][r]);
+          if (ok) {
+            mxs = fmaxf(mxs, zs[mb][nb][r]);
+            mxt = fmaxf(mxt, zt[mb][nb][r]);
+          }
+        }
+      const float ms_new = fmaxf(ms[nb], mxs * c2), mt_new = fmaxf(mt[nb], mxt * c2);
+      const float m1_new = fmaxf(m1[nb], mxs * kLog2e);
+      if (ms_new == kNegInf) continue;
+      const float fs = fast_exp2(ms[nb] - ms_new), ft = fast_exp2(mt[nb] - mt_new);
+      const float f1 = fast_exp2(m1[nb] - m1_new);
+      float sl = 0.f, tl = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = full || (vrow0 + mb * 32 + acc_row(r, lane) < a.V);
+          float es = fast_exp2(fmaf(zs[mb][nb][r], c2, -ms_new));
+          float et = fast_exp2(fmaf(zt[mb][nb][r], c2, -mt_new));
+          float e1 = kSep1 ? fast_exp2(fmaf(zs[mb][nb][r], kLog2e, -m1_new)) : 0.f;
+          if (!ok) es = et = e1 = 0.f;
+          sl += es;
+          tl += et;
+          s1 += e1;
+        }
+      ls[nb] = fmaf(ls[nb], fs, sl);
+      lt[nb] = fmaf(lt[nb], ft, tl);
+      ms[nb] = ms_new;
+      mt[nb] = mt_new;
+      if (kSep1) {
+        l1[nb] = fmaf(l1[nb], f1, s1);
+        m1[nb] = m1_new;
+      }
+    }
+    // 3) top-k candidates: rounds until no token's buffer overflowed
+    uint32_t done[NB][2] = {{0u, 0u}, {0u, 0u}};
+    const int rel0 = (int)(vrow0 - vbase);
+    while (true) {
+      int ov = 0;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = wn * (TN / 2) + nb * 32 + (lane & 31);
+        const uint32_t th = theta[col];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int bit = mb * 16 + r;
+            const int rel = rel0 + mb * 32 + acc_row(r, lane);
+            const bool ok = full || (vbase + rel < a.V);
+            const uint32_t w = (bf16_key(zt[mb][nb][r]) << 16) | (0xFFFFu - (uint32_t)rel);
+            if (ok && w > th && !((done[nb][bit >> 5] >> (bit & 31)) & 1u)) {
+              const int slot = atomicAdd(&cntB[col], 1);
+              if (slot < kCandCap) {
+                B[col][slot] = w;
+                done[nb][bit >> 5] |= 1u << (bit & 31);
+              } else {
+                ov = 1;
+              }
+            }
+          }
+      }
+      const int any = __syncthreads_or(ov);
+      for (int t = wave; t < TN; t += 4)
+        if (cntB[t] > 0) merge_token(t);
+      __syncthreads();
+      if (!any) break;
+    }
+  };
+  sweep<true, TM, TN, decltype(epi)&, 2>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+
+  // LSE partials: lanes l and l^32, then the two vocabulary-half waves
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    merge2(ms[nb], ls[nb], __shfl_xor(ms[nb], 32), __shfl_xor(ls[nb], 32));
+    merge2(mt[nb], lt[nb], __shfl_xor(mt[nb], 32), __shfl_xor(lt[nb], 32));
+    merge2(m1[nb], l1[nb], __shfl_xor(m1[nb], 32), __shfl_xor(l1[nb], 32));
+  }
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = wn * (TN / 2) + nb * 32 + lane;
+      red[0 * TN + col] = ms[nb];
+      red[1 * TN + col] = ls[nb];
+      red[2 * TN + col] = mt[nb];
+      red[3 * TN + col] = lt[nb];
+      red[4 * TN + col] = m1[nb];
+      red[5 * TN + col] = l1[nb];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = wn * (TN / 2) + nb * 32 + lane;
+      merge2(ms[nb], ls[nb], red[0 * TN + col], red[1 * TN + col]);
+      merge2(mt[nb], lt[nb], red[2 * TN + col], red[3 * TN + col]);
+      merge2(m1[nb], l1[nb], red[4 * TN + col], red[5 * TN + col]);
+      const int64_t n = (int64_t)tt * TN + col;
+      if (n < a.N) {
+        const int64_t S_ = a.n_splits;
+        a.part[(0 * S_ + sp) * a.N + n] = ms[nb];
+        a.part[(1 * S_ + sp) * a.N + n] = ls[nb];
+        a.part[(2 * S_ + sp) * a.N + n] = mt[nb];
+        a.part[(3 * S_ + sp) * a.N + n] = lt[nb];
+        a.part[(4 * S_ + sp) * a.N + n] = m1[nb];
+        a.part[(5 * S_ + sp) * a.N + n] = l1[nb];
+      }
+    }
+  }
+  // the top-k list of each token (padded with 0 words when the split is short)
+  for (int i = tid; i < TN * K; i += kThreads) {
+    const int t = i / K, j = i - t * K;
+    const int64_t n = (int64_t)tt * TN + t;
+    if (n < a.N) a.lists[((int64_t)sp * a.N + n) * K + j] = j < cntS[t] ? S[t][j] : 0u;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge: one wave per token.
+// ---------------------------------------------------------------------------
+struct MergeArgs {
+  const uint16_t *h_s, *W_s;
+  int64_t N, V;
+  int32_t d_s;
+  int k, n_splits;
+  float tau, inv_tau;
+  const float* part;
+  const uint32_t* lists;
+  const int32_t* labels;
+  int32_t* idx;
+  float *val_t, *val_s, *binary, *cond, *ce, *p_mass, *q_mass, *lse_s, *lse_t;
+  int sep1;
+};
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
+
+// Student logit for vocabulary row v (fp32 accumulation, rounded to bf16),
+// computed by the whole wave: lane-strided partial dot, then a wave sum.
+__device__ __forceinline__ float student_logit(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int64_t v,
+                                               int32_t d, int lane) {
+  const uint16_t* w = W + v * d;
+  float acc = 0.f;
+  for (int i = lane * 8; i < d; i += 64 * 8) {
+    const u32x4 hv = *reinterpret_cast<const u32x4*>(h + i);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(w + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t hx = hv[e], wx = wv[e];
+      acc = fmaf(__builtin_bit_cast(float, hx << 16), __builtin_bit_cast(float, wx << 16), acc);
+      acc = fmaf(__builtin_bit_cast(float, hx & 0xFFFF0000u), __builtin_bit_cast(float, wx & 0xFFFF0000u), acc);
+    }
+  }
+  return round_bf16(wave_sum(acc));
+}
+
+__device__ __forceinline__ float log1mexp_f(float x) {  // log(1 - e^x), x <= 0
+  return x > -0.69314718f ? logf(-expm1f(x)) : log1pf(-expf(x));
+}
+
+constexpr int kMaxSplits = 8;  // vocabularies up to 8 * 65536 entries
+
+__global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
+  __shared__ unsigned long long cand[4][kMaxSplits * KD_TOPK_MAX];
+  __shared__ unsigned long long sel[4][KD_TOPK_MAX];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * 4 + wave;
+  if (n >= a.N) return;  // whole waves only: no block barrier below
+  const int K = a.k, S = a.n_splits;
+  const int64_t SN = (int64_t)S;
+
+  // log-sum-exps (base 2, tempered; m_1/l_1 untempered when kept apart)
+  float ms = kNegInf, ls = 0.f, mt = kNegInf, lt = 0.f, m1 = kNegInf, l1 = 0.f;
+  for (int s = lane; s < S; s += 64) {
+    merge2(ms, ls, a.part[(0 * SN + s) * a.N + n], a.part[(1 * SN + s) * a.N + n]);
+    merge2(mt, lt, a.part[(2 * SN + s) * a.N + n], a.part[(3 * SN + s) * a.N + n]);
+    merge2(m1, l1, a.part[(4 * SN + s) * a.N + n], a.part[(5 * SN + s) * a.N + n]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    merge2(ms, ls, __shfl_xor(ms, o), __shfl_xor(ls, o));
+    merge2(mt, lt, __shfl_xor(mt, o), __shfl_xor(lt, o));
+    merge2(m1, l1, __shfl_xor(m1, o), __shfl_xor(l1, o));
+  }
+  const float Ls = (ms + log2f(ls)) * kLn2;  // natural LSE of the tempered bf16 logits
+  const float Lt = (mt + log2f(lt)) * kLn2;
+  const float L1 = a.sep1 ? (m1 + log2f(l1)) * kLn2 : Ls;  // untempered student LSE (tau == 1: the same)
+
+  // candidates as 64-bit words: key << 32 | (0xFFFFFFFF - vocabulary index); 0 = empty
+  const int C = S * K;
+  unsigned long long* cw = cand[wave];
+  for (int i = lane; i < C; i += 64) {
+    const int s = i / K;
+    const uint32_t w = a.lists[((int64_t)s * a.N + n) * K + (i - s * K)];
+    const uint32_t vidx = (uint32_t)s * kTopkSplit + (0xFFFFu - (w & 0xFFFFu));
+    cw[i] = w == 0u ? 0ull : ((unsigned long long)(w >> 16) << 32) | (0xFFFFFFFFull - vidx);
+  }
+  __builtin_amdgcn_wave_barrier();
+  // rank every candidate against all others (all words are distinct); rank < K is its slot
+  for (int i = lane; i < C; i += 64) {
+    const unsigned long long x = cw[i];
+    int r = 0;
+    for (int j = 0; j < C; ++j) r += cw[j] > x;
+    if (x != 0ull && r < K) sel[wave][r] = x;
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  const bool act = lane < K;
+  const unsigned long long xj = act ? sel[wave][lane] : 0ull;
+  const int32_t vj = (int32_t)(0xFFFFFFFFu - (uint32_t)(xj & 0xFFFFFFFFull));
+  const float tj = act ? key_to_f32((uint32_t)(xj >> 32)) : 0.f;
+  // student bf16 logits at the selected indices: one wave-wide dot product each
+  const uint16_t* h = a.h_s + n * a.d_s;
+  float sj = 0.f;
+  for (int j = 0; j < K; ++j) {
+    const int32_t v = __shfl(vj, j);
+    const float zsv = student_logit(h, a.W_s, v, a.d_s, lane);
+    if (lane == j) sj = zsv;
+  }
+  if (act) {
+    a.idx[n * K + lane] = vj;
+    if (a.val_t) a.val_t[n * K + lane] = tj;
+    if (a.val_s) a.val_s[n * K + lane] = sj;
+  }
+  const float t2 = tj * a.inv_tau, s2 = sj * a.inv_tau;
+  const float mtK = wave_max(act ? t2 : kNegInf), msK = wave_max(act ? s2 : kNegInf);
+  const float et = act ? expf(t2 - mtK) : 0.f, es = act ? expf(s2 - msK) : 0.f;
+  const float set = wave_sum(et), ses = wave_sum(es);
+  const float LKt = mtK + logf(set), LKs = msK + logf(ses);
+  // Tail masses below fp32 resolution are held at 2^-24 so that their logs stay
+  // finite; with the whole vocabulary selected there is no tail at all.
+  const bool all = (int64_t)K >= a.V;
+  const float logP = fminf(LKt - Lt, -5.9604645e-8f), logQ = fminf(LKs - Ls, -5.9604645e-8f);
+  const float cterm = act ? (et / set) * ((t2 - LKt) - (s2 - LKs)) : 0.f;
+  const float condv = wave_sum(cterm);
+  if (lane == 0) {
+    const float P = expf(logP), Q = expf(logQ);
+    const float l1P = log1mexp_f(logP), l1Q = log1mexp_f(logQ);
+    const float tail = (1.f - P) * (l1P - l1Q);
+    a.binary[n] = all ? 0.f : P * (logP - logQ) + tail;
+    a.cond[n] = condv;
+    a.p_mass[n] = all ? 1.f : P;
+    a.q_mass[n] = all ? 1.f : Q;
+    a.lse_s[n] = Ls;
+    a.lse_t[n] = Lt;
+  }
+  if (a.labels) {
+    const int32_t y = a.labels[n];
+    if (y >= 0 && y < a.V) {
+      const float zy = student_logit(h, a.W_s, y, a.d_s, lane);
+      if (lane == 0) a.ce[n] = L1 - zy;
+    } else if (lane == 0) {
+      a.ce[n] = NAN;
+    }
+  }
+}
+
+}  // namespace
+
+size_t topk_workspace_bytes(const Plan& p, int32_t k) {
+  const int64_t n_splits = (p.V + kTopkSplit - 1) / kTopkSplit;
+  return align_up((size_t)kTopkFields * n_splits * p.N * sizeof(float), 256) +
+         align_up((size_t)n_splits * p.N * k * sizeof(uint32_t), 256);
+}
+
+hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
+  TopkArgs a{};
+  a.ps = PairDesc{static_cast<const char*>(io.W_s), static_cast<const char*>(io.h_s), (int64_t)p.d_s * 2,
+                  (int64_t)p.d_s * 2, p.V, p.N, p.d_s * 2};
+  a.pt = PairDesc{static_cast<const char*>(io.W_t), static_cast<const char*>(io.h_t), (int64_t)p.d_t * 2,
+                  (int64_t)p.d_t * 2, p.V, p.N, p.d_t * 2};
+  a.N = p.N;
+  a.V = p.V;
+  a.d_s = p.d_s;
+  a.k = io.k;
+  a.c2 = kLog2e / io.tau;
+  a.inv_tau = 1.f / io.tau;
+  a.n_tok_tiles = p.n_tok_tiles;
+  a.n_vtiles = p.n_vtiles;
+  a.tiles_per_split = kTopkSplit / kTileV;
+  a.n_splits = (int)((p.V + kTopkSplit - 1) / kTopkSplit);
+  if (a.n_splits > kMaxSplits) return hipErrorInvalidValue;
+  a.part = static_cast<float*>(io.workspace);
+  a.lists = reinterpret_cast<uint32_t*>(static_cast<char*>(io.workspace) +
+                                        align_up((size_t)kTopkFields * a.n_splits * p.N * sizeof(float), 256));
+  const bool sep1 = io.labels != nullptr && io.tau != 1.f;
+  const dim3 grid(p.n_tok_tiles * a.n_splits);
+  if (sep1)
+    hipLaunchKernelGGL(topk_sweep_kernel<true>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(topk_sweep_kernel<false>, grid, dim3(kThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  MergeArgs m{};
+  m.h_s = static_cast<const uint16_t*>(io.h_s);
+  m.W_s = static_cast<const uint16_t*>(io.W_s);
+  m.N = p.N;
+  m.V = p.V;
+  m.d_s = p.d_s;
+  m.k = io.k;
+  m.n_splits = a.n_splits;
+  m.tau = io.tau;
+  m.inv_tau = 1.f / io.tau;
+  m.part = a.part;
+  m.lists = a.lists;
+  m.labels = io.labels;
+  m.idx = io.idx;
+  m.val_t = io.val;
+  m.val_s = io.val_s;
+  m.binary = io.binary;
+  m.cond = io.cond;
+  m.ce = io.ce;
+  m.p_mass = io.p_mass;
+  m.q_mass = io.q_mass;
+  m.lse_s = io.lse_s;
+  m.lse_t = io.lse_t;
+  m.sep1 = sep1;
+  hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)((p.N + 3) / 4)), dim3(256), 0, st, m);
+  return hipGetLastError();
+}
+
 }  // namespace kd
