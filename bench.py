@@ -36,9 +36,52 @@ def parse():
     ap.add_argument("--chunk-v", type=int, default=8192)
     ap.add_argument("--beta", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=96)
+    ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a "
+                         "'--calibrate-copy' run into the traffic record and exit")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
+
+
+def summarize_traffic(fetch_csv, write_csv, out_path):
+    """Per-launch HBM bytes of the forward sweep kernel from two rocprofv3
+    counter runs (FETCH_SIZE, then WRITE_SIZE, both in KiB per dispatch),
+    each scaled by what the same counter reads for the 1 GiB copy kernel."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            vals[r["Kernel_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: statistics.median(v.values()) for k, v in vals.items()}
+
+    f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w = per_kernel(write_csv, "WRITE_SIZE")
+    copy = [k for k in f if "elementwise" in k or "copy" in k.lower()]
+    fwd = [k for k in f if "fwd_kernel" in k]
+    if not copy or not fwd:
+        raise SystemExit(f"kernels not found: copy={copy} fwd={fwd}")
+    ck = max(copy, key=lambda k: f[k])
+    ff = COPY_BYTES / (f[ck] * 1024.0)
+    fw = COPY_BYTES / (w[ck] * 1024.0)
+    fk = fwd[0]
+    rec = {"kernel": fk, "copy_kernel": ck, "fetch_kib": f[fk], "write_kib": w.get(fk, 0.0),
+           "copy_fetch_kib": f[ck], "copy_write_kib": w[ck], "fetch_scale": ff, "write_scale": fw,
+           "bytes_per_launch": f[fk] * 1024.0 * ff + w.get(fk, 0.0) * 1024.0 * fw,
+           "kernel_source_hash": kernel_hash()}
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
 
 
 def cpu_baseline(w, beta, rows_n):
@@ -65,6 +108,9 @@ def cpu_baseline(w, beta, rows_n):
 
 def main():
     args = parse()
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.traffic)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU: "
               "no sharding or collectives are built)", file=sys.stderr)
@@ -103,6 +149,12 @@ def main():
         kd.kd_bwd(*dev, beta, tau, lse_s, lse_t, aux, chunk_V=args.chunk_v, workspace=ws_b, stream=stream, dh=dh)
         return loss
 
+    if args.calibrate_copy:  # a plain copy of known size for scaling the byte counters
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             step()

@@ -76,3 +76,23 @@ def test_topk_workload_v248k_sampled():
     exact, flagged = check_topk_rows(out, w.h_s, w.W_s, w.h_t, w.W_t, rows, w.k, w.tau, w.labels)
     print(f"exact {exact} flagged {flagged}", flush=True)
     assert exact >= len(rows) // 2
+
+
+def test_topk_workload_svd256_teacher_sampled():
+    """The same workload with the teacher compressed to rank 256 (its hidden
+    state projected on the top-256 right singular vectors of W_t, and W_t
+    replaced by the matching left singular vectors), both rounded to bf16 and
+    fed to the kernel as an ordinary d_t = 256 teacher."""
+    kd, torch = _kd()
+    w = workload(5)
+    r = kdsynth.SVD_RANK
+    print(f"{w.name} rank-{r} teacher: factorising W_t {w.W_t.shape}", flush=True)
+    h_r, W_r, S = O.svd_teacher(w.h_t, w.W_t, r, method="gram")
+    assert np.allclose(W_r.T @ W_r, np.eye(r), atol=1e-6)
+    h_rb = kdsynth.f32_to_bf16_bits(h_r.astype(np.float32))
+    W_rb = kdsynth.f32_to_bf16_bits(W_r.astype(np.float32))
+    rows = kdsynth.sample_rows(w.N, 16, seed=11)
+    out = _run(kd, torch, (w.h_s, w.W_s, h_rb, W_rb), w.k, w.tau, w.labels)
+    exact, flagged = check_topk_rows(out, w.h_s, w.W_s, h_rb, W_rb, rows, w.k, w.tau, w.labels)
+    print(f"exact {exact} flagged {flagged}", flush=True)
+    assert exact >= len(rows) // 2
