@@ -86,13 +86,33 @@ __device__ __forceinline__ void dma_stage(char* dst, __amdgpu_buffer_rsrc_t ra, 
   }
 }
 
+// Pinned instruction order of one stage (sched_group_barrier takes literal
+// counts, hence the compile-time recursion over MFMA index M): the LDS reads
+// of sub-step 0 first; then each MFMA is followed by at most one LDS read of
+// the next sub-step, and the `kLoads` direct-to-LDS loads are spread evenly
+// over the first three quarters of the MFMAs.
+template <int kMf, int kRd, int kLoads, int M = 0>
+__device__ __forceinline__ void pin_stage_order() {
+  if constexpr (M == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kRd, 0);
+  if constexpr (M < 4 * kMf) {
+    constexpr int kSpan = 3 * kMf;
+    constexpr int lo = M * kLoads / kSpan, hi = (M + 1) * kLoads / kSpan;
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if constexpr (M < 3 * kMf && (M % kMf) < kRd) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    if constexpr (M < kSpan && hi > lo) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, hi - lo, 0);
+    pin_stage_order<kMf, kRd, kLoads, M + 1>();
+  }
+}
+
 // MFMAs of one LDS stage for this wave: four k16 sub-steps, fragments double
 // buffered in registers so the reads of sub-step j+1 overlap the MFMAs of j.
 // a_off / b_off: this lane's row byte offset; colx[j]: its swizzled chunk
-// byte offset for sub-step j.
-template <bool kBf16, int MB, int NB>
+// byte offset for sub-step j. `issue` emits the direct-to-LDS loads of a later
+// stage; they are spread between the MFMAs (a burst of loads right after the
+// barrier would stall the wave's issue while the address unit drains them).
+template <bool kBf16, int MB, int NB, int kLoads, class Issue>
 __device__ __forceinline__ void mma_ring_stage(floatx16 (&acc)[MB][NB], const char* cur, int a_off, int b_off,
-                                               const int (&colx)[4]) {
+                                               const int (&colx)[4], Issue&& issue) {
   u32x4 fa[2][MB], fb[2][NB];
   auto rd = [&](int s, int j) {
 #pragma unroll
@@ -123,7 +143,9 @@ __device__ __forceinline__ void mma_ring_stage(floatx16 (&acc)[MB][NB], const ch
   };
   constexpr int kRd = MB + NB;
   constexpr int kMf = MB * NB * (kBf16 ? 1 : 4);
+  constexpr int kTotMf = 4 * kMf;
   rd(0, 0);
+  issue();
   rd(1, 1);
   mm(0);
   rd(0, 2);
@@ -131,16 +153,7 @@ __device__ __forceinline__ void mma_ring_stage(floatx16 (&acc)[MB][NB], const ch
   rd(1, 3);
   mm(0);
   mm(1);
-  __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kRd, 0);
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-#pragma unroll
-    for (int i = 0; i < kMf; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      if (i < kRd) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-  }
-  __builtin_amdgcn_sched_group_barrier(kSchedMfma, kMf, 0);
+  pin_stage_order<kMf, kRd, kLoads>();
 }
 
 // Shared LDS of the stage ring: three separate objects, so that the compiler
@@ -177,26 +190,27 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
   const __amdgpu_buffer_rsrc_t rb1 = make_rsrc(p1.B + b_row0 * p1.ldb, (p1.b_rows - b_row0) * p1.ldb);
   const __amdgpu_buffer_rsrc_t rb2 = make_rsrc(p2.B + b_row0 * p2.ldb, (p2.b_rows - b_row0) * p2.ldb);
 
-  // Fetch cursor: the stage issued next (tile, pair, stage).
+  // Fetch cursor: the stage issued next (tile, pair, stage). The loads pick
+  // their operand pair with selects, not branches, so that they stay in the
+  // MFMA block and can be interleaved with it; the cursor advances after it.
   int ft = a_tile_begin, fp = 0, fs = 0;
   auto issue = [&](char* dst) {
     const bool valid = ft < a_tile_end;
+    const bool second = fp != 0;
     const int64_t a_row0 = (int64_t)(valid ? ft : a_tile_begin) * TM;
-    if (fp == 0)
-      dma_stage<TM, TN>(dst, make_rsrc(p1.A + a_row0 * p1.lda, (p1.a_rows - a_row0) * p1.lda), rb1, la1, lb1, p1.lda,
-                        p1.ldb, fs * kStageBytes, p1.kbytes, valid, wave, lane);
-    else
-      dma_stage<TM, TN>(dst, make_rsrc(p2.A + a_row0 * p2.lda, (p2.a_rows - a_row0) * p2.lda), rb2, la2, lb2, p2.lda,
-                        p2.ldb, fs * kStageBytes, p2.kbytes, valid, wave, lane);
-    if (++fs == (fp == 0 ? ks1 : ks2)) {
-      fs = 0;
-      if (fp == 0 && ks2 > 0) {
-        fp = 1;
-      } else {
-        fp = 0;
-        ++ft;
-      }
-    }
+    const char* A = second ? p2.A : p1.A;
+    const int64_t lda = second ? p2.lda : p1.lda, ldb = second ? p2.ldb : p1.ldb;
+    const int64_t a_rows = second ? p2.a_rows : p1.a_rows;
+    dma_stage<TM, TN>(dst, make_rsrc(A + a_row0 * lda, (a_rows - a_row0) * lda), second ? rb2 : rb1,
+                      second ? la2 : la1, second ? lb2 : lb1, lda, ldb, fs * kStageBytes,
+                      second ? p2.kbytes : p1.kbytes, valid, wave, lane);
+  };
+  auto advance = [&] {
+    const bool wrap = fs + 1 == (fp == 0 ? ks1 : ks2);
+    const int nfp = (fp == 0 && ks2 > 0) ? 1 : 0;
+    ft += (wrap && nfp == 0) ? 1 : 0;
+    fs = wrap ? 0 : fs + 1;
+    fp = wrap ? nfp : fp;
   };
 
   // One ring step on buffer `cur`: wait for its loads (with three buffers the
@@ -205,8 +219,8 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
   auto step = [&](floatx16(&acc)[MB][NB], char* cur, char* refill) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(NBUF == 3 ? kDma : 0));
     lds_barrier();
-    issue(refill);
-    mma_ring_stage<kBf16>(acc, cur, a_off, b_off, colx);
+    mma_ring_stage<kBf16, MB, NB, kDma>(acc, cur, a_off, b_off, colx, [&] { issue(refill); });
+    advance();
   };
   // Run `ks` stages into `acc` starting with ring position `rot`.
   auto run = [&](floatx16(&acc)[MB][NB], int ks, int rot) {
@@ -261,8 +275,12 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
   floatx16 acc1[MB][NB], acc2[MB][NB];
   zero_acc(acc1);
   zero_acc(acc2);
-  issue(lds.b0);                    // stage 0
-  if (NBUF == 3) issue(lds.b1);     // stage 1
+  issue(lds.b0);  // stage 0
+  advance();
+  if (NBUF == 3) {  // stage 1
+    issue(lds.b1);
+    advance();
+  }
   int rot = 0;
   for (int tile = a_tile_begin; tile < a_tile_end; ++tile) {
     run(acc1, ks1, rot);
