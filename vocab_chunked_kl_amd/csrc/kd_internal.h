@@ -10,9 +10,16 @@
 
 namespace kd {
 
-// Logit tile: 256 vocabulary rows x 128 tokens per workgroup (4 waves, 2 x 2).
+// Logit tile: 256 vocabulary rows x 128 tokens per workgroup, split over
+// kLogitWM x kLogitWN waves (vocabulary x tokens).
 constexpr int kTileV = 256;
 constexpr int kTileT = 128;
+#ifndef KD_LOGIT_WM
+#define KD_LOGIT_WM 4
+#endif
+constexpr int kLogitWM = KD_LOGIT_WM;
+constexpr int kLogitWN = 2;
+constexpr int kLogitThreads = 64 * kLogitWM * kLogitWN;
 // dh tile: 256 tokens x 128 hidden units.
 constexpr int kTileDhT = 256;
 constexpr int kTileDhD = 128;

@@ -101,16 +101,17 @@ __device__ __forceinline__ void merge_record(float& ms, float& ls, float& mt, fl
 // the log-sum-exps, first JSD sweep), kModeJSD (mixture sums given the LSEs).
 // ---------------------------------------------------------------------------
 template <bool kBf16, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void fwd_kernel(LogitArgs a) {
-  constexpr int TM = kTileV, TN = kTileT, MB = TM / 64, NB = TN / 64;
+__global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
+  constexpr int TM = kTileV, TN = kTileT, WM = kLogitWM, WN = kLogitWN;
+  constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
   KD_RING_LDS(TM, TN);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
   block_coords(L, a.n_tok_tiles, a.n_splits, tt, sp);
   const int vt0 = sp * a.tiles_per_split;
   const int vt1 = min(vt0 + a.tiles_per_split, a.n_vtiles);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
-  const int64_t tok0 = (int64_t)tt * TN + wn * (TN / 2);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave % WM, wn = wave / WM;
+  const int64_t tok0 = (int64_t)tt * TN + wn * (TN / WN);
   const float c2 = a.c2;
 
   float ms[NB], ls[NB], mt[NB], lt[NB], ac[NB];
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(LogitArgs a) {
   const float beta = a.beta, omb = 1.f - a.beta;
 
   auto epi = [&](int vt, auto& zs, auto& zt) {
-    const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / 2);
+    const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
     const bool full = (int64_t)(vt + 1) * TM <= a.V;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(LogitArgs a) {
       }
     }
   };
-  sweep<kBf16, TM, TN>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<kBf16, TM, TN, WM, WN>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 
   // Lanes l and l ^ 32 hold the same tokens (other vocabulary rows).
 #pragma unroll
@@ -212,36 +213,49 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_kernel(LogitArgs a) {
       merge_record<MODE>(ms[nb], ls[nb], mt[nb], lt[nb], ac[nb], oms, ols, omt, olt, oac);
     }
   }
-  // Waves wm = 0 and 1 hold the two vocabulary halves of the same tokens.
-  __shared__ float red[kFwdFields * TN];
-  if (wm == 1 && lane < 32) {
+  // The WM waves with the same wn hold the vocabulary slices of the same
+  // tokens: waves wm > 0 publish their records, wave wm = 0 merges them.
+  constexpr int kF = MODE == kModeJSD ? kJsdFields : kFwdFields;
+  __shared__ float red[(WM > 1 ? WM - 1 : 1) * kF * TN];
+  if (wm > 0 && lane < 32) {
+    float* r = red + (wm - 1) * kF * TN;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = wn * (TN / 2) + nb * 32 + lane;
-      red[0 * TN + col] = ms[nb];
-      red[1 * TN + col] = ls[nb];
-      red[2 * TN + col] = mt[nb];
-      red[3 * TN + col] = lt[nb];
-      red[4 * TN + col] = ac[nb];
+      const int col = wn * (TN / WN) + nb * 32 + lane;
+      if constexpr (MODE == kModeJSD) {
+        r[0 * TN + col] = ls[nb];
+        r[1 * TN + col] = lt[nb];
+      } else {
+        r[0 * TN + col] = ms[nb];
+        r[1 * TN + col] = ls[nb];
+        r[2 * TN + col] = mt[nb];
+        r[3 * TN + col] = lt[nb];
+        r[4 * TN + col] = ac[nb];
+      }
     }
   }
   __syncthreads();
   if (wm == 0 && lane < 32) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = wn * (TN / 2) + nb * 32 + lane;
+      const int col = wn * (TN / WN) + nb * 32 + lane;
       const int64_t n = (int64_t)tt * TN + col;
-      if constexpr (MODE == kModeJSD) {
-        ls[nb] += red[1 * TN + col];
-        lt[nb] += red[3 * TN + col];
-        if (n < a.N) {
+#pragma unroll
+      for (int w = 0; w < WM - 1; ++w) {
+        const float* r = red + w * kF * TN;
+        if constexpr (MODE == kModeJSD) {
+          ls[nb] += r[0 * TN + col];
+          lt[nb] += r[1 * TN + col];
+        } else {
+          merge_record<MODE>(ms[nb], ls[nb], mt[nb], lt[nb], ac[nb], r[0 * TN + col], r[1 * TN + col],
+                             r[2 * TN + col], r[3 * TN + col], r[4 * TN + col]);
+        }
+      }
+      if (n < a.N) {
+        if constexpr (MODE == kModeJSD) {
           a.part[(0 * (int64_t)a.n_splits + sp) * a.N + n] = ls[nb];
           a.part[(1 * (int64_t)a.n_splits + sp) * a.N + n] = lt[nb];
-        }
-      } else {
-        merge_record<MODE>(ms[nb], ls[nb], mt[nb], lt[nb], ac[nb], red[0 * TN + col], red[1 * TN + col],
-                           red[2 * TN + col], red[3 * TN + col], red[4 * TN + col]);
-        if (n < a.N) {
+        } else {
           a.part[(0 * (int64_t)a.n_splits + sp) * a.N + n] = ms[nb];
           a.part[(1 * (int64_t)a.n_splits + sp) * a.N + n] = ls[nb];
           a.part[(2 * (int64_t)a.n_splits + sp) * a.N + n] = mt[nb];
@@ -293,16 +307,17 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 // Backward, step 1: G[n, v - c0] = grad[n] / tau * dloss_n / ds_v for one chunk.
 // ---------------------------------------------------------------------------
 template <bool kBf16, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void bwdg_kernel(LogitArgs a) {
-  constexpr int TM = kTileV, TN = kTileT, MB = TM / 64, NB = TN / 64;
+__global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
+  constexpr int TM = kTileV, TN = kTileT, WM = kLogitWM, WN = kLogitWN;
+  constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
   KD_RING_LDS(TM, TN);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
   block_coords(L, a.n_tok_tiles, a.n_splits, tt, sp);
   const int vt0 = a.vt_offset + sp * a.tiles_per_split;
   const int vt1 = min(vt0 + a.tiles_per_split, a.vt_offset + a.n_vtiles);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
-  const int64_t tok0 = (int64_t)tt * TN + wn * (TN / 2);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave % WM, wn = wave / WM;
+  const int64_t tok0 = (int64_t)tt * TN + wn * (TN / WN);
   const float c2 = a.c2, inv_tau = a.inv_tau, beta = a.beta, omb = 1.f - a.beta;
 
   float Ls2[NB], Lt2[NB], K1[NB], gsc[NB];
@@ -321,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwdg_kernel(LogitArgs a) {
   }
 
   auto epi = [&](int vt, auto& zs, auto& zt) {
-    const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / 2);
+    const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int64_t n = tok0 + nb * 32 + (lane & 31);
@@ -365,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwdg_kernel(LogitArgs a) {
         }
     }
   };
-  sweep<kBf16, TM, TN>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<kBf16, TM, TN, WM, WN>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -431,16 +446,16 @@ __global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
         }
       }
   };
-  sweep<kBf16, TM, TN>(a.p, none, (int64_t)dt * TN, tt, tt + 1, lds, epi);
+  sweep<kBf16, TM, TN, 2, 2>(a.p, none, (int64_t)dt * TN, tt, tt + 1, lds, epi);
 }
 
 template <bool kBf16>
 hipError_t launch_fwd_mode(int mode, dim3 grid, const LogitArgs& la, hipStream_t st) {
   switch (mode) {
-    case kModeFKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeFKL>), grid, dim3(kThreads), 0, st, la); break;
-    case kModeRKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeRKL>), grid, dim3(kThreads), 0, st, la); break;
-    case kModeLSE: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeLSE>), grid, dim3(kThreads), 0, st, la); break;
-    default: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeJSD>), grid, dim3(kThreads), 0, st, la); break;
+    case kModeFKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeFKL>), grid, dim3(kLogitThreads), 0, st, la); break;
+    case kModeRKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeRKL>), grid, dim3(kLogitThreads), 0, st, la); break;
+    case kModeLSE: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeLSE>), grid, dim3(kLogitThreads), 0, st, la); break;
+    default: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeJSD>), grid, dim3(kLogitThreads), 0, st, la); break;
   }
   return hipGetLastError();
 }
@@ -448,9 +463,9 @@ hipError_t launch_fwd_mode(int mode, dim3 grid, const LogitArgs& la, hipStream_t
 template <bool kBf16>
 hipError_t launch_bwdg_mode(int mode, dim3 grid, const LogitArgs& la, hipStream_t st) {
   switch (mode) {
-    case kModeFKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeFKL>), grid, dim3(kThreads), 0, st, la); break;
-    case kModeRKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeRKL>), grid, dim3(kThreads), 0, st, la); break;
-    default: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeJSD>), grid, dim3(kThreads), 0, st, la); break;
+    case kModeFKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeFKL>), grid, dim3(kLogitThreads), 0, st, la); break;
+    case kModeRKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeRKL>), grid, dim3(kLogitThreads), 0, st, la); break;
+    default: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeJSD>), grid, dim3(kLogitThreads), 0, st, la); break;
   }
   return hipGetLastError();
 }

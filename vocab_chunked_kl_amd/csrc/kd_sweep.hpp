@@ -54,17 +54,18 @@ struct Ring {
   static constexpr int kBytes = (TM + TN) * kStageBytes;
 };
 
-// Issue the direct-to-LDS loads of one stage (this wave's share: TM/32 + TN/32
-// instructions of 8 rows each). `a_base` / `b_base`: resources starting at the
-// tile's first row; `lane_row` = (lane >> 3) * ld for each operand; `cterm[i]`:
-// this lane's chunk byte offset for instruction index i & 3. A lane whose
-// chunk lies at or past the row length, or every lane when `valid` is false,
-// reads past the resource end and writes zeros.
-template <int TM, int TN>
+// Issue the direct-to-LDS loads of one stage (this wave's share of NW waves:
+// (TM + TN) / (8 NW) instructions of 8 rows each). `a_base` / `b_base`:
+// resources starting at the tile's first row; `lane_row` = (lane >> 3) * ld
+// for each operand; a lane whose chunk lies at or past the row length, or
+// every lane when `valid` is false, reads past the resource end and writes
+// zeros.
+template <int TM, int TN, int NW>
 __device__ __forceinline__ void dma_stage(char* dst, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           int32_t a_lane_row, int32_t b_lane_row, int64_t lda, int64_t ldb,
                                           int32_t kbyte0, int32_t kbytes, bool valid, int wave, int lane) {
-  constexpr int QA = TM / 32, QB = TN / 32;  // instructions per wave
+  constexpr int QA = TM / (8 * NW), QB = TN / (8 * NW);  // instructions per wave
+  static_assert(QA * 8 * NW == TM && QB * 8 * NW == TN, "tile rows must split evenly over the waves");
   const int c_lo = lane & 7, c_hi = lane >> 3;
 #pragma unroll
   for (int i = 0; i < QA; ++i) {
@@ -165,18 +166,23 @@ struct RingLds {
   char* b2;
 };
 
-template <bool kBf16, int TM, int TN, class Epi, int NBUF = 3>
+// WM x WN waves: wave w owns rows (w % WM) * TM / WM .. of the A tile and rows
+// (w / WM) * TN / WN .. of the B tile; its accumulators are [MB][NB] 32 x 32
+// MFMA blocks, MB = TM / (32 WM), NB = TN / (32 WN).
+template <bool kBf16, int TM, int TN, int WM, int WN, class Epi, int NBUF = 3>
 __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, int64_t b_row0, int a_tile_begin,
                                       int a_tile_end, const RingLds<TM, TN>& lds, Epi&& epi) {
   static_assert(NBUF == 2 || NBUF == 3, "ring of two or three stage buffers");
-  constexpr int MB = TM / 64, NB = TN / 64;
-  constexpr int kDma = TM / 32 + TN / 32;  // direct-to-LDS loads per wave per stage
+  constexpr int NW = WM * WN;
+  constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
+  static_assert(MB * 32 * WM == TM && NB * 32 * WN == TN, "wave tiles must be multiples of 32");
+  constexpr int kDma = (TM + TN) / (8 * NW);  // direct-to-LDS loads per wave per stage
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r32 = lane & 31;
-  const int a_off = ((wave & 1) * (TM / 2) + r32) * kStageBytes;
-  const int b_off = (TM + (wave >> 1) * (TN / 2) + r32) * kStageBytes;
+  const int a_off = ((wave % WM) * (TM / WM) + r32) * kStageBytes;
+  const int b_off = (TM + (wave / WM) * (TN / WN) + r32) * kStageBytes;
   int colx[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) colx[j] = ((2 * j + (lane >> 5)) ^ lds_swz(r32)) * 16;
@@ -201,7 +207,7 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
     const char* A = second ? p2.A : p1.A;
     const int64_t lda = second ? p2.lda : p1.lda, ldb = second ? p2.ldb : p1.ldb;
     const int64_t a_rows = second ? p2.a_rows : p1.a_rows;
-    dma_stage<TM, TN>(dst, make_rsrc(A + a_row0 * lda, (a_rows - a_row0) * lda), second ? rb2 : rb1,
+    dma_stage<TM, TN, NW>(dst, make_rsrc(A + a_row0 * lda, (a_rows - a_row0) * lda), second ? rb2 : rb1,
                       second ? la2 : la1, second ? lb2 : lb1, lda, ldb, fs * kStageBytes,
                       second ? p2.kbytes : p1.kbytes, valid, wave, lane);
   };

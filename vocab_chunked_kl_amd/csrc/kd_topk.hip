@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_sweep_kernel(TopkArgs a) {
       if (!any) break;
     }
   };
-  sweep<true, TM, TN, decltype(epi)&, 2>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<true, TM, TN, 2, 2, decltype(epi)&, 2>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 
   // LSE partials: lanes l and l^32, then the two vocabulary-half waves
 #pragma unroll
