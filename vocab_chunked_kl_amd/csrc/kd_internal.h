@@ -20,9 +20,23 @@ constexpr int kTileT = 128;
 constexpr int kLogitWM = KD_LOGIT_WM;
 constexpr int kLogitWN = 2;
 constexpr int kLogitThreads = 64 * kLogitWM * kLogitWN;
-// dh tile: 256 tokens x 128 hidden units.
+// dh tile: 256 tokens x kTileDhD hidden units over kDhWM x kDhWN waves, with
+// a ring of kDhBuf LDS stages.
 constexpr int kTileDhT = 256;
-constexpr int kTileDhD = 128;
+#ifndef KD_DH_TILE_D
+#define KD_DH_TILE_D 256
+#endif
+constexpr int kTileDhD = KD_DH_TILE_D;
+#ifndef KD_DH_WM
+#define KD_DH_WM 4
+#endif
+#ifndef KD_DH_WN
+#define KD_DH_WN 2
+#endif
+constexpr int kDhWM = KD_DH_WM;
+constexpr int kDhWN = KD_DH_WN;
+constexpr int kDhThreads = 64 * kDhWM * kDhWN;
+constexpr int kDhBuf = kTileDhD > 128 ? 2 : 3;
 // Number of token tiles grouped together in the block order (L2 reuse).
 #ifndef KD_TOK_GROUP
 #define KD_TOK_GROUP 8

@@ -42,6 +42,13 @@ constexpr float kNegInf = -INFINITY;
   __shared__ __attribute__((aligned(16))) char ring2_[Ring<TM, TN>::kBytes]; \
   const RingLds<TM, TN> lds{ring0_, ring1_, ring2_}
 
+// A ring of NBUF (2 or 3) stage buffers.
+#define KD_RING_LDS_N(TM, TN, NBUF)                                                    \
+  __shared__ __attribute__((aligned(16))) char ring0_[Ring<TM, TN>::kBytes];          \
+  __shared__ __attribute__((aligned(16))) char ring1_[Ring<TM, TN>::kBytes];          \
+  __shared__ __attribute__((aligned(16))) char ring2_[(NBUF) > 2 ? Ring<TM, TN>::kBytes : 16]; \
+  const RingLds<TM, TN> lds{ring0_, ring1_, ring2_}
+
 struct LogitArgs {
   PairDesc ps, pt;   // (W_s, h_s) and (W_t, h_t)
   int64_t N, V;
@@ -421,32 +428,46 @@ struct DhArgs {
 };
 
 template <bool kBf16>
-__global__ __launch_bounds__(kThreads, 1) void dh_kernel(DhArgs a) {
-  constexpr int TM = kTileDhT, TN = kTileDhD, MB = TM / 64, NB = TN / 64;
-  KD_RING_LDS(TM, TN);
+__global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
+  constexpr int TM = kTileDhT, TN = kTileDhD, WM = kDhWM, WN = kDhWN;
+  constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
+  KD_RING_LDS_N(TM, TN, kDhBuf);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, dt;
   block_coords(L, a.n_tok_tiles, a.n_d_tiles, tt, dt);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave & 1, wn = wave >> 1;
-  PairDesc none = a.p;
-  none.kbytes = 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave % WM, wn = wave / WM;
+  // Read-modify-write of dh, one 32-row slice at a time: all loads of the
+  // slice are issued before its stores, so they overlap instead of forming a
+  // chain of dependent round trips.
   auto epi = [&](int tile, auto& acc, auto&) {
+    const int64_t d0 = (int64_t)dt * TN + wn * (TN / WN) + (lane & 31);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int mb = 0; mb < MB; ++mb) {
+      const int64_t n0 = (int64_t)tile * TM + wm * (TM / WM) + mb * 32;
+      float old[NB][16];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int64_t d = (int64_t)dt * TN + wn * (TN / 2) + nb * 32 + (lane & 31);
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) old[nb][r] = 0.f;
+      if (!a.first) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t n = n0 + acc_row(r, lane), d = d0 + nb * 32;
+            if (n < a.N && d < a.d_s) old[nb][r] = a.dh[n * a.d_s + d];
+          }
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t n = (int64_t)tile * TM + wm * (TM / 2) + mb * 32 + acc_row(r, lane);
-          if (n < a.N && d < a.d_s) {
-            float* o = a.dh + n * a.d_s + d;
-            *o = a.first ? acc[mb][nb][r] : *o + acc[mb][nb][r];
-          }
+          const int64_t n = n0 + acc_row(r, lane), d = d0 + nb * 32;
+          if (n < a.N && d < a.d_s) a.dh[n * a.d_s + d] = old[nb][r] + acc[mb][nb][r];
         }
-      }
+    }
   };
-  sweep<kBf16, TM, TN, 2, 2>(a.p, none, (int64_t)dt * TN, tt, tt + 1, lds, epi);
+  sweep<kBf16, TM, TN, WM, WN, decltype(epi)&, kDhBuf, false>(a.p, a.p, (int64_t)dt * TN, tt, tt + 1, lds, epi);
 }
 
 template <bool kBf16>
@@ -602,9 +623,9 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
     da.first = c0 == 0;
     const dim3 dgrid(n_tok_tiles_dh * n_d_tiles);
     if (p.bf16)
-      hipLaunchKernelGGL(dh_kernel<true>, dgrid, dim3(kThreads), 0, st, da);
+      hipLaunchKernelGGL(dh_kernel<true>, dgrid, dim3(kDhThreads), 0, st, da);
     else
-      hipLaunchKernelGGL(dh_kernel<false>, dgrid, dim3(kThreads), 0, st, da);
+      hipLaunchKernelGGL(dh_kernel<false>, dgrid, dim3(kDhThreads), 0, st, da);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

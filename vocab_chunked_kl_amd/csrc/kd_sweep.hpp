@@ -19,6 +19,10 @@
 
 #include "kd_device.hpp"
 
+#ifndef KD_SPAN2
+#define KD_SPAN2 3
+#endif
+
 namespace kd {
 
 struct PairDesc {
@@ -91,17 +95,16 @@ __device__ __forceinline__ void dma_stage(char* dst, __amdgpu_buffer_rsrc_t ra, 
 // counts, hence the compile-time recursion over MFMA index M): the LDS reads
 // of sub-step 0 first; then each MFMA is followed by at most one LDS read of
 // the next sub-step, and the `kLoads` direct-to-LDS loads are spread evenly
-// over the first three quarters of the MFMAs.
-template <int kMf, int kRd, int kLoads, int M = 0>
+// over the first kSpan MFMAs.
+template <int kMf, int kRd, int kLoads, int kSpan, int M = 0>
 __device__ __forceinline__ void pin_stage_order() {
   if constexpr (M == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kRd, 0);
   if constexpr (M < 4 * kMf) {
-    constexpr int kSpan = 3 * kMf;
     constexpr int lo = M * kLoads / kSpan, hi = (M + 1) * kLoads / kSpan;
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
     if constexpr (M < 3 * kMf && (M % kMf) < kRd) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     if constexpr (M < kSpan && hi > lo) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, hi - lo, 0);
-    pin_stage_order<kMf, kRd, kLoads, M + 1>();
+    pin_stage_order<kMf, kRd, kLoads, kSpan, M + 1>();
   }
 }
 
@@ -111,7 +114,7 @@ __device__ __forceinline__ void pin_stage_order() {
 // byte offset for sub-step j. `issue` emits the direct-to-LDS loads of a later
 // stage; they are spread between the MFMAs (a burst of loads right after the
 // barrier would stall the wave's issue while the address unit drains them).
-template <bool kBf16, int MB, int NB, int kLoads, class Issue>
+template <bool kBf16, int MB, int NB, int kLoads, int kSpanQ, class Issue>
 __device__ __forceinline__ void mma_ring_stage(floatx16 (&acc)[MB][NB], const char* cur, int a_off, int b_off,
                                                const int (&colx)[4], Issue&& issue) {
   u32x4 fa[2][MB], fb[2][NB];
@@ -154,7 +157,7 @@ __device__ __forceinline__ void mma_ring_stage(floatx16 (&acc)[MB][NB], const ch
   rd(1, 3);
   mm(0);
   mm(1);
-  pin_stage_order<kMf, kRd, kLoads>();
+  pin_stage_order<kMf, kRd, kLoads, kSpanQ == 0 ? 1 : kSpanQ * kMf>();
 }
 
 // Shared LDS of the stage ring: three separate objects, so that the compiler
@@ -169,7 +172,9 @@ struct RingLds {
 // WM x WN waves: wave w owns rows (w % WM) * TM / WM .. of the A tile and rows
 // (w / WM) * TN / WN .. of the B tile; its accumulators are [MB][NB] 32 x 32
 // MFMA blocks, MB = TM / (32 WM), NB = TN / (32 WN).
-template <bool kBf16, int TM, int TN, int WM, int WN, class Epi, int NBUF = 3>
+// kDual = false: one operand pair only (p2 is ignored, the epilogue gets acc1
+// twice and no second accumulator is allocated).
+template <bool kBf16, int TM, int TN, int WM, int WN, class Epi, int NBUF = 3, bool kDual = true>
 __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, int64_t b_row0, int a_tile_begin,
                                       int a_tile_end, const RingLds<TM, TN>& lds, Epi&& epi) {
   static_assert(NBUF == 2 || NBUF == 3, "ring of two or three stage buffers");
@@ -188,7 +193,7 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
   for (int j = 0; j < 4; ++j) colx[j] = ((2 * j + (lane >> 5)) ^ lds_swz(r32)) * 16;
 
   const int ks1 = (p1.kbytes + kStageBytes - 1) / kStageBytes;
-  const int ks2 = (p2.kbytes + kStageBytes - 1) / kStageBytes;
+  const int ks2 = kDual ? (p2.kbytes + kStageBytes - 1) / kStageBytes : 0;
   if (a_tile_end <= a_tile_begin || ks1 == 0) return;
 
   const int32_t la1 = (int32_t)((lane >> 3) * p1.lda), la2 = (int32_t)((lane >> 3) * p2.lda);
@@ -202,7 +207,7 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
   int ft = a_tile_begin, fp = 0, fs = 0;
   auto issue = [&](char* dst) {
     const bool valid = ft < a_tile_end;
-    const bool second = fp != 0;
+    const bool second = kDual && fp != 0;
     const int64_t a_row0 = (int64_t)(valid ? ft : a_tile_begin) * TM;
     const char* A = second ? p2.A : p1.A;
     const int64_t lda = second ? p2.lda : p1.lda, ldb = second ? p2.ldb : p1.ldb;
@@ -225,7 +230,7 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
   auto step = [&](floatx16(&acc)[MB][NB], char* cur, char* refill) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(NBUF == 3 ? kDma : 0));
     lds_barrier();
-    mma_ring_stage<kBf16, MB, NB, kDma>(acc, cur, a_off, b_off, colx, [&] { issue(refill); });
+    mma_ring_stage<kBf16, MB, NB, kDma, NBUF == 3 ? 3 : KD_SPAN2>(acc, cur, a_off, b_off, colx, [&] { issue(refill); });
     advance();
   };
   // Run `ks` stages into `acc` starting with ring position `rot`.
@@ -278,9 +283,9 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
     }
   };
 
-  floatx16 acc1[MB][NB], acc2[MB][NB];
+  floatx16 acc1[MB][NB], acc2[kDual ? MB : 1][kDual ? NB : 1];
   zero_acc(acc1);
-  zero_acc(acc2);
+  if constexpr (kDual) zero_acc(acc2);
   issue(lds.b0);  // stage 0
   advance();
   if (NBUF == 3) {  // stage 1
@@ -291,13 +296,17 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
   for (int tile = a_tile_begin; tile < a_tile_end; ++tile) {
     run(acc1, ks1, rot);
     rot = (rot + ks1) % NBUF;
-    if (ks2 > 0) {
-      run(acc2, ks2, rot);
-      rot = (rot + ks2) % NBUF;
+    if constexpr (kDual) {
+      if (ks2 > 0) {
+        run(acc2, ks2, rot);
+        rot = (rot + ks2) % NBUF;
+      }
+      epi(tile, acc1, acc2);
+      zero_acc(acc2);
+    } else {
+      epi(tile, acc1, acc1);
     }
-    epi(tile, acc1, acc2);
     zero_acc(acc1);
-    zero_acc(acc2);
   }
   // drain the loads issued past the end before the LDS is reused
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
