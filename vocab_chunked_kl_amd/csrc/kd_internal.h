@@ -10,10 +10,24 @@
 
 namespace kd {
 
-// Logit tile: 256 vocabulary rows x 128 tokens per workgroup, split over
-// kLogitWM x kLogitWN waves (vocabulary x tokens).
+// Logit tile: 256 vocabulary rows x kTileT tokens per workgroup, split over
+// kLogitWM x kLogitWN waves (vocabulary x tokens), with a ring of kLogitBuf
+// LDS stages.
 constexpr int kTileV = 256;
-constexpr int kTileT = 128;
+#ifndef KD_TILE_T
+#define KD_TILE_T 128
+#endif
+constexpr int kTileT = KD_TILE_T;
+#ifndef KD_LOGIT_RB
+#define KD_LOGIT_RB 128
+#endif
+#ifndef KD_LOGIT_BUF
+#define KD_LOGIT_BUF 3
+#endif
+constexpr int kLogitRB = KD_LOGIT_RB;   // bytes of K per LDS stage row
+constexpr int kLogitBuf = KD_LOGIT_BUF;
+// Token tile of the top-k sweep (its per-token selection state lives in LDS).
+constexpr int kTopkT = 128;
 #ifndef KD_LOGIT_WM
 #define KD_LOGIT_WM 4
 #endif
@@ -36,7 +50,14 @@ constexpr int kTileDhD = KD_DH_TILE_D;
 constexpr int kDhWM = KD_DH_WM;
 constexpr int kDhWN = KD_DH_WN;
 constexpr int kDhThreads = 64 * kDhWM * kDhWN;
-constexpr int kDhBuf = kTileDhD > 128 ? 2 : 3;
+#ifndef KD_DH_RB
+#define KD_DH_RB 128
+#endif
+constexpr int kDhRB = KD_DH_RB;
+#ifndef KD_DH_BUF
+#define KD_DH_BUF (kTileDhD > 128 ? 2 : 3)
+#endif
+constexpr int kDhBuf = KD_DH_BUF;
 // Number of token tiles grouped together in the block order (L2 reuse).
 #ifndef KD_TOK_GROUP
 #define KD_TOK_GROUP 8

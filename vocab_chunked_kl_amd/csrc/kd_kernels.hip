@@ -35,19 +35,24 @@ namespace {
 
 constexpr float kNegInf = -INFINITY;
 
-// The three LDS stage buffers of the sweep ring, as separate objects.
-#define KD_RING_LDS(TM, TN)                                                   \
-  __shared__ __attribute__((aligned(16))) char ring0_[Ring<TM, TN>::kBytes]; \
-  __shared__ __attribute__((aligned(16))) char ring1_[Ring<TM, TN>::kBytes]; \
-  __shared__ __attribute__((aligned(16))) char ring2_[Ring<TM, TN>::kBytes]; \
-  const RingLds<TM, TN> lds{ring0_, ring1_, ring2_}
+// The NBUF (<= 6) LDS stage buffers of a sweep ring, as separate objects.
+#define KD_RING_LDS_N(TM, TN, RB, NBUF)                                                             \
+  __shared__ __attribute__((aligned(16))) char ring0_[Ring<TM, TN, RB>::kBytes];                    \
+  __shared__ __attribute__((aligned(16))) char ring1_[Ring<TM, TN, RB>::kBytes];                    \
+  __shared__ __attribute__((aligned(16))) char ring2_[(NBUF) > 2 ? Ring<TM, TN, RB>::kBytes : 16]; \
+  __shared__ __attribute__((aligned(16))) char ring3_[(NBUF) > 3 ? Ring<TM, TN, RB>::kBytes : 16]; \
+  __shared__ __attribute__((aligned(16))) char ring4_[(NBUF) > 4 ? Ring<TM, TN, RB>::kBytes : 16]; \
+  __shared__ __attribute__((aligned(16))) char ring5_[(NBUF) > 5 ? Ring<TM, TN, RB>::kBytes : 16]; \
+  const RingLds<NBUF> lds = ring_of<NBUF>(ring0_, ring1_, ring2_, ring3_, ring4_, ring5_)
 
-// A ring of NBUF (2 or 3) stage buffers.
-#define KD_RING_LDS_N(TM, TN, NBUF)                                                    \
-  __shared__ __attribute__((aligned(16))) char ring0_[Ring<TM, TN>::kBytes];          \
-  __shared__ __attribute__((aligned(16))) char ring1_[Ring<TM, TN>::kBytes];          \
-  __shared__ __attribute__((aligned(16))) char ring2_[(NBUF) > 2 ? Ring<TM, TN>::kBytes : 16]; \
-  const RingLds<TM, TN> lds{ring0_, ring1_, ring2_}
+template <int NBUF>
+__device__ __forceinline__ RingLds<NBUF> ring_of(char* r0, char* r1, char* r2, char* r3, char* r4, char* r5) {
+  char* all[6] = {r0, r1, r2, r3, r4, r5};
+  RingLds<NBUF> r;
+#pragma unroll
+  for (int i = 0; i < NBUF; ++i) r.b[i] = all[i];
+  return r;
+}
 
 struct LogitArgs {
   PairDesc ps, pt;   // (W_s, h_s) and (W_t, h_t)
@@ -111,7 +116,7 @@ template <bool kBf16, int MODE>
 __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
   constexpr int TM = kTileV, TN = kTileT, WM = kLogitWM, WN = kLogitWN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
-  KD_RING_LDS(TM, TN);
+  KD_RING_LDS_N(TM, TN, kLogitRB, kLogitBuf);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
   block_coords(L, a.n_tok_tiles, a.n_splits, tt, sp);
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
       }
     }
   };
-  sweep<kBf16, TM, TN, WM, WN>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<kBf16, TM, TN, WM, WN, kLogitBuf, kLogitRB, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 
   // Lanes l and l ^ 32 hold the same tokens (other vocabulary rows).
 #pragma unroll
@@ -317,7 +322,7 @@ template <bool kBf16, int MODE>
 __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
   constexpr int TM = kTileV, TN = kTileT, WM = kLogitWM, WN = kLogitWN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
-  KD_RING_LDS(TM, TN);
+  KD_RING_LDS_N(TM, TN, kLogitRB, kLogitBuf);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
   block_coords(L, a.n_tok_tiles, a.n_splits, tt, sp);
@@ -387,7 +392,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
         }
     }
   };
-  sweep<kBf16, TM, TN, WM, WN>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<kBf16, TM, TN, WM, WN, kLogitBuf, kLogitRB, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -431,7 +436,7 @@ template <bool kBf16>
 __global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
   constexpr int TM = kTileDhT, TN = kTileDhD, WM = kDhWM, WN = kDhWN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
-  KD_RING_LDS_N(TM, TN, kDhBuf);
+  KD_RING_LDS_N(TM, TN, kDhRB, kDhBuf);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, dt;
   block_coords(L, a.n_tok_tiles, a.n_d_tiles, tt, dt);
@@ -467,7 +472,7 @@ __global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
         }
     }
   };
-  sweep<kBf16, TM, TN, WM, WN, decltype(epi)&, kDhBuf, false>(a.p, a.p, (int64_t)dt * TN, tt, tt + 1, lds, epi);
+  sweep<kBf16, TM, TN, WM, WN, kDhBuf, kDhRB, false>(a.p, a.p, (int64_t)dt * TN, tt, tt + 1, lds, epi);
 }
 
 template <bool kBf16>

@@ -1,5 +1,5 @@
 // kd_sweep.hpp - the pipelined MFMA tile loop shared by the logit-rebuilding
-// kernels and the dh GEMM.
+// kernels, the top-k sweep and the dh GEMM.
 //
 // A block owns a fixed B tile (TN rows: a token tile for the logit kernels, a
 // d-tile of the transposed unembedding for dh) and walks a run of A tiles
@@ -11,19 +11,28 @@
 // both for the same (vocabulary, token) tile, as the block logit rebuild of
 // the Nitrobrew notes ("Nitrobrew 的两个动作") needs them side by side.
 //
-// Pipeline: a ring of three LDS stage buffers filled by direct-to-LDS buffer
-// loads (no staging registers, no LDS store instructions). While stage i is
-// multiplied, the loads of stages i+1 and i+2 are in flight; one barrier per
-// stage recycles the buffer read in the previous step.
+// Pipeline: a ring of NBUF LDS stage buffers (RB bytes of K per row each)
+// filled by direct-to-LDS buffer loads (no staging registers, no LDS store
+// instructions). While stage g is multiplied, the loads of stages g+1 ..
+// g+NBUF-2 are in flight and stage g+NBUF-1 is being issued; one barrier per
+// stage recycles the buffer read in the previous step. The stage sequence
+// (tile by tile: pair 1, then pair 2) runs on continuously through the ring.
 #pragma once
+
+#include <type_traits>
 
 #include "kd_device.hpp"
 
-#ifndef KD_SPAN2
-#define KD_SPAN2 3
-#endif
-
 namespace kd {
+
+// f(integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, class Fn>
+__device__ __forceinline__ void static_for(Fn&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 struct PairDesc {
   const char* A;      // [a_rows, K] row-major
@@ -46,48 +55,59 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // sched_group_barrier masks
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
 
-// LDS stage layout: [A tile: TM rows][B tile: TN rows], 128 bytes per row,
-// unpadded, with the 16-byte chunks of row R stored at slot (chunk ^ swz(R)),
-// swz(R) = (R & 7) ^ ((R >> 3) & 3). Direct-to-LDS loads write 64 lanes x 16
-// bytes contiguously (8 rows per instruction), and the XOR spreads the MFMA
-// fragment reads of 16 consecutive rows over all banks.
-__device__ __forceinline__ int lds_swz(int r) { return (r & 7) ^ ((r >> 3) & 3); }
+// LDS stage layout: [A tile: TM rows][B tile: TN rows], RB bytes per row,
+// unpadded, with the 16-byte chunks of row R stored at slot (chunk ^ swz(R)).
+// A direct-to-LDS load writes 64 lanes x 16 bytes contiguously (1024 / RB
+// rows); the XOR makes the MFMA fragment reads (16 consecutive rows at one
+// chunk per 16 lanes) hit 16 distinct 16-byte bank groups:
+//   RB = 128: swz(R) = (R & 7) ^ ((R >> 3) & 3)   (8 chunks, rows alternate halves)
+//   RB =  64: swz(R) = (R >> 2) & 3               (4 chunks, 4 rows per 256 bytes)
+template <int RB>
+struct RowFmt {
+  static_assert(RB == 64 || RB == 128, "64- or 128-byte stage rows");
+  static constexpr int kChunks = RB / 16;         // 16-byte chunks per row
+  static constexpr int kRowsPerLoad = 1024 / RB;  // rows per 64-lane direct-to-LDS load
+  static constexpr int kSub = RB / 32;            // MFMA k-substeps (32 bytes of K) per stage
+  __device__ static __forceinline__ int swz(int r) { return RB == 128 ? (r & 7) ^ ((r >> 3) & 3) : (r >> 2) & 3; }
+};
 
-template <int TM, int TN>
+template <int TM, int TN, int RB = 128>
 struct Ring {
-  static constexpr int kBytes = (TM + TN) * kStageBytes;
+  static constexpr int kBytes = (TM + TN) * RB;
 };
 
 // Issue the direct-to-LDS loads of one stage (this wave's share of NW waves:
-// (TM + TN) / (8 NW) instructions of 8 rows each). `a_base` / `b_base`:
-// resources starting at the tile's first row; `lane_row` = (lane >> 3) * ld
-// for each operand; a lane whose chunk lies at or past the row length, or
-// every lane when `valid` is false, reads past the resource end and writes
-// zeros.
-template <int TM, int TN, int NW>
+// (TM + TN) / (rows per load * NW) instructions). `ra` / `rb`: resources
+// starting at the tile's first row; `a_lane_row` / `b_lane_row`: this lane's
+// row-in-group times the row pitch. A lane whose chunk lies at or past the
+// row length, or every lane when `valid` is false, reads past the resource
+// end and writes zeros.
+template <int TM, int TN, int NW, int RB>
 __device__ __forceinline__ void dma_stage(char* dst, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                           int32_t a_lane_row, int32_t b_lane_row, int64_t lda, int64_t ldb,
                                           int32_t kbyte0, int32_t kbytes, bool valid, int wave, int lane) {
-  constexpr int QA = TM / (8 * NW), QB = TN / (8 * NW);  // instructions per wave
-  static_assert(QA * 8 * NW == TM && QB * 8 * NW == TN, "tile rows must split evenly over the waves");
-  const int c_lo = lane & 7, c_hi = lane >> 3;
+  using F = RowFmt<RB>;
+  constexpr int RPL = F::kRowsPerLoad;
+  constexpr int QA = TM / (RPL * NW), QB = TN / (RPL * NW);  // instructions per wave
+  static_assert(QA * RPL * NW == TM && QB * RPL * NW == TN, "tile rows must split evenly over the waves");
+  const int slot = lane % F::kChunks, rig = lane / F::kChunks;  // LDS slot, row in the load's group
 #pragma unroll
   for (int i = 0; i < QA; ++i) {
-    const int q = wave * QA + i;                 // 8-row group index within the tile
-    const int c = c_lo ^ c_hi ^ (q & 3);         // global chunk this lane moves
+    const int q = wave * QA + i;                   // row group index within the tile
+    const int c = slot ^ F::swz(q * RPL + rig);    // global chunk this lane moves
     const bool in = valid && (kbyte0 + c * 16 < kbytes);
-    const int32_t off = in ? a_lane_row + (int32_t)(8 * q * lda) + c * 16 + kbyte0 : 0x7FFFFFF0;
+    const int32_t off = in ? a_lane_row + (int32_t)(RPL * q * lda) + c * 16 + kbyte0 : 0x7FFFFFF0;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(dst + q * 1024), 16, off,
                                              0, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < QB; ++i) {
     const int q = wave * QB + i;
-    const int c = c_lo ^ c_hi ^ (q & 3);
+    const int c = slot ^ F::swz(q * RPL + rig);
     const bool in = valid && (kbyte0 + c * 16 < kbytes);
-    const int32_t off = in ? b_lane_row + (int32_t)(8 * q * ldb) + c * 16 + kbyte0 : 0x7FFFFFF0;
+    const int32_t off = in ? b_lane_row + (int32_t)(RPL * q * ldb) + c * 16 + kbyte0 : 0x7FFFFFF0;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (__attribute__((address_space(3))) void*)(dst + TM * kStageBytes + q * 1024), 16, off, 0, 0, 0);
+        rb, (__attribute__((address_space(3))) void*)(dst + TM * RB + q * 1024), 16, off, 0, 0, 0);
   }
 }
 
@@ -96,37 +116,39 @@ __device__ __forceinline__ void dma_stage(char* dst, __amdgpu_buffer_rsrc_t ra, 
 // of sub-step 0 first; then each MFMA is followed by at most one LDS read of
 // the next sub-step, and the `kLoads` direct-to-LDS loads are spread evenly
 // over the first kSpan MFMAs.
-template <int kMf, int kRd, int kLoads, int kSpan, int M = 0>
+template <int kSub, int kMf, int kRd, int kLoads, int kSpan, int M = 0>
 __device__ __forceinline__ void pin_stage_order() {
   if constexpr (M == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kRd, 0);
-  if constexpr (M < 4 * kMf) {
+  if constexpr (M < kSub * kMf) {
     constexpr int lo = M * kLoads / kSpan, hi = (M + 1) * kLoads / kSpan;
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    if constexpr (M < 3 * kMf && (M % kMf) < kRd) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    if constexpr (M < (kSub - 1) * kMf && (M % kMf) < kRd) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
     if constexpr (M < kSpan && hi > lo) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, hi - lo, 0);
-    pin_stage_order<kMf, kRd, kLoads, kSpan, M + 1>();
+    pin_stage_order<kSub, kMf, kRd, kLoads, kSpan, M + 1>();
   }
 }
 
-// MFMAs of one LDS stage for this wave: four k16 sub-steps, fragments double
+// MFMAs of one LDS stage for this wave: kSub k16 sub-steps, fragments double
 // buffered in registers so the reads of sub-step j+1 overlap the MFMAs of j.
 // a_off / b_off: this lane's row byte offset; colx[j]: its swizzled chunk
 // byte offset for sub-step j. `issue` emits the direct-to-LDS loads of a later
-// stage; they are spread between the MFMAs (a burst of loads right after the
-// barrier would stall the wave's issue while the address unit drains them).
-template <bool kBf16, int MB, int NB, int kLoads, int kSpanQ, class Issue>
+// stage; they are spread over the first three quarters of the MFMAs (a burst
+// right after the barrier would stall the wave while the address unit drains
+// them).
+template <bool kBf16, int MB, int NB, int kLoads, int RB, class Issue>
 __device__ __forceinline__ void mma_ring_stage(floatx16 (&acc)[MB][NB], const char* cur, int a_off, int b_off,
-                                               const int (&colx)[4], Issue&& issue) {
+                                               const int (&colx)[RowFmt<RB>::kSub], Issue&& issue) {
+  constexpr int kSub = RowFmt<RB>::kSub;
   u32x4 fa[2][MB], fb[2][NB];
-  auto rd = [&](int s, int j) {
+  auto rd = [&](int s, int j) __attribute__((always_inline)) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
-      fa[s][mb] = *reinterpret_cast<const u32x4*>(cur + a_off + colx[j] + mb * 32 * kStageBytes);
+      fa[s][mb] = *reinterpret_cast<const u32x4*>(cur + a_off + colx[j] + mb * 32 * RB);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      fb[s][nb] = *reinterpret_cast<const u32x4*>(cur + b_off + colx[j] + nb * 32 * kStageBytes);
+      fb[s][nb] = *reinterpret_cast<const u32x4*>(cur + b_off + colx[j] + nb * 32 * RB);
   };
-  auto mm = [&](int s) {
+  auto mm = [&](int s) __attribute__((always_inline)) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -138,6 +160,10 @@ __device__ __forceinline__ void mma_ring_stage(floatx16 (&acc)[MB][NB], const ch
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
+            // fp32: four 32x32x2 MFMAs per sub-step; lane half g supplies
+            // k = 8j + 4g + e on both operands, so every k is summed once.
+            // The element is copied out first: a bit_cast of a vector-element
+            // lvalue reads element 0 with this compiler.
             const uint32_t ae = fa[s][mb][e], be = fb[s][nb][e];
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, ae),
                                                                __builtin_bit_cast(float, be), acc[mb][nb], 0, 0, 0);
@@ -147,26 +173,22 @@ __device__ __forceinline__ void mma_ring_stage(floatx16 (&acc)[MB][NB], const ch
   };
   constexpr int kRd = MB + NB;
   constexpr int kMf = MB * NB * (kBf16 ? 1 : 4);
-  constexpr int kTotMf = 4 * kMf;
+  constexpr int kSpan = (3 * kSub * kMf) / 4 > 0 ? (3 * kSub * kMf) / 4 : 1;
   rd(0, 0);
   issue();
-  rd(1, 1);
-  mm(0);
-  rd(0, 2);
-  mm(1);
-  rd(1, 3);
-  mm(0);
-  mm(1);
-  pin_stage_order<kMf, kRd, kLoads, kSpanQ == 0 ? 1 : kSpanQ * kMf>();
+#pragma unroll
+  for (int j = 0; j < kSub; ++j) {
+    if (j + 1 < kSub) rd((j + 1) & 1, j + 1);
+    mm(j & 1);
+  }
+  pin_stage_order<kSub, kMf, kRd, kLoads, kSpan>();
 }
 
-// Shared LDS of the stage ring: three separate objects, so that the compiler
-// sees that reads of one stage never alias the loads landing in another.
-template <int TM, int TN>
+// Shared LDS of the stage ring: separate objects, so that the compiler sees
+// that reads of one stage never alias the loads landing in another.
+template <int NBUF>
 struct RingLds {
-  char* b0;
-  char* b1;
-  char* b2;
+  char* b[NBUF];
 };
 
 // WM x WN waves: wave w owns rows (w % WM) * TM / WM .. of the A tile and rows
@@ -174,49 +196,63 @@ struct RingLds {
 // MFMA blocks, MB = TM / (32 WM), NB = TN / (32 WN).
 // kDual = false: one operand pair only (p2 is ignored, the epilogue gets acc1
 // twice and no second accumulator is allocated).
-template <bool kBf16, int TM, int TN, int WM, int WN, class Epi, int NBUF = 3, bool kDual = true>
+template <bool kBf16, int TM, int TN, int WM, int WN, int NBUF, int RB, bool kDual, class Epi>
 __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, int64_t b_row0, int a_tile_begin,
-                                      int a_tile_end, const RingLds<TM, TN>& lds, Epi&& epi) {
-  static_assert(NBUF == 2 || NBUF == 3, "ring of two or three stage buffers");
+                                      int a_tile_end, const RingLds<NBUF>& lds, Epi&& epi) {
+  static_assert(NBUF >= 2 && NBUF <= 6, "ring of two to six stage buffers");
+  using F = RowFmt<RB>;
   constexpr int NW = WM * WN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
   static_assert(MB * 32 * WM == TM && NB * 32 * WN == TN, "wave tiles must be multiples of 32");
-  constexpr int kDma = (TM + TN) / (8 * NW);  // direct-to-LDS loads per wave per stage
+  constexpr int kDma = (TM + TN) / (F::kRowsPerLoad * NW);  // direct-to-LDS loads per wave per stage
+  static_assert((NBUF - 2) * kDma < 64, "vmcnt counts up to 63");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int r32 = lane & 31;
-  const int a_off = ((wave % WM) * (TM / WM) + r32) * kStageBytes;
-  const int b_off = (TM + (wave / WM) * (TN / WN) + r32) * kStageBytes;
-  int colx[4];
+  const int a_off = ((wave % WM) * (TM / WM) + r32) * RB;
+  const int b_off = (TM + (wave / WM) * (TN / WN) + r32) * RB;
+  int colx[F::kSub];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) colx[j] = ((2 * j + (lane >> 5)) ^ lds_swz(r32)) * 16;
+  for (int j = 0; j < F::kSub; ++j) colx[j] = ((2 * j + (lane >> 5)) ^ F::swz(r32)) * 16;
 
-  const int ks1 = (p1.kbytes + kStageBytes - 1) / kStageBytes;
-  const int ks2 = kDual ? (p2.kbytes + kStageBytes - 1) / kStageBytes : 0;
+  // Stages per pair. With more than three buffers each pair's count is
+  // rounded up to a multiple of NBUF (the extra stages load nothing and add
+  // zeros), so that every run starts at ring position 0 and the unrolled loop
+  // body is NBUF steps long; with two or three buffers the ring position
+  // carries over between runs instead (one unrolled copy per position).
+  constexpr bool kPad = NBUF > 3;
+  int ks1 = (p1.kbytes + RB - 1) / RB;
+  int ks2 = kDual ? (p2.kbytes + RB - 1) / RB : 0;
   if (a_tile_end <= a_tile_begin || ks1 == 0) return;
+  if constexpr (kPad) {
+    ks1 = (ks1 + NBUF - 1) / NBUF * NBUF;
+    ks2 = (ks2 + NBUF - 1) / NBUF * NBUF;
+  }
 
-  const int32_t la1 = (int32_t)((lane >> 3) * p1.lda), la2 = (int32_t)((lane >> 3) * p2.lda);
-  const int32_t lb1 = (int32_t)((lane >> 3) * p1.ldb), lb2 = (int32_t)((lane >> 3) * p2.ldb);
+  const int rig = lane / F::kChunks;
+  const int32_t la1 = (int32_t)(rig * p1.lda), la2 = (int32_t)(rig * p2.lda);
+  const int32_t lb1 = (int32_t)(rig * p1.ldb), lb2 = (int32_t)(rig * p2.ldb);
   const __amdgpu_buffer_rsrc_t rb1 = make_rsrc(p1.B + b_row0 * p1.ldb, (p1.b_rows - b_row0) * p1.ldb);
   const __amdgpu_buffer_rsrc_t rb2 = make_rsrc(p2.B + b_row0 * p2.ldb, (p2.b_rows - b_row0) * p2.ldb);
 
-  // Fetch cursor: the stage issued next (tile, pair, stage). The loads pick
-  // their operand pair with selects, not branches, so that they stay in the
-  // MFMA block and can be interleaved with it; the cursor advances after it.
+  // Fetch cursor: the stage issued next (tile ft, pair fp, stage fs). The
+  // loads pick their operand pair with selects, not branches, so that they
+  // stay in the MFMA block and can be interleaved with it; the cursor
+  // advances after it.
   int ft = a_tile_begin, fp = 0, fs = 0;
-  auto issue = [&](char* dst) {
+  auto issue = [&](char* dst) __attribute__((always_inline)) {
     const bool valid = ft < a_tile_end;
     const bool second = kDual && fp != 0;
     const int64_t a_row0 = (int64_t)(valid ? ft : a_tile_begin) * TM;
     const char* A = second ? p2.A : p1.A;
     const int64_t lda = second ? p2.lda : p1.lda, ldb = second ? p2.ldb : p1.ldb;
     const int64_t a_rows = second ? p2.a_rows : p1.a_rows;
-    dma_stage<TM, TN, NW>(dst, make_rsrc(A + a_row0 * lda, (a_rows - a_row0) * lda), second ? rb2 : rb1,
-                      second ? la2 : la1, second ? lb2 : lb1, lda, ldb, fs * kStageBytes,
-                      second ? p2.kbytes : p1.kbytes, valid, wave, lane);
+    dma_stage<TM, TN, NW, RB>(dst, make_rsrc(A + a_row0 * lda, (a_rows - a_row0) * lda), second ? rb2 : rb1,
+                              second ? la2 : la1, second ? lb2 : lb1, lda, ldb, fs * RB,
+                              second ? p2.kbytes : p1.kbytes, valid, wave, lane);
   };
-  auto advance = [&] {
+  auto advance = [&]() __attribute__((always_inline)) {
     const bool wrap = fs + 1 == (fp == 0 ? ks1 : ks2);
     const int nfp = (fp == 0 && ks2 > 0) ? 1 : 0;
     ft += (wrap && nfp == 0) ? 1 : 0;
@@ -224,74 +260,49 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
     fp = wrap ? nfp : fp;
   };
 
-  // One ring step on buffer `cur`: wait for its loads (with three buffers the
-  // next stage's loads stay in flight), barrier, refill the buffer read one
-  // step earlier with the stage NBUF-1 ahead, multiply `cur`.
-  auto step = [&](floatx16(&acc)[MB][NB], char* cur, char* refill) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NBUF == 3 ? kDma : 0));
+  // One ring step on buffer I: wait for its loads (the NBUF-2 later stages
+  // stay in flight), barrier, refill the buffer read one step earlier with
+  // the stage NBUF-1 ahead, multiply buffer I.
+  auto step = [&](floatx16(&acc)[MB][NB], auto I) __attribute__((always_inline)) {
+    constexpr int i = decltype(I)::value;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 2) * kDma));
     lds_barrier();
-    mma_ring_stage<kBf16, MB, NB, kDma, NBUF == 3 ? 3 : KD_SPAN2>(acc, cur, a_off, b_off, colx, [&] { issue(refill); });
+    mma_ring_stage<kBf16, MB, NB, kDma, RB>(acc, lds.b[i], a_off, b_off, colx,
+                                            [&]() __attribute__((always_inline)) { issue(lds.b[(i + NBUF - 1) % NBUF]); });
     advance();
   };
-  // Run `ks` stages into `acc` starting with ring position `rot`.
-  auto run = [&](floatx16(&acc)[MB][NB], int ks, int rot) {
-    int s = 0;
-    if constexpr (NBUF == 3) {
-      switch (rot) {
-        case 0:
-          for (; s + 3 <= ks; s += 3) {
-            step(acc, lds.b0, lds.b2);
-            step(acc, lds.b1, lds.b0);
-            step(acc, lds.b2, lds.b1);
-          }
-          if (s < ks) step(acc, lds.b0, lds.b2), ++s;
-          if (s < ks) step(acc, lds.b1, lds.b0), ++s;
-          break;
-        case 1:
-          for (; s + 3 <= ks; s += 3) {
-            step(acc, lds.b1, lds.b0);
-            step(acc, lds.b2, lds.b1);
-            step(acc, lds.b0, lds.b2);
-          }
-          if (s < ks) step(acc, lds.b1, lds.b0), ++s;
-          if (s < ks) step(acc, lds.b2, lds.b1), ++s;
-          break;
-        default:
-          for (; s + 3 <= ks; s += 3) {
-            step(acc, lds.b2, lds.b1);
-            step(acc, lds.b0, lds.b2);
-            step(acc, lds.b1, lds.b0);
-          }
-          if (s < ks) step(acc, lds.b2, lds.b1), ++s;
-          if (s < ks) step(acc, lds.b0, lds.b2), ++s;
-          break;
-      }
-    } else {
-      if (rot == 0) {
-        for (; s + 2 <= ks; s += 2) {
-          step(acc, lds.b0, lds.b1);
-          step(acc, lds.b1, lds.b0);
-        }
-        if (s < ks) step(acc, lds.b0, lds.b1);
-      } else {
-        for (; s + 2 <= ks; s += 2) {
-          step(acc, lds.b1, lds.b0);
-          step(acc, lds.b0, lds.b1);
-        }
-        if (s < ks) step(acc, lds.b1, lds.b0);
-      }
+  // Run `ks` stages into `acc` starting at ring position `rot`: one unrolled
+  // copy of the loop per starting position, so buffer indices stay constant.
+  auto run = [&](floatx16(&acc)[MB][NB], int ks, int rot) __attribute__((always_inline)) {
+    if constexpr (kPad) {
+      for (int s = 0; s < ks; s += NBUF)
+        static_for<0, NBUF>([&](auto I) __attribute__((always_inline)) { step(acc, I); });
+      return;
     }
+    static_for<0, NBUF>([&](auto R) __attribute__((always_inline)) {
+      constexpr int r = decltype(R)::value;
+      if (rot == r) {
+        int s = 0;
+        for (; s + NBUF <= ks; s += NBUF)
+          static_for<0, NBUF>([&](auto I) __attribute__((always_inline)) { step(acc, std::integral_constant<int, (r + I) % NBUF>{}); });
+        static_for<0, NBUF - 1>([&](auto I) __attribute__((always_inline)) {
+          if (s < ks) {
+            step(acc, std::integral_constant<int, (r + I) % NBUF>{});
+            ++s;
+          }
+        });
+      }
+    });
   };
 
   floatx16 acc1[MB][NB], acc2[kDual ? MB : 1][kDual ? NB : 1];
   zero_acc(acc1);
   if constexpr (kDual) zero_acc(acc2);
-  issue(lds.b0);  // stage 0
-  advance();
-  if (NBUF == 3) {  // stage 1
-    issue(lds.b1);
+  // prologue: the first NBUF-1 stages
+  static_for<0, NBUF - 1>([&](auto I) __attribute__((always_inline)) {
+    issue(lds.b[I]);
     advance();
-  }
+  });
   int rot = 0;
   for (int tile = a_tile_begin; tile < a_tile_end; ++tile) {
     run(acc1, ks1, rot);

@@ -74,7 +74,7 @@ __device__ __forceinline__ void merge2(float& m, float& l, float m2, float l2) {
 #define KD_RING2_LDS(TM, TN)                                                  \
   __shared__ __attribute__((aligned(16))) char ring0_[Ring<TM, TN>::kBytes]; \
   __shared__ __attribute__((aligned(16))) char ring1_[Ring<TM, TN>::kBytes]; \
-  const RingLds<TM, TN> lds{ring0_, ring1_, nullptr}
+  const RingLds<2> lds{{ring0_, ring1_}}
 
 // ---------------------------------------------------------------------------
 // Sweep: per (token tile, vocabulary split) top-k lists and LSE partials.
@@ -82,7 +82,7 @@ __device__ __forceinline__ void merge2(float& m, float& l, float m2, float l2) {
 // ---------------------------------------------------------------------------
 template <bool kSep1>
 __global__ __launch_bounds__(kThreads, 1) void topk_sweep_kernel(TopkArgs a) {
-  constexpr int TM = kTileV, TN = kTileT, MB = TM / 64, NB = TN / 64;
+  constexpr int TM = kTileV, TN = kTopkT, MB = TM / 64, NB = TN / 64;
   KD_RING2_LDS(TM, TN);
   __shared__ uint32_t S[TN][KD_TOPK_MAX];  // running top-k words, descending
   __shared__ uint32_t B[TN][kCandCap];     // candidate buffer
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_sweep_kernel(TopkArgs a) {
       if (!any) break;
     }
   };
-  sweep<true, TM, TN, 2, 2, decltype(epi)&, 2>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<true, TM, TN, 2, 2, 2, 128, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 
   // LSE partials: lanes l and l^32, then the two vocabulary-half waves
 #pragma unroll
@@ -440,7 +440,7 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   a.k = io.k;
   a.c2 = kLog2e / io.tau;
   a.inv_tau = 1.f / io.tau;
-  a.n_tok_tiles = p.n_tok_tiles;
+  a.n_tok_tiles = (int)((p.N + kTopkT - 1) / kTopkT);
   a.n_vtiles = p.n_vtiles;
   a.tiles_per_split = kTopkSplit / kTileV;
   a.n_splits = (int)((p.V + kTopkSplit - 1) / kTopkSplit);
@@ -449,7 +449,7 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   a.lists = reinterpret_cast<uint32_t*>(static_cast<char*>(io.workspace) +
                                         align_up((size_t)kTopkFields * a.n_splits * p.N * sizeof(float), 256));
   const bool sep1 = io.labels != nullptr && io.tau != 1.f;
-  const dim3 grid(p.n_tok_tiles * a.n_splits);
+  const dim3 grid(a.n_tok_tiles * a.n_splits);
   if (sep1)
     hipLaunchKernelGGL(topk_sweep_kernel<true>, grid, dim3(kThreads), 0, st, a);
   else
