@@ -61,6 +61,21 @@ __device__ __forceinline__ void zero_acc(floatx16 (&acc)[MB][NB]) {
 // Output row (within the wave's 32-row block) held by register r of this lane.
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// Block -> (token tile, vocabulary split): groups of G token tiles visit
+// every split before the next group starts, so that the blocks of one XCD (a
+// contiguous logical range after xcd_remap) share both W and h rows.
+template <int G>
+__device__ __forceinline__ void block_coords(int L, int n_tok_tiles, int n_splits, int& tt, int& sp) {
+  constexpr int kTokGroup = G;
+  const int per_group = kTokGroup * n_splits;
+  const int group = L / per_group;
+  const int within = L - group * per_group;
+  const int rest = n_tok_tiles - group * kTokGroup;
+  const int g_eff = rest < kTokGroup ? rest : kTokGroup;
+  tt = group * kTokGroup + within % g_eff;
+  sp = within / g_eff;
+}
+
 // XCD-aware block order: hardware block b runs on XCD b % 8; give each XCD a
 // contiguous run of logical tiles so that blocks sharing operand rows meet in
 // that XCD's L2. Identity when the grid is not a multiple of 8.

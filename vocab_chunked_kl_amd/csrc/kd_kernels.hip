@@ -69,19 +69,6 @@ struct LogitArgs {
   int64_t g_col0;    // vocabulary index of G's column 0
 };
 
-// Block -> (token tile, vocabulary split): groups of kTokGroup token tiles
-// visit every split before the next group starts, so that the blocks of one
-// XCD (a contiguous logical range after xcd_remap) share both W and h rows.
-__device__ __forceinline__ void block_coords(int L, int n_tok_tiles, int n_splits, int& tt, int& sp) {
-  const int per_group = kTokGroup * n_splits;
-  const int group = L / per_group;
-  const int within = L - group * per_group;
-  const int rest = n_tok_tiles - group * kTokGroup;
-  const int g_eff = rest < kTokGroup ? rest : kTokGroup;
-  tt = group * kTokGroup + within % g_eff;
-  sp = within / g_eff;
-}
-
 __device__ __forceinline__ void merge_online(float& m, float& l, float m2, float l2) {
   const float mm = fmaxf(m, m2);
   const float f1 = (m == kNegInf) ? 0.f : fast_exp2(m - mm);
@@ -119,7 +106,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
   KD_RING_LDS_N(TM, TN, kLogitRB, kLogitBuf);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
-  block_coords(L, a.n_tok_tiles, a.n_splits, tt, sp);
+  block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_splits, tt, sp);
   const int vt0 = sp * a.tiles_per_split;
   const int vt1 = min(vt0 + a.tiles_per_split, a.n_vtiles);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave % WM, wn = wave / WM;
@@ -325,7 +312,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
   KD_RING_LDS_N(TM, TN, kLogitRB, kLogitBuf);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
-  block_coords(L, a.n_tok_tiles, a.n_splits, tt, sp);
+  block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_splits, tt, sp);
   const int vt0 = a.vt_offset + sp * a.tiles_per_split;
   const int vt1 = min(vt0 + a.tiles_per_split, a.vt_offset + a.n_vtiles);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave % WM, wn = wave / WM;
@@ -439,7 +426,7 @@ __global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
   KD_RING_LDS_N(TM, TN, kDhRB, kDhBuf);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, dt;
-  block_coords(L, a.n_tok_tiles, a.n_d_tiles, tt, dt);
+  block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_d_tiles, tt, dt);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave % WM, wn = wave / WM;
   // Read-modify-write of dh, one 32-row slice at a time: all loads of the
   // slice are issued before its stores, so they overlap instead of forming a

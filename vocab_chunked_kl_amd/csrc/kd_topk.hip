@@ -76,31 +76,35 @@ __device__ __forceinline__ void merge2(float& m, float& l, float m2, float l2) {
   __shared__ __attribute__((aligned(16))) char ring1_[Ring<TM, TN>::kBytes]; \
   const RingLds<2> lds{{ring0_, ring1_}}
 
+// Wave grid of the top-k sweep: 4 vocabulary slices x 2 token halves.
+constexpr int kTopkWM = 4, kTopkWN = 2, kTopkThreads = 64 * kTopkWM * kTopkWN;
+
 // ---------------------------------------------------------------------------
 // Sweep: per (token tile, vocabulary split) top-k lists and LSE partials.
 // kSep1: also accumulate the untempered student LSE (tau != 1, for the CE).
 // ---------------------------------------------------------------------------
 template <bool kSep1>
-__global__ __launch_bounds__(kThreads, 1) void topk_sweep_kernel(TopkArgs a) {
-  constexpr int TM = kTileV, TN = kTopkT, MB = TM / 64, NB = TN / 64;
+__global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a) {
+  constexpr int TM = kTileV, TN = kTopkT, WM = kTopkWM, WN = kTopkWN, NW = WM * WN;
+  constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
   KD_RING2_LDS(TM, TN);
   __shared__ uint32_t S[TN][KD_TOPK_MAX];  // running top-k words, descending
   __shared__ uint32_t B[TN][kCandCap];     // candidate buffer
   __shared__ int cntS[TN], cntB[TN];
   __shared__ uint32_t theta[TN];           // k-th word once full, else 0
-  __shared__ float red[kTopkFields * TN];
+  __shared__ float red[(WM - 1) * kTopkFields * TN];
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int tt = L % a.n_tok_tiles;
-  const int sp = L / a.n_tok_tiles;
+  int tt, sp;
+  block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_splits, tt, sp);
   const int vt0 = sp * a.tiles_per_split;
   const int vt1 = min(vt0 + a.tiles_per_split, a.n_vtiles);
   const int64_t vbase = (int64_t)sp * kTopkSplit;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave & 1, wn = wave >> 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave % WM, wn = wave / WM;
   const int K = a.k;
   const float c2 = a.c2;
 
-  for (int t = tid; t < TN; t += kThreads) {
+  for (int t = tid; t < TN; t += kTopkThreads) {
     cntS[t] = 0;
     cntB[t] = 0;
     theta[t] = 0u;
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_sweep_kernel(TopkArgs a) {
   };
 
   auto epi = [&](int vt, auto& zs, auto& zt) {
-    const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / 2);
+    const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
     const bool full = (int64_t)(vt + 1) * TM <= a.V;
     // 1) round both logit tiles to bf16; 2) online LSEs of the tempered values
 #pragma unroll
@@ -187,13 +191,18 @@ __global__ __launch_bounds__(kThreads, 1) void topk_sweep_kernel(TopkArgs a) {
       }
     }
     // 3) top-k candidates: rounds until no token's buffer overflowed
-    uint32_t done[NB][2] = {{0u, 0u}, {0u, 0u}};
+    constexpr int kDoneWords = (MB * 16 + 31) / 32;
+    uint32_t done[NB][kDoneWords];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < kDoneWords; ++i) done[nb][i] = 0u;
     const int rel0 = (int)(vrow0 - vbase);
     while (true) {
       int ov = 0;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int col = wn * (TN / 2) + nb * 32 + (lane & 31);
+        const int col = wn * (TN / WN) + nb * 32 + (lane & 31);
         const uint32_t th = theta[col];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
@@ -215,41 +224,46 @@ __global__ __launch_bounds__(kThreads, 1) void topk_sweep_kernel(TopkArgs a) {
           }
       }
       const int any = __syncthreads_or(ov);
-      for (int t = wave; t < TN; t += 4)
+      for (int t = wave; t < TN; t += NW)
         if (cntB[t] > 0) merge_token(t);
       __syncthreads();
       if (!any) break;
     }
   };
-  sweep<true, TM, TN, 2, 2, 2, 128, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<true, TM, TN, WM, WN, 2, 128, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 
-  // LSE partials: lanes l and l^32, then the two vocabulary-half waves
+  // LSE partials: lanes l and l^32, then the WM vocabulary-slice waves
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     merge2(ms[nb], ls[nb], __shfl_xor(ms[nb], 32), __shfl_xor(ls[nb], 32));
     merge2(mt[nb], lt[nb], __shfl_xor(mt[nb], 32), __shfl_xor(lt[nb], 32));
     merge2(m1[nb], l1[nb], __shfl_xor(m1[nb], 32), __shfl_xor(l1[nb], 32));
   }
-  if (wm == 1 && lane < 32) {
+  if (wm > 0 && lane < 32) {
+    float* r = red + (wm - 1) * kTopkFields * TN;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = wn * (TN / 2) + nb * 32 + lane;
-      red[0 * TN + col] = ms[nb];
-      red[1 * TN + col] = ls[nb];
-      red[2 * TN + col] = mt[nb];
-      red[3 * TN + col] = lt[nb];
-      red[4 * TN + col] = m1[nb];
-      red[5 * TN + col] = l1[nb];
+      const int col = wn * (TN / WN) + nb * 32 + lane;
+      r[0 * TN + col] = ms[nb];
+      r[1 * TN + col] = ls[nb];
+      r[2 * TN + col] = mt[nb];
+      r[3 * TN + col] = lt[nb];
+      r[4 * TN + col] = m1[nb];
+      r[5 * TN + col] = l1[nb];
     }
   }
   __syncthreads();
   if (wm == 0 && lane < 32) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = wn * (TN / 2) + nb * 32 + lane;
-      merge2(ms[nb], ls[nb], red[0 * TN + col], red[1 * TN + col]);
-      merge2(mt[nb], lt[nb], red[2 * TN + col], red[3 * TN + col]);
-      merge2(m1[nb], l1[nb], red[4 * TN + col], red[5 * TN + col]);
+      const int col = wn * (TN / WN) + nb * 32 + lane;
+#pragma unroll
+      for (int w = 0; w < WM - 1; ++w) {
+        const float* r = red + w * kTopkFields * TN;
+        merge2(ms[nb], ls[nb], r[0 * TN + col], r[1 * TN + col]);
+        merge2(mt[nb], lt[nb], r[2 * TN + col], r[3 * TN + col]);
+        merge2(m1[nb], l1[nb], r[4 * TN + col], r[5 * TN + col]);
+      }
       const int64_t n = (int64_t)tt * TN + col;
       if (n < a.N) {
         const int64_t S_ = a.n_splits;
@@ -263,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 1) void topk_sweep_kernel(TopkArgs a) {
     }
   }
   // the top-k list of each token (padded with 0 words when the split is short)
-  for (int i = tid; i < TN * K; i += kThreads) {
+  for (int i = tid; i < TN * K; i += kTopkThreads) {
     const int t = i / K, j = i - t * K;
     const int64_t n = (int64_t)tt * TN + t;
     if (n < a.N) a.lists[((int64_t)sp * a.N + n) * K + j] = j < cntS[t] ? S[t][j] : 0u;
@@ -360,6 +374,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
     const uint32_t vidx = (uint32_t)s * kTopkSplit + (0xFFFFu - (w & 0xFFFFu));
     cw[i] = w == 0u ? 0ull : ((unsigned long long)(w >> 16) << 32) | (0xFFFFFFFFull - vidx);
   }
+  if (lane < K) sel[wave][lane] = 0ull;  // slots left empty stay 0 (never read as an index)
   __builtin_amdgcn_wave_barrier();
   // rank every candidate against all others (all words are distinct); rank < K is its slot
   for (int i = lane; i < C; i += 64) {
@@ -372,14 +387,17 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
 
   const bool act = lane < K;
   const unsigned long long xj = act ? sel[wave][lane] : 0ull;
-  const int32_t vj = (int32_t)(0xFFFFFFFFu - (uint32_t)(xj & 0xFFFFFFFFull));
+  // an empty slot (only possible with fewer than k finite candidates) or a
+  // decoded index outside the vocabulary is never dereferenced
+  const uint32_t vdec = 0xFFFFFFFFu - (uint32_t)(xj & 0xFFFFFFFFull);
+  const int32_t vj = (xj != 0ull && (int64_t)vdec < a.V) ? (int32_t)vdec : -1;
   const float tj = act ? key_to_f32((uint32_t)(xj >> 32)) : 0.f;
   // student bf16 logits at the selected indices: one wave-wide dot product each
   const uint16_t* h = a.h_s + n * a.d_s;
   float sj = 0.f;
   for (int j = 0; j < K; ++j) {
-    const int32_t v = __shfl(vj, j);
-    const float zsv = student_logit(h, a.W_s, v, a.d_s, lane);
+    const int32_t v = __shfl(vj, j);  // wave-uniform
+    const float zsv = v >= 0 ? student_logit(h, a.W_s, v, a.d_s, lane) : kNegInf;
     if (lane == j) sj = zsv;
   }
   if (act) {
@@ -451,9 +469,9 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   const bool sep1 = io.labels != nullptr && io.tau != 1.f;
   const dim3 grid(a.n_tok_tiles * a.n_splits);
   if (sep1)
-    hipLaunchKernelGGL(topk_sweep_kernel<true>, grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(topk_sweep_kernel<true>, grid, dim3(kTopkThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(topk_sweep_kernel<false>, grid, dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL(topk_sweep_kernel<false>, grid, dim3(kTopkThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MergeArgs m{};
