@@ -10,55 +10,30 @@
 
 namespace kd {
 
-// Logit tile: 256 vocabulary rows x kTileT tokens per workgroup, split over
-// kLogitWM x kLogitWN waves (vocabulary x tokens), with a ring of kLogitBuf
-// LDS stages.
+// Logit tile: 256 vocabulary rows x 128 tokens per workgroup on a 4 x 2 wave
+// grid (64 x 64 per wave: two waves per SIMD), with a ring of three LDS
+// stages of 128 bytes of K per row (48 KiB each).
 constexpr int kTileV = 256;
-#ifndef KD_TILE_T
-#define KD_TILE_T 128
-#endif
-constexpr int kTileT = KD_TILE_T;
-#ifndef KD_LOGIT_RB
-#define KD_LOGIT_RB 128
-#endif
-#ifndef KD_LOGIT_BUF
-#define KD_LOGIT_BUF 3
-#endif
-constexpr int kLogitRB = KD_LOGIT_RB;   // bytes of K per LDS stage row
-constexpr int kLogitBuf = KD_LOGIT_BUF;
-// Token tile of the top-k sweep (its per-token selection state lives in LDS).
-constexpr int kTopkT = 128;
-#ifndef KD_LOGIT_WM
-#define KD_LOGIT_WM 4
-#endif
-constexpr int kLogitWM = KD_LOGIT_WM;
+constexpr int kTileT = 128;
+constexpr int kLogitWM = 4;
 constexpr int kLogitWN = 2;
 constexpr int kLogitThreads = 64 * kLogitWM * kLogitWN;
-// dh tile: 256 tokens x kTileDhD hidden units over kDhWM x kDhWN waves, with
-// a ring of kDhBuf LDS stages.
+constexpr int kLogitRB = 128;
+constexpr int kLogitBuf = 3;
+// Token tile of the top-k sweep (its per-token selection state lives in LDS).
+constexpr int kTopkT = 128;
+// dh tile: 256 tokens x 256 hidden units, 4 x 2 waves (64 x 128 per wave, one
+// accumulator), ring of two 64 KiB stages.
 constexpr int kTileDhT = 256;
-#ifndef KD_DH_TILE_D
-#define KD_DH_TILE_D 256
-#endif
-constexpr int kTileDhD = KD_DH_TILE_D;
-#ifndef KD_DH_WM
-#define KD_DH_WM 4
-#endif
-#ifndef KD_DH_WN
-#define KD_DH_WN 2
-#endif
-constexpr int kDhWM = KD_DH_WM;
-constexpr int kDhWN = KD_DH_WN;
+constexpr int kTileDhD = 256;
+constexpr int kDhWM = 4;
+constexpr int kDhWN = 2;
 constexpr int kDhThreads = 64 * kDhWM * kDhWN;
-#ifndef KD_DH_RB
-#define KD_DH_RB 128
-#endif
-constexpr int kDhRB = KD_DH_RB;
-#ifndef KD_DH_BUF
-#define KD_DH_BUF (kTileDhD > 128 ? 2 : 3)
-#endif
-constexpr int kDhBuf = KD_DH_BUF;
-// Number of token tiles grouped together in the block order (L2 reuse).
+constexpr int kDhRB = 128;
+constexpr int kDhBuf = 2;
+// Token tiles grouped together in the block order: the 32 blocks that run at
+// once on one XCD are 8 token tiles x 4 vocabulary splits, the split that
+// minimises the operand bytes its L2 fetches (measured best of 4, 8, 16).
 #ifndef KD_TOK_GROUP
 #define KD_TOK_GROUP 8
 #endif

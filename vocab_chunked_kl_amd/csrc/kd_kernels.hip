@@ -35,19 +35,16 @@ namespace {
 
 constexpr float kNegInf = -INFINITY;
 
-// The NBUF (<= 6) LDS stage buffers of a sweep ring, as separate objects.
+// The NBUF (2 or 3) LDS stage buffers of a sweep ring, as separate objects.
 #define KD_RING_LDS_N(TM, TN, RB, NBUF)                                                             \
   __shared__ __attribute__((aligned(16))) char ring0_[Ring<TM, TN, RB>::kBytes];                    \
   __shared__ __attribute__((aligned(16))) char ring1_[Ring<TM, TN, RB>::kBytes];                    \
   __shared__ __attribute__((aligned(16))) char ring2_[(NBUF) > 2 ? Ring<TM, TN, RB>::kBytes : 16]; \
-  __shared__ __attribute__((aligned(16))) char ring3_[(NBUF) > 3 ? Ring<TM, TN, RB>::kBytes : 16]; \
-  __shared__ __attribute__((aligned(16))) char ring4_[(NBUF) > 4 ? Ring<TM, TN, RB>::kBytes : 16]; \
-  __shared__ __attribute__((aligned(16))) char ring5_[(NBUF) > 5 ? Ring<TM, TN, RB>::kBytes : 16]; \
-  const RingLds<NBUF> lds = ring_of<NBUF>(ring0_, ring1_, ring2_, ring3_, ring4_, ring5_)
+  const RingLds<NBUF> lds = ring_of<NBUF>(ring0_, ring1_, ring2_)
 
 template <int NBUF>
-__device__ __forceinline__ RingLds<NBUF> ring_of(char* r0, char* r1, char* r2, char* r3, char* r4, char* r5) {
-  char* all[6] = {r0, r1, r2, r3, r4, r5};
+__device__ __forceinline__ RingLds<NBUF> ring_of(char* r0, char* r1, char* r2) {
+  char* all[3] = {r0, r1, r2};
   RingLds<NBUF> r;
 #pragma unroll
   for (int i = 0; i < NBUF; ++i) r.b[i] = all[i];

@@ -11,8 +11,8 @@
 // both for the same (vocabulary, token) tile, as the block logit rebuild of
 // the Nitrobrew notes ("Nitrobrew 的两个动作") needs them side by side.
 //
-// Pipeline: a ring of NBUF LDS stage buffers (RB bytes of K per row each)
-// filled by direct-to-LDS buffer loads (no staging registers, no LDS store
+// Pipeline: a ring of NBUF (2 or 3) LDS stage buffers (RB = 128 bytes of K
+// per row each) filled by direct-to-LDS buffer loads (no staging registers, no LDS store
 // instructions). While stage g is multiplied, the loads of stages g+1 ..
 // g+NBUF-2 are in flight and stage g+NBUF-1 is being issued; one barrier per
 // stage recycles the buffer read in the previous step. The stage sequence
@@ -56,19 +56,20 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100;
 
 // LDS stage layout: [A tile: TM rows][B tile: TN rows], RB bytes per row,
-// unpadded, with the 16-byte chunks of row R stored at slot (chunk ^ swz(R)).
-// A direct-to-LDS load writes 64 lanes x 16 bytes contiguously (1024 / RB
-// rows); the XOR makes the MFMA fragment reads (16 consecutive rows at one
-// chunk per 16 lanes) hit 16 distinct 16-byte bank groups:
-//   RB = 128: swz(R) = (R & 7) ^ ((R >> 3) & 3)   (8 chunks, rows alternate halves)
-//   RB =  64: swz(R) = (R >> 2) & 3               (4 chunks, 4 rows per 256 bytes)
+// unpadded, with the 16-byte chunks of row R stored at slot (chunk ^ swz(R)),
+// swz(R) = (R & 7) ^ ((R >> 3) & 3). A direct-to-LDS load writes 64 lanes x 16
+// bytes contiguously (8 rows); the XOR makes the MFMA fragment reads (16
+// consecutive rows at one chunk per 16 lanes) hit 16 distinct 16-byte bank
+// groups (consecutive rows sit in alternate halves of the 256-byte bank row).
+// (64-byte rows with deeper rings were measured slower: twice the barriers
+// and per-stage scalar work for the same bytes in flight.)
 template <int RB>
 struct RowFmt {
-  static_assert(RB == 64 || RB == 128, "64- or 128-byte stage rows");
+  static_assert(RB == 128, "128-byte stage rows");
   static constexpr int kChunks = RB / 16;         // 16-byte chunks per row
   static constexpr int kRowsPerLoad = 1024 / RB;  // rows per 64-lane direct-to-LDS load
   static constexpr int kSub = RB / 32;            // MFMA k-substeps (32 bytes of K) per stage
-  __device__ static __forceinline__ int swz(int r) { return RB == 128 ? (r & 7) ^ ((r >> 3) & 3) : (r >> 2) & 3; }
+  __device__ static __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 3); }
 };
 
 template <int TM, int TN, int RB = 128>
@@ -199,7 +200,7 @@ struct RingLds {
 template <bool kBf16, int TM, int TN, int WM, int WN, int NBUF, int RB, bool kDual, class Epi>
 __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, int64_t b_row0, int a_tile_begin,
                                       int a_tile_end, const RingLds<NBUF>& lds, Epi&& epi) {
-  static_assert(NBUF >= 2 && NBUF <= 6, "ring of two to six stage buffers");
+  static_assert(NBUF == 2 || NBUF == 3, "ring of two or three stage buffers");
   using F = RowFmt<RB>;
   constexpr int NW = WM * WN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
@@ -216,19 +217,10 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
 #pragma unroll
   for (int j = 0; j < F::kSub; ++j) colx[j] = ((2 * j + (lane >> 5)) ^ F::swz(r32)) * 16;
 
-  // Stages per pair. With more than three buffers each pair's count is
-  // rounded up to a multiple of NBUF (the extra stages load nothing and add
-  // zeros), so that every run starts at ring position 0 and the unrolled loop
-  // body is NBUF steps long; with two or three buffers the ring position
-  // carries over between runs instead (one unrolled copy per position).
-  constexpr bool kPad = NBUF > 3;
-  int ks1 = (p1.kbytes + RB - 1) / RB;
-  int ks2 = kDual ? (p2.kbytes + RB - 1) / RB : 0;
+  // stages per pair; the ring position carries over from run to run
+  const int ks1 = (p1.kbytes + RB - 1) / RB;
+  const int ks2 = kDual ? (p2.kbytes + RB - 1) / RB : 0;
   if (a_tile_end <= a_tile_begin || ks1 == 0) return;
-  if constexpr (kPad) {
-    ks1 = (ks1 + NBUF - 1) / NBUF * NBUF;
-    ks2 = (ks2 + NBUF - 1) / NBUF * NBUF;
-  }
 
   const int rig = lane / F::kChunks;
   const int32_t la1 = (int32_t)(rig * p1.lda), la2 = (int32_t)(rig * p2.lda);
@@ -274,11 +266,6 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
   // Run `ks` stages into `acc` starting at ring position `rot`: one unrolled
   // copy of the loop per starting position, so buffer indices stay constant.
   auto run = [&](floatx16(&acc)[MB][NB], int ks, int rot) __attribute__((always_inline)) {
-    if constexpr (kPad) {
-      for (int s = 0; s < ks; s += NBUF)
-        static_for<0, NBUF>([&](auto I) __attribute__((always_inline)) { step(acc, I); });
-      return;
-    }
     static_for<0, NBUF>([&](auto R) __attribute__((always_inline)) {
       constexpr int r = decltype(R)::value;
       if (rot == r) {
