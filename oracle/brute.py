@@ -69,6 +69,23 @@ def fd_grad_h(h_s, W_s, h_t, W_t, beta, tau, eps=1e-5):
     return grads
 
 
+def fd_grad_W(h_s, W_s, h_t, W_t, beta, tau, eps=1e-5):
+    """Central finite differences of the summed loss w.r.t. each entry of W_s."""
+    grads = []
+    for v in range(len(W_s)):
+        g = []
+        for i in range(len(W_s[v])):
+            Wp = [list(r) for r in W_s]
+            Wm = [list(r) for r in W_s]
+            Wp[v][i] += eps
+            Wm[v][i] -= eps
+            lp = math.fsum(loss_rows(h_s, Wp, h_t, W_t, beta, tau))
+            lm = math.fsum(loss_rows(h_s, Wm, h_t, W_t, beta, tau))
+            g.append((lp - lm) / (2 * eps))
+        grads.append(g)
+    return grads
+
+
 def topk_row(keys, k):
     """k indices of the largest keys, ties broken by the lower index."""
     return [i for _, i in sorted(((-v, i) for i, v in enumerate(keys)))[:k]]

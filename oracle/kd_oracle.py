@@ -16,7 +16,9 @@ sums). Sources, cited by page title and section:
   gradient "p - q", reverse-KL gradient "p (log p - log q - KL)", with p the
   student there), the ``forward_kl`` / ``reverse_kl`` listing under "VeRL PR"
   (student/teacher hidden states, both unembeddings, temperature; gradients
-  reach the student only).
+  reach the student only), and "工程落地：简单 idea，不等于简单集成" (the student
+  hidden state and the student unembedding receive gradients, the teacher's
+  parameters are frozen).
 * [White-box OPD]  ars-opd-rebuild "03 · 层 2：White-box OPD 基线": section 2.3
   (the beta table: beta=0 KL(teacher||student), beta=1 KL(student||teacher),
   0<beta<1 beta*KL(teacher||m) + (1-beta)*KL(student||m) with
@@ -39,7 +41,7 @@ import numpy as np
 
 __all__ = [
     "as_f64", "bf16_round", "bf16_neighbours", "logits", "lse", "log_softmax", "divergence",
-    "kd_fwd", "grad_student_logits", "kd_bwd", "topk_order", "topk_three_terms", "kd_topk_fwd",
+    "kd_fwd", "grad_student_logits", "kd_bwd", "kd_bwd_w", "topk_order", "topk_three_terms", "kd_topk_fwd",
     "fp32_dot_error_bound", "svd_teacher", "log1mexp",
 ]
 
@@ -241,6 +243,21 @@ def kd_bwd(h_s, W_s, h_t, W_t, beta: float, tau: float, grad_loss=None) -> np.nd
     for v0 in range(0, W_s.shape[0], _SLAB):
         out += g[:, v0:v0 + _SLAB] @ as_f64(W_s[v0:v0 + _SLAB])
     return out
+
+
+def kd_bwd_w(h_s, W_s, h_t, W_t, beta: float, tau: float, grad_loss=None) -> np.ndarray:
+    """dL/dW_s[v, :] = sum_n grad_loss[n] * (g[n, v] / tau) * h_s[n, :].
+
+    The student unembedding receives a gradient as well as the student hidden
+    state; the teacher's parameters stay fixed ([Nitrobrew notes],
+    "工程落地：简单 idea，不等于简单集成"). Same g and 1/tau as ``kd_bwd``: the
+    two gradients are the two factors' sides of z_s = h_s W_s^T."""
+    s = logits(h_s, W_s) / tau
+    t = logits(h_t, W_t) / tau
+    g = grad_student_logits(s, t, beta) / tau
+    if grad_loss is not None:
+        g = g * np.asarray(grad_loss, dtype=np.float64)[:, None]
+    return g.T @ as_f64(h_s)
 
 
 # ---------------------------------------------------------------------------

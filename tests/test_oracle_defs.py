@@ -223,6 +223,39 @@ def test_gradient_matches_finite_differences(beta, tau):
 
 
 @pytest.mark.parametrize("beta", BETAS)
+@pytest.mark.parametrize("tau", (1.0, 2.0))
+def test_weight_gradient_matches_finite_differences(beta, tau):
+    g = rng(18)
+    N, V, ds, dt = 3, 7, 5, 4
+    h_s, h_t = g.normal(size=(N, ds)), g.normal(size=(N, dt))
+    W_s, W_t = g.normal(0, 0.7, size=(V, ds)), g.normal(0, 0.7, size=(V, dt))
+    fd = np.array(brute.fd_grad_W(h_s.tolist(), W_s.tolist(), h_t.tolist(), W_t.tolist(), beta, tau))
+    an = O.kd_bwd_w(h_s, W_s, h_t, W_t, beta, tau)
+    assert an.shape == (V, ds)
+    assert np.allclose(an, fd, atol=2e-9, rtol=1e-7), np.abs(an - fd).max()
+    # grad_loss weights the tokens' contributions
+    gl = np.array([0.5, -2.0, 1.5])
+    an2 = O.kd_bwd_w(h_s, W_s, h_t, W_t, beta, tau, grad_loss=gl)
+    parts = [O.kd_bwd_w(h_s[i:i + 1], W_s, h_t[i:i + 1], W_t, beta, tau) for i in range(N)]
+    assert np.allclose(an2, sum(w * p for w, p in zip(gl, parts)), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("beta", BETAS)
+def test_weight_and_hidden_gradients_agree(beta):
+    # both are the two sides of z_s = h_s W_s^T: sum_v W_s[v].dW_s[v] equals
+    # sum_n h_s[n].dh_s[n] (each is sum_{n,v} dL/dz_s[n,v] z_s[n,v]), and the
+    # rows of dW_s sum to zero because each token's dL/ds sums to zero
+    g = rng(19)
+    N, V, ds, dt = 5, 40, 6, 9
+    h_s, h_t = g.normal(size=(N, ds)), g.normal(size=(N, dt))
+    W_s, W_t = g.normal(0, 0.8, size=(V, ds)), g.normal(0, 0.8, size=(V, dt))
+    dW = O.kd_bwd_w(h_s, W_s, h_t, W_t, beta, 1.5)
+    dh = O.kd_bwd(h_s, W_s, h_t, W_t, beta, 1.5)
+    assert abs(np.sum(W_s * dW) - np.sum(h_s * dh)) < 1e-12 * (1 + np.abs(W_s * dW).sum())
+    assert np.all(np.abs(dW.sum(0)) < 1e-13)
+
+
+@pytest.mark.parametrize("beta", BETAS)
 def test_gradient_sums_to_zero(beta):
     g = rng(9)
     s, t = g.normal(0, 3, (6, 500)), g.normal(0, 3, (6, 500))
