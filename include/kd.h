@@ -19,7 +19,8 @@
  *   - Layout: row-major and contiguous. h_s [N, d_s], h_t [N, d_t] hold one
  *     token per row ([B, T, D] flattened); W_s [V, d_s], W_t [V, d_t] hold one
  *     vocabulary entry per row (the nn.Linear weight layout). Inputs must be
- *     16-byte aligned and d_s, d_t multiples of 8 (else KD_ERR_UNSUPPORTED).
+ *     16-byte aligned and d_s, d_t multiples of 8 with 256 * d * element size
+ *     below 2^31 (else KD_ERR_UNSUPPORTED).
  *     V is arbitrary (vocabulary tails are masked, never read as logit 0).
  *   - dtype: KD_BF16 (uint16 bf16 bit patterns) or KD_F32, for all four of
  *     h_s, W_s, h_t, W_t alike.
@@ -56,7 +57,7 @@ typedef enum {
 
 typedef enum { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
 
-typedef enum { KD_OP_FWD = 0, KD_OP_BWD = 1, KD_OP_TOPK = 2 } kd_op;
+typedef enum { KD_OP_FWD = 0, KD_OP_BWD = 1, KD_OP_TOPK = 2, KD_OP_BWD_W = 3 } kd_op;
 
 /* Largest k accepted by kd_topk_fwd. */
 #define KD_TOPK_MAX 64
@@ -65,13 +66,16 @@ typedef enum { KD_OP_FWD = 0, KD_OP_BWD = 1, KD_OP_TOPK = 2 } kd_op;
 
 /*
  * kd_workspace_size - device workspace (bytes) that `op` needs for this shape.
- *   op: KD_OP_FWD (kd_fwd), KD_OP_BWD (kd_bwd) or KD_OP_TOPK (kd_topk_fwd).
- *   beta is read for KD_OP_FWD/KD_OP_BWD, chunk_V for KD_OP_BWD, k for
+ *   op: KD_OP_FWD (kd_fwd), KD_OP_BWD (kd_bwd without dW_s), KD_OP_BWD_W
+ *   (kd_bwd with dW_s) or KD_OP_TOPK (kd_topk_fwd).
+ *   beta is read for KD_OP_FWD, chunk_V for the backward ops, k for
  *   KD_OP_TOPK; d_s/d_t/dtype size the backward's per-chunk buffers.
  *   The backward's workspace is O(N * chunk_V) (the gradient tile G of one
- *   vocabulary chunk, bf16) plus O(chunk_V * d_s) for one transposed chunk of
- *   W_s; the forward's is O(N * V / vocab_split) floats of partial statistics.
- *   Writes the size to *bytes (host pointer). Pure host function.
+ *   vocabulary chunk, in the input dtype) plus O(chunk_V * d_s) for one
+ *   transposed chunk of W_s; KD_OP_BWD_W adds a transposed copy of G and of
+ *   h_s (O(N * chunk_V + N * d_s)). The forward's is O(N * V / 2048) floats
+ *   of partial statistics. Writes the size to *bytes (host pointer). Pure
+ *   host function.
  */
 kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t d_t, kd_dtype dtype,
                             float beta, int32_t chunk_V, int32_t k, size_t* bytes);
@@ -100,26 +104,35 @@ kd_status kd_fwd(const void* h_s, const void* W_s, const void* h_t, const void* 
                  float* lse_t, float* aux, void* workspace, size_t ws_bytes, void* stream);
 
 /*
- * kd_bwd - gradient of sum_n grad_loss[n] * loss[n] with respect to h_s.
+ * kd_bwd - gradient of sum_n grad_loss[n] * loss[n] with respect to h_s and,
+ *   optionally, W_s.
  *   Source: Nitrobrew notes, "仓库实现": the gradient is recomputed block by
- *   block instead of storing logits; only the student receives a gradient.
+ *   block instead of storing logits; "工程落地：简单 idea，不等于简单集成": the
+ *   student hidden state and the student unembedding receive gradients, the
+ *   teacher's parameters stay fixed.
  *   With g = dloss/ds (s the tempered student logits):
  *     beta = 0:  g = q - p
  *     beta = 1:  g = q (log q - log p - KL(q || p))
  *     else:      g = (1 - beta) q (log q - log m - KL(q || m))
- *   dh_s[n, :] = grad_loss[n] * sum_v (g[n, v] / tau) W_s[v, :].
+ *   dh_s[n, :] = grad_loss[n] * sum_v (g[n, v] / tau) W_s[v, :]
+ *   dW_s[v, :] = sum_n grad_loss[n] * (g[n, v] / tau) h_s[n, :]
  *
  *   lse_s, lse_t, aux (device, [N] fp32, read): as written by kd_fwd with the
  *         same inputs, beta and tau (aux unused when beta == 0, may be NULL).
  *   grad_loss (device, [N] fp32, read; NULL means all ones).
  *   chunk_V: vocabulary entries per recompute chunk (a positive multiple of
- *         256); the workspace holds one [N, chunk_V] bf16 gradient chunk.
- *   dh_s  (device, [N, d_s] fp32, overwritten).
+ *         256); the workspace holds one [N, chunk_V] gradient chunk.
+ *   dh_s  (device, [N, d_s] fp32, overwritten; may be NULL if dW_s is not).
+ *   dW_s  (device, [V, d_s] fp32, overwritten; may be NULL). When given, the
+ *         workspace must hold kd_workspace_size(KD_OP_BWD_W, ...) bytes and
+ *         256 * N (rounded up to 128) * element size must stay below 2^31
+ *         (about 4.19M bf16 / 2.09M fp32 tokens; else KD_ERR_UNSUPPORTED).
+ *   chunk_V * element size * 256 < 2^31 as well (else KD_ERR_UNSUPPORTED).
  */
 kd_status kd_bwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
                  int32_t d_s, int32_t d_t, float beta, float tau, kd_dtype dtype, int32_t chunk_V,
                  const float* lse_s, const float* lse_t, const float* aux, const float* grad_loss, float* dh_s,
-                 void* workspace, size_t ws_bytes, void* stream);
+                 float* dW_s, void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * kd_topk_fwd - top-k three-term decomposition over bf16 logits.

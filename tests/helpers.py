@@ -64,6 +64,25 @@ def grad_floor(lse_s, lse_t, loss, W_s, tau):
     return 8 * U32 * (2 * np.abs(lse_s) + 2 * np.abs(lse_t) + np.abs(loss)) * wmax / tau
 
 
+def wgrad_floor(h_s, W_s, h_t, W_t, beta, tau, grad=None):
+    """Per-row floor of dL/dW_s in fp32 (small cases only: uses full logits).
+    Row v gathers sum_n dL/ds[n, v] h_s[n] / tau; the fp32 error of each
+    dL/ds[n, v] is bounded like the dh_s floor's (eight roundings of the
+    O(|L_s| + |L_t| + |KL|) terms), weighted by that entry's student
+    probability, so row v's floor is the sum over tokens of that bound times
+    max(q[n, v], the teacher's p[n, v]) times |h_s[n]| |grad[n]|."""
+    from oracle import kd_oracle as O
+    s = O.logits(h_s, W_s) / tau
+    t = O.logits(h_t, W_t) / tau
+    q = np.exp(O.log_softmax(s))
+    p = np.exp(O.log_softmax(t))
+    ref = O.kd_fwd(h_s, W_s, h_t, W_t, beta, tau)
+    per_tok = 8 * U32 * (2 * np.abs(ref["lse_s"]) + 2 * np.abs(ref["lse_t"]) + np.abs(ref["loss"])) / tau
+    hn = np.linalg.norm(O.as_f64(h_s), axis=1)
+    gw = np.ones(h_s.shape[0]) if grad is None else np.abs(np.asarray(grad, dtype=np.float64))
+    return (np.maximum(q, p) * (per_tok * hn * gw)[:, None]).sum(axis=0)
+
+
 def assert_grad_rows(gpu, ref, name="dh_s", floor=None):
     """Per row: cosine >= COS_MIN and max|d|/max|ref| <= MAXREL; rows whose
     reference norm is below ``floor`` (see grad_floor) must instead agree to

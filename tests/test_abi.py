@@ -40,6 +40,14 @@ def test_workspace_sizes():
     for cv in (2048, 8192):
         b = kd.workspace_size(kd.KD_OP_BWD, N, V, ds, dt, kd.KD_BF16, chunk_V=cv)
         assert b == N * cv * 2 + ds * cv * 2
+        # with dW_s: plus the chunk transposed [chunk_V, Np] and h_s transposed [d_s, Np],
+        # Np = N rounded up to the 128-token tile
+        for n in (N, 300):
+            np_ = -(-n // 128) * 128
+            al = lambda x: -(-x // 256) * 256  # noqa: E731
+            bw = kd.workspace_size(kd.KD_OP_BWD_W, n, V, ds, dt, kd.KD_BF16, chunk_V=cv)
+            b0 = kd.workspace_size(kd.KD_OP_BWD, n, V, ds, dt, kd.KD_BF16, chunk_V=cv)
+            assert bw == b0 + al(cv * np_ * 2) + al(ds * np_ * 2)
     f1 = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt, kd.KD_BF16, beta=1.0)
     f5 = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt, kd.KD_BF16, beta=0.5)
     # forward: one partial record (5 floats; +2 for the JSD sums) per token per
@@ -82,12 +90,22 @@ def test_bwd_and_topk_validation():
     import vocab_chunked_kl_amd as kd
     lib = kd.load_library()
     args = [FAKE, FAKE, FAKE, FAKE, 8, 100, 64, 64, 1.0, 1.0, 1]
-    # chunk_V not a multiple of 256
-    assert lib.kd_bwd(*args, 300, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 40, None) == 1
+    # chunk_V not a multiple of 256, or so large that a 256-row tile of it passes 2 GiB
+    assert lib.kd_bwd(*args, 300, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 40, None) == 1
+    assert lib.kd_bwd(*args, 1 << 22, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 1 << 40, None) == 2
     # workspace too small
-    assert lib.kd_bwd(*args, 256, FAKE, FAKE, FAKE, None, FAKE, FAKE, 16, None) == 3
-    # missing dh
-    assert lib.kd_bwd(*args, 256, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None) == 1
+    assert lib.kd_bwd(*args, 256, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, 16, None) == 3
+    # neither dh nor dW
+    assert lib.kd_bwd(*args, 256, FAKE, FAKE, FAKE, None, None, None, FAKE, 1 << 40, None) == 1
+    # dW with only the dh-sized workspace
+    bws = kd.workspace_size(kd.KD_OP_BWD, 8, 100, 64, 64, kd.KD_BF16, chunk_V=256)
+    assert lib.kd_bwd(*args, 256, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, bws, None) == 3
+    assert lib.kd_bwd(*args, 256, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, bws, None) == 3
+    # dW with more tokens than the token-contracted GEMM's 32-bit tile offsets allow
+    many = [FAKE, FAKE, FAKE, FAKE, 1 << 23, 100, 64, 64, 1.0, 1.0, 1]
+    assert lib.kd_bwd(*many, 256, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None) == 2
+    # misaligned dW
+    assert lib.kd_bwd(*args, 256, FAKE, FAKE, FAKE, None, FAKE, FAKE + 2, FAKE, 1 << 40, None) == 2
     targs = [FAKE, FAKE, FAKE, FAKE, 8, 100, 64, 64]
     outs = [FAKE] * 10
     # k out of range, fp32 inputs, labels without ce

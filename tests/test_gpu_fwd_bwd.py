@@ -5,8 +5,12 @@ Small cases compare every row and span several tiles with ragged tails
 full-size workloads compare a seeded subset of rows (always the first and
 last) computed one by one by the oracle, in the launch configuration the
 benchmark uses. Tolerances (tests/helpers.py): per-token loss and LSEs
-|d| <= 1e-3 |ref| + 1e-5; dL/dh_s per row cosine >= 0.9999 and
-max|d| / max|ref| <= 2e-2.
+|d| <= 1e-3 |ref| + 1e-5; dL/dh_s and dL/dW_s per row cosine >= 0.9999 and
+max|d| / max|ref| <= 2e-2 (rows below the fp32 floor compared absolutely).
+dL/dW_s at full size needs a full [N, V] gradient on the CPU, so it is
+checked there through identities that hold at any size: its rows sum to
+zero, and sum W_s . dW_s equals sum h_s . dh_s (both are the sum of
+dL/dz_s * z_s).
 """
 import sys
 
@@ -15,7 +19,7 @@ import pytest
 
 import kdsynth
 from oracle import kd_oracle as O
-from tests.helpers import assert_close, assert_grad_rows, grad_floor, to_dev, upload, workload
+from tests.helpers import assert_close, assert_grad_rows, grad_floor, to_dev, upload, wgrad_floor, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -147,3 +151,87 @@ def test_workload_heavy_head_v248k_sampled():
     rows = kdsynth.sample_rows(w.N, 20, must=must)
     _say(f"{w.name} N={w.N} V={w.V} rows={len(rows)}")
     run_case(kd, torch, (w.h_s, w.W_s, w.h_t, w.W_t), 1.0, w.tau, rows=rows, chunk_V=8192)
+
+
+# --------------------------------------------------------------------------- dL/dW_s
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("beta,tau", [(0.0, 1.0), (1.0, 1.0), (1.0, 2.0), (0.5, 1.5)])
+def test_weight_gradient_ragged_small(dtype, beta, tau):
+    kd, torch = _kd()
+    N, V, ds, dt = 300, 1000, 64, 200
+    arrays = kdsynth.small_case(11, N, V, ds, dt, dtype=dtype)
+    h_s, W_s, h_t, W_t = arrays
+    grad = np.random.default_rng(4).uniform(-1, 2, size=N)
+    grad[::5] = 0.0
+    _say(f"dW ragged {dtype} N={N} V={V} d_s={ds} d_t={dt} beta={beta} tau={tau}")
+    dev = [to_dev(x) for x in arrays]
+    loss, lse_s, lse_t, aux = kd.kd_fwd(*dev, beta, tau)
+    g = torch.from_numpy(grad.astype(np.float32)).cuda()
+    dh, dW = kd.kd_bwd(*dev, beta, tau, lse_s, lse_t, aux, grad_loss=g, chunk_V=256, want_dW=True)
+    dh_only = kd.kd_bwd(*dev, beta, tau, lse_s, lse_t, aux, grad_loss=g, chunk_V=256)
+    _, dW_only = kd.kd_bwd(*dev, beta, tau, lse_s, lse_t, aux, grad_loss=g, chunk_V=256, want_dh=False,
+                           want_dW=True)
+    torch.cuda.synchronize()
+    ref = O.kd_bwd_w(h_s, W_s, h_t, W_t, beta, tau, grad_loss=grad)
+    assert_grad_rows(dW.cpu().numpy(), ref, name="dW_s", floor=wgrad_floor(h_s, W_s, h_t, W_t, beta, tau, grad))
+    # the dh_s path is unchanged by also asking for dW_s, and dW_s alone is the same
+    assert np.array_equal(dh.cpu().numpy(), dh_only.cpu().numpy())
+    assert np.array_equal(dW.cpu().numpy(), dW_only.cpu().numpy())
+
+
+@pytest.mark.parametrize("N,V", [(1, 2), (1, 300), (129, 2), (65, 257)])
+def test_weight_gradient_degenerate(N, V):
+    kd, torch = _kd()
+    arrays = kdsynth.small_case(5, N, V, 32, 48)
+    dev = [to_dev(x) for x in arrays]
+    for beta in (0.0, 0.5, 1.0):
+        _say(f"dW degenerate N={N} V={V} beta={beta}")
+        loss, lse_s, lse_t, aux = kd.kd_fwd(*dev, beta, 1.0)
+        _, dW = kd.kd_bwd(*dev, beta, 1.0, lse_s, lse_t, aux, chunk_V=256, want_dW=True)
+        torch.cuda.synchronize()
+        ref = O.kd_bwd_w(*arrays, beta, 1.0)
+        assert_grad_rows(dW.cpu().numpy(), ref, name="dW_s", floor=wgrad_floor(*arrays, beta, 1.0))
+
+
+def test_weight_gradient_chunk_invariance():
+    kd, torch = _kd()
+    arrays = kdsynth.small_case(8, 384, 5000, 256, 128)
+    dev = [to_dev(x) for x in arrays]
+    loss, lse_s, lse_t, aux = kd.kd_fwd(*dev, 1.0, 1.0)
+    outs = [kd.kd_bwd(*dev, 1.0, 1.0, lse_s, lse_t, aux, chunk_V=c, want_dh=False, want_dW=True)[1].cpu().numpy()
+            for c in (256, 1024, 8192)]
+    for o in outs[1:]:
+        assert np.allclose(o, outs[0], rtol=1e-4, atol=1e-7)
+
+
+def _identity_check(kd, torch, w, beta, chunk_V):
+    dev = upload(w)
+    loss, lse_s, lse_t, aux = kd.kd_fwd(*dev, beta, w.tau)
+    dh, dW = kd.kd_bwd(*dev, beta, w.tau, lse_s, lse_t, aux, chunk_V=chunk_V, want_dW=True)
+    torch.cuda.synchronize()
+    W_s = dev[1].float()
+    h_s = dev[0].float()
+    a = float((W_s.double() * dW.double()).sum())
+    b = float((h_s.double() * dh.double()).sum())
+    scale = float((W_s.double() * dW.double()).abs().sum())
+    assert abs(a - b) <= 1e-3 * scale, (a, b, scale)
+    col = dW.double().sum(0)
+    assert float(col.abs().max()) <= 1e-3 * float(dW.double().abs().sum(0).max()), float(col.abs().max())
+    assert torch.isfinite(dW).all()
+    del dev, dh, dW
+    torch.cuda.empty_cache()
+
+
+def test_weight_gradient_identities_v152k_n4k():
+    kd, torch = _kd()
+    w = workload(2)
+    _say(f"dW identities {w.name} N={w.N} V={w.V}")
+    _identity_check(kd, torch, w, 1.0, 8192)
+
+
+@pytest.mark.parametrize("beta", [0.0, 1.0])
+def test_weight_gradient_identities_v152k_n32k(beta):
+    kd, torch = _kd()
+    w = workload(3)
+    _say(f"dW identities {w.name} N={w.N} V={w.V} beta={beta}")
+    _identity_check(kd, torch, w, beta, 16384)

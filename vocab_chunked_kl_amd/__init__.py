@@ -34,7 +34,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkd.so")
 KD_OK, KD_ERR_INVALID_ARG, KD_ERR_UNSUPPORTED, KD_ERR_WORKSPACE, KD_ERR_HIP = range(5)
 KD_F32, KD_BF16 = 0, 1
-KD_OP_FWD, KD_OP_BWD, KD_OP_TOPK = 0, 1, 2
+KD_OP_FWD, KD_OP_BWD, KD_OP_TOPK, KD_OP_BWD_W = 0, 1, 2, 3
 KD_TOPK_MAX = 64
 KD_TOPK_MAX_V = 524288
 EXPORTED = ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_status_string", "kd_last_error")
@@ -63,7 +63,7 @@ def load_library(path: str = LIB_PATH):
                                       ctypes.POINTER(sz)]
     lib.kd_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, f32, f32, ctypes.c_int, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, f32, f32, ctypes.c_int, i32, vp, vp, vp, vp, vp, vp,
-                           sz, vp]
+                           vp, sz, vp]
     lib.kd_topk_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, ctypes.c_int, vp, vp, vp, vp, vp, vp,
                                 vp, vp, vp, vp, vp, vp, sz, vp]
     for fn in ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd"):
@@ -147,21 +147,34 @@ def kd_fwd(h_s, W_s, h_t, W_t, beta: float, tau: float, workspace=None, stream=N
 
 
 def kd_bwd(h_s, W_s, h_t, W_t, beta: float, tau: float, lse_s, lse_t, aux, grad_loss=None, chunk_V: int = 8192,
-           workspace=None, stream=None, dh=None):
-    """dL/dh_s (fp32 [N, d_s]) for L = sum_n grad_loss[n] * loss[n]."""
+           workspace=None, stream=None, dh=None, dW=None, want_dh: bool = True, want_dW: bool = False):
+    """dL/dh_s (fp32 [N, d_s]) and, with ``want_dW``, dL/dW_s (fp32 [V, d_s])
+    for L = sum_n grad_loss[n] * loss[n]. Returns dh, or (dh, dW) when
+    ``want_dW`` (dh is None when ``want_dh`` is False)."""
     lib = load_library()
     N, V, d_s, d_t, dt = _inputs(h_s, W_s, h_t, W_t)
     dev = h_s.device
-    if dh is None:
+    if not want_dh and not want_dW:
+        raise ValueError("nothing to compute: want_dh and want_dW are both False")
+    if want_dh and dh is None:
         dh = torch.empty(N, d_s, dtype=torch.float32, device=dev)
-    nbytes = workspace_size(KD_OP_BWD, N, V, d_s, d_t, dt, beta=beta, chunk_V=chunk_V)
+    if want_dW and dW is None:
+        dW = torch.empty(V, d_s, dtype=torch.float32, device=dev)
+    for name, t, shape in (("dh", dh if want_dh else None, (N, d_s)), ("dW", dW if want_dW else None, (V, d_s))):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 tensor of shape {shape}")
+    op = KD_OP_BWD_W if want_dW else KD_OP_BWD
+    nbytes = workspace_size(op, N, V, d_s, d_t, dt, beta=beta, chunk_V=chunk_V)
     ws = _workspace(nbytes, dev, workspace)
     for name, t in (("lse_s", lse_s), ("lse_t", lse_t), ("aux", aux), ("grad_loss", grad_loss)):
         if t is not None and (t.dtype != torch.float32 or t.numel() != N or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous fp32 tensor of {N} elements")
     _check(lib.kd_bwd(_ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t), N, V, d_s, d_t, float(beta), float(tau), dt,
-                      int(chunk_V), _ptr(lse_s), _ptr(lse_t), _ptr(aux), _ptr(grad_loss), _ptr(dh), _ptr(ws),
+                      int(chunk_V), _ptr(lse_s), _ptr(lse_t), _ptr(aux), _ptr(grad_loss),
+                      _ptr(dh if want_dh else None), _ptr(dW if want_dW else None), _ptr(ws),
                       ws.numel() * ws.element_size(), _stream(stream)))
+    if want_dW:
+        return (dh if want_dh else None), dW
     return dh
 
 
@@ -201,12 +214,20 @@ class _KD(torch.autograd.Function):
 
     @staticmethod
     def backward(ctx, grad_loss):
+        # the student hidden state and unembedding receive gradients; the
+        # teacher's inputs are frozen
         xs, ws, xt, wt, lse_s, lse_t, aux = ctx.saved_tensors
-        if ctx.needs_input_grad[1] or ctx.needs_input_grad[2] or ctx.needs_input_grad[3]:
-            raise NotImplementedError("only the student hidden state receives a gradient here")
-        dh = kd_bwd(xs, ws, xt, wt, ctx.beta, ctx.tau, lse_s, lse_t, aux,
-                    grad_loss=grad_loss.float().contiguous(), chunk_V=ctx.chunk_V)
-        return dh.to(xs.dtype), None, None, None, None, None, None
+        if ctx.needs_input_grad[2] or ctx.needs_input_grad[3]:
+            raise NotImplementedError("the teacher's hidden state and unembedding receive no gradient")
+        want_dh, want_dW = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        if not want_dh and not want_dW:
+            return None, None, None, None, None, None, None
+        out = kd_bwd(xs, ws, xt, wt, ctx.beta, ctx.tau, lse_s, lse_t, aux,
+                     grad_loss=grad_loss.float().contiguous(), chunk_V=ctx.chunk_V, want_dh=want_dh,
+                     want_dW=want_dW)
+        dh, dW = out if want_dW else (out, None)
+        return (dh.to(xs.dtype) if dh is not None else None, dW.to(ws.dtype) if dW is not None else None,
+                None, None, None, None, None)
 
 
 def _divergence(xs, xt, ws, wt, beta, temperature, reduction, chunk_V, labels, ignore_index):

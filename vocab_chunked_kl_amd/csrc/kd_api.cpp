@@ -24,6 +24,8 @@ kd_status hip_fail(hipError_t e, const char* where) {
   return KD_ERR_HIP;
 }
 
+constexpr int64_t kMaxTileBytes = 0x7FFFFFF0;  // largest buffer-resource extent
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
@@ -39,8 +41,9 @@ kd_status check_common(const void* h_s, const void* W_s, const void* h_t, const 
     return fail(KD_ERR_UNSUPPORTED, "inputs must be 16-byte aligned");
   // token and vocabulary tile indices are 32-bit in the kernels
   if (N > ((int64_t)1 << 38) || V > ((int64_t)1 << 38)) return fail(KD_ERR_UNSUPPORTED, "N or V too large");
+  // byte offsets inside a 256-row operand tile are 32-bit
   const int64_t esz = dtype == KD_BF16 ? 2 : 4;
-  if ((int64_t)d_s * esz > (int64_t)1 << 30 || (int64_t)d_t * esz > (int64_t)1 << 30)
+  if (256 * (int64_t)d_s * esz >= kMaxTileBytes || 256 * (int64_t)d_t * esz >= kMaxTileBytes)
     return fail(KD_ERR_UNSUPPORTED, "hidden size too large");
   return KD_OK;
 }
@@ -77,8 +80,9 @@ kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t
       *bytes = kd::fwd_workspace_bytes(p, beta > 0.f && beta < 1.f);
       return KD_OK;
     case KD_OP_BWD:
+    case KD_OP_BWD_W:
       if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
-      *bytes = kd::bwd_workspace_bytes(p, chunk_V);
+      *bytes = kd::bwd_workspace_bytes(p, chunk_V, op == KD_OP_BWD_W);
       return KD_OK;
     case KD_OP_TOPK:
       if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
@@ -112,21 +116,30 @@ kd_status kd_fwd(const void* h_s, const void* W_s, const void* h_t, const void* 
 kd_status kd_bwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
                  int32_t d_s, int32_t d_t, float beta, float tau, kd_dtype dtype, int32_t chunk_V,
                  const float* lse_s, const float* lse_t, const float* aux, const float* grad_loss, float* dh_s,
-                 void* workspace, size_t ws_bytes, void* stream) {
+                 float* dW_s, void* workspace, size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
   kd_status s = check_common(h_s, W_s, h_t, W_t, N, V, d_s, d_t, dtype);
   if (s != KD_OK) return s;
   if (bad_beta(beta)) return fail(KD_ERR_INVALID_ARG, "beta outside [0, 1]");
   if (bad_tau(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be positive and finite");
   if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
-  if (!lse_s || !lse_t || !dh_s) return fail(KD_ERR_INVALID_ARG, "null pointer (lse_s, lse_t, dh_s)");
+  const int64_t esz = dtype == KD_BF16 ? 2 : 4;
+  if (256 * (int64_t)chunk_V * esz >= kMaxTileBytes) return fail(KD_ERR_UNSUPPORTED, "chunk_V too large");
+  if (!lse_s || !lse_t) return fail(KD_ERR_INVALID_ARG, "null pointer (lse_s, lse_t)");
+  if (!dh_s && !dW_s) return fail(KD_ERR_INVALID_ARG, "dh_s and dW_s are both null");
   if (!aux && beta > 0.f) return fail(KD_ERR_INVALID_ARG, "aux may be null only for beta == 0");
-  if (!aligned4(dh_s) || !aligned4(lse_s) || !aligned4(lse_t)) return fail(KD_ERR_UNSUPPORTED, "misaligned float arrays");
+  if ((dh_s && !aligned4(dh_s)) || (dW_s && !aligned4(dW_s)) || !aligned4(lse_s) || !aligned4(lse_t))
+    return fail(KD_ERR_UNSUPPORTED, "misaligned float arrays");
+  // the weight-gradient GEMM contracts over the (padded) tokens: 256 such rows stay below 2 GiB
+  if (dW_s && 256 * ((N + 127) / 128 * 128) * esz >= kMaxTileBytes)
+    return fail(KD_ERR_UNSUPPORTED, "too many tokens for dW_s");
   const kd::Plan p = kd::make_plan(N, V, d_s, d_t, dtype == KD_BF16);
-  const size_t need = kd::bwd_workspace_bytes(p, chunk_V);
-  if (!workspace || ws_bytes < need) return fail(KD_ERR_WORKSPACE, "workspace smaller than kd_workspace_size(BWD)");
+  const size_t need = kd::bwd_workspace_bytes(p, chunk_V, dW_s != nullptr);
+  if (!workspace || ws_bytes < need)
+    return fail(KD_ERR_WORKSPACE, dW_s ? "workspace smaller than kd_workspace_size(BWD_W)"
+                                       : "workspace smaller than kd_workspace_size(BWD)");
   if (!aligned16(workspace)) return fail(KD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
-  kd::BwdIO io{h_s, W_s, h_t, W_t, beta, tau, chunk_V, lse_s, lse_t, aux, grad_loss, dh_s, workspace};
+  kd::BwdIO io{h_s, W_s, h_t, W_t, beta, tau, chunk_V, lse_s, lse_t, aux, grad_loss, dh_s, dW_s, workspace};
   hipError_t e = kd::run_bwd(p, io, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KD_OK : hip_fail(e, "kd_bwd launch");
 }

@@ -62,7 +62,7 @@ struct Plan {
 Plan make_plan(int64_t N, int64_t V, int32_t d_s, int32_t d_t, bool bf16);
 size_t align_up(size_t x, size_t a);
 size_t fwd_workspace_bytes(const Plan& p, bool jsd);
-size_t bwd_workspace_bytes(const Plan& p, int32_t chunk_V);
+size_t bwd_workspace_bytes(const Plan& p, int32_t chunk_V, bool with_dW);
 
 struct FwdIO {
   const void *h_s, *W_s, *h_t, *W_t;
@@ -77,7 +77,8 @@ struct BwdIO {
   float beta, tau;
   int32_t chunk_V;
   const float *lse_s, *lse_t, *aux, *grad;
-  float* dh;
+  float* dh;  // may be null when dW is not
+  float* dW;  // may be null
   void* workspace;
 };
 hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t stream);

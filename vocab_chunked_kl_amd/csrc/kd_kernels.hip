@@ -61,9 +61,12 @@ struct LogitArgs {
   int vt_offset;     // first vocabulary tile of the grid (backward chunks)
   float* part;       // forward partial statistics
   const float *lse_s, *lse_t, *aux, *grad;
-  char* G;           // backward gradient chunk
+  char* G;           // backward gradient chunk [N][chunk] (null: not written)
   int64_t ldg;       // G row pitch in bytes
   int64_t g_col0;    // vocabulary index of G's column 0
+  char* GT;          // the same chunk transposed, [chunk][Np] (null: not written)
+  int64_t ldgt;      // GT row pitch in bytes
+  int64_t Np;        // tokens rounded up to the token tile (GT columns written)
 };
 
 __device__ __forceinline__ void merge_online(float& m, float& l, float m2, float l2) {
@@ -361,7 +364,20 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
             }
             g4[e] = (v < a.V) ? g * gsc[nb] : 0.f;
           }
-          if (n < a.N) {
+          if (a.GT && n < a.Np) {
+            // transposed copy for the weight gradient: token-contiguous rows;
+            // tokens past N carry g = 0, so the padding columns are zeros
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int64_t row = vrow0 + mb * 32 + 8 * rg + 4 * (lane >> 5) + e - a.g_col0;
+              char* dst = a.GT + row * a.ldgt;
+              if constexpr (kBf16)
+                *reinterpret_cast<uint16_t*>(dst + n * 2) = (uint16_t)f32_to_bf16_bits(g4[e]);
+              else
+                *reinterpret_cast<float*>(dst + n * 4) = g4[e];
+            }
+          }
+          if (a.G && n < a.N) {
             const int64_t col = vrow0 + mb * 32 + 8 * rg + 4 * (lane >> 5) - a.g_col0;
             char* dst = a.G + n * a.ldg;
             if constexpr (kBf16) {
@@ -405,15 +421,19 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ W,
 }
 
 // ---------------------------------------------------------------------------
-// Backward, step 3: dh[n, d] (+)= sum_j G[n, j] WsT[d, j] over one chunk.
+// Backward, step 3: dh[n, d] (+)= sum_j G[n, j] WsT[d, j] over one chunk, and
+// dW_s[c0 + j, d] = sum_n GT[j, n] hsT[d, n].
 // ---------------------------------------------------------------------------
+// out[r, d] (+)= sum_k A[r, k] B[d, k]: dh (A = G, token rows; B = the W_s
+// chunk transposed) or dW_s (A = G transposed, vocabulary rows of the chunk;
+// B = h_s transposed), both operands contracted over contiguous K.
 struct DhArgs {
-  PairDesc p;        // A = G (token rows), B = WsT (hidden-unit rows)
-  int64_t N;
-  int32_t d_s;
+  PairDesc p;
+  int64_t N;         // valid output rows
+  int32_t d_s;       // output columns (and row pitch)
   int n_tok_tiles, n_d_tiles;
-  float* dh;
-  int first;         // 1: overwrite dh, 0: accumulate
+  float* dh;         // output
+  int first;         // 1: overwrite, 0: accumulate
 };
 
 template <bool kBf16>
@@ -523,8 +543,17 @@ size_t fwd_workspace_bytes(const Plan& p, bool jsd) {
   return align_up(kFwdFields * rec, 256) + (jsd ? align_up(kJsdFields * rec, 256) : 0);
 }
 
-size_t bwd_workspace_bytes(const Plan& p, int32_t chunk_V) {
-  return align_up((size_t)p.N * chunk_V * p.esz, 256) + align_up((size_t)p.d_s * chunk_V * p.esz, 256);
+// Tokens rounded up to the logit token tile: the token extent (K) of the
+// weight-gradient GEMM, zero-padded.
+int64_t padded_tokens(const Plan& p) { return (p.N + kTileT - 1) / kTileT * kTileT; }
+
+size_t bwd_workspace_bytes(const Plan& p, int32_t chunk_V, bool with_dW) {
+  size_t b = align_up((size_t)p.N * chunk_V * p.esz, 256) + align_up((size_t)p.d_s * chunk_V * p.esz, 256);
+  if (with_dW) {
+    const size_t np = (size_t)padded_tokens(p);
+    b += align_up((size_t)chunk_V * np * p.esz, 256) + align_up((size_t)p.d_s * np * p.esz, 256);
+  }
+  return b;
 }
 
 hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
@@ -569,19 +598,45 @@ hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
 
 hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   const int mode = io.beta == 1.f ? kModeRKL : (io.beta == 0.f ? kModeFKL : kModeJSD);
+  const int64_t np = padded_tokens(p);
   char* G = static_cast<char*>(io.workspace);
   char* WsT = G + align_up((size_t)p.N * io.chunk_V * p.esz, 256);
+  char* GT = WsT + align_up((size_t)p.d_s * io.chunk_V * p.esz, 256);
+  char* hsT = GT + align_up((size_t)io.chunk_V * np * p.esz, 256);
   LogitArgs la = logit_args(p, io.h_s, io.W_s, io.h_t, io.W_t, io.tau, io.beta);
   la.lse_s = io.lse_s;
   la.lse_t = io.lse_t;
   la.aux = io.aux;
   la.grad = io.grad;
-  la.G = G;
+  la.G = io.dh ? G : nullptr;
   la.ldg = (int64_t)io.chunk_V * p.esz;
+  la.GT = io.dW ? GT : nullptr;
+  la.ldgt = np * p.esz;
+  la.Np = np;
   la.tiles_per_split = 1;
   const int n_d_tiles = (p.d_s + kTileDhD - 1) / kTileDhD;
   const int n_tok_tiles_dh = (int)((p.N + kTileDhT - 1) / kTileDhT);
   hipError_t e;
+  auto transpose = [&](const void* src, char* dst, int64_t rows, int64_t c0, int64_t cols, int64_t pitch) {
+    const dim3 tgrid((unsigned)(cols / 64), (unsigned)((p.d_s + 63) / 64));
+    if (p.bf16)
+      hipLaunchKernelGGL(transpose_kernel<uint16_t>, tgrid, dim3(256), 0, st, static_cast<const uint16_t*>(src),
+                         reinterpret_cast<uint16_t*>(dst), rows, p.d_s, c0, pitch);
+    else
+      hipLaunchKernelGGL(transpose_kernel<float>, tgrid, dim3(256), 0, st, static_cast<const float*>(src),
+                         reinterpret_cast<float*>(dst), rows, p.d_s, c0, pitch);
+    return hipGetLastError();
+  };
+  auto gemm = [&](const DhArgs& da, int n_row_tiles) {
+    const dim3 dgrid(n_row_tiles * n_d_tiles);
+    if (p.bf16)
+      hipLaunchKernelGGL(dh_kernel<true>, dgrid, dim3(kDhThreads), 0, st, da);
+    else
+      hipLaunchKernelGGL(dh_kernel<false>, dgrid, dim3(kDhThreads), 0, st, da);
+    return hipGetLastError();
+  };
+  // h_s transposed once ([d_s][Np], zero past N): the token-contiguous B operand of dW
+  if (io.dW && (e = transpose(io.h_s, hsT, p.N, 0, np, np)) != hipSuccess) return e;
   for (int64_t c0 = 0; c0 < p.V; c0 += io.chunk_V) {
     const int64_t ccols = (p.V - c0 < io.chunk_V) ? p.V - c0 : io.chunk_V;
     const int ctiles = (int)((ccols + kTileV - 1) / kTileV);
@@ -593,29 +648,32 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
     const dim3 grid(p.n_tok_tiles * ctiles);
     e = p.bf16 ? launch_bwdg_mode<true>(mode, grid, la, st) : launch_bwdg_mode<false>(mode, grid, la, st);
     if (e != hipSuccess) return e;
-    const dim3 tgrid((unsigned)(kcols / 64), (unsigned)((p.d_s + 63) / 64));
-    if (p.bf16)
-      hipLaunchKernelGGL(transpose_kernel<uint16_t>, tgrid, dim3(256), 0, st, static_cast<const uint16_t*>(io.W_s),
-                         reinterpret_cast<uint16_t*>(WsT), p.V, p.d_s, c0, (int64_t)io.chunk_V);
-    else
-      hipLaunchKernelGGL(transpose_kernel<float>, tgrid, dim3(256), 0, st, static_cast<const float*>(io.W_s),
-                         reinterpret_cast<float*>(WsT), p.V, p.d_s, c0, (int64_t)io.chunk_V);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    DhArgs da{};
-    da.p = PairDesc{G, WsT, (int64_t)io.chunk_V * p.esz, (int64_t)io.chunk_V * p.esz, p.N, p.d_s,
-                    (int32_t)(kcols * p.esz)};
-    da.N = p.N;
-    da.d_s = p.d_s;
-    da.n_tok_tiles = n_tok_tiles_dh;
-    da.n_d_tiles = n_d_tiles;
-    da.dh = io.dh;
-    da.first = c0 == 0;
-    const dim3 dgrid(n_tok_tiles_dh * n_d_tiles);
-    if (p.bf16)
-      hipLaunchKernelGGL(dh_kernel<true>, dgrid, dim3(kDhThreads), 0, st, da);
-    else
-      hipLaunchKernelGGL(dh_kernel<false>, dgrid, dim3(kDhThreads), 0, st, da);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (io.dh) {
+      // dh_s (+)= G . W_s[chunk], with the chunk of W_s transposed to [d_s][chunk]
+      if ((e = transpose(io.W_s, WsT, p.V, c0, kcols, io.chunk_V)) != hipSuccess) return e;
+      DhArgs da{};
+      da.p = PairDesc{G, WsT, (int64_t)io.chunk_V * p.esz, (int64_t)io.chunk_V * p.esz, p.N, p.d_s,
+                      (int32_t)(kcols * p.esz)};
+      da.N = p.N;
+      da.d_s = p.d_s;
+      da.n_tok_tiles = n_tok_tiles_dh;
+      da.n_d_tiles = n_d_tiles;
+      da.dh = io.dh;
+      da.first = c0 == 0;
+      if ((e = gemm(da, n_tok_tiles_dh)) != hipSuccess) return e;
+    }
+    if (io.dW) {
+      // dW_s[chunk] = G^T . h_s: rows of the chunk, contracted over the tokens
+      DhArgs dw{};
+      dw.p = PairDesc{GT, hsT, np * p.esz, np * p.esz, kcols, p.d_s, (int32_t)(np * p.esz)};
+      dw.N = ccols;
+      dw.d_s = p.d_s;
+      dw.n_tok_tiles = (int)(kcols / kTileDhT);
+      dw.n_d_tiles = n_d_tiles;
+      dw.dh = io.dW + c0 * p.d_s;
+      dw.first = 1;
+      if ((e = gemm(dw, dw.n_tok_tiles)) != hipSuccess) return e;
+    }
   }
   return hipSuccess;
 }
