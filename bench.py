@@ -9,7 +9,10 @@ step, the roofline of the dominant kernel (the forward sweep, timed with HIP
 events on its own stream) and the fp64 CPU oracle timed on a bounded sample
 of the same workload.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk-v C] [--no-cpu]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk-v C] [--beta B] [--with-dw] [--no-cpu]
+
+--with-dw adds dL/dW_s to the backward (one more GEMM sweep per chunk); the
+default step is the loss and dL/dh_s.
 """
 from __future__ import annotations
 
@@ -35,6 +38,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--chunk-v", type=int, default=16384)
     ap.add_argument("--beta", type=float, default=1.0)
+    ap.add_argument("--with-dw", action="store_true",
+                    help="also compute dL/dW_s in the backward (the step then runs three GEMM sweeps)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"))
@@ -131,11 +136,13 @@ def main():
     dev = [to_dev(x) for x in (w.h_s, w.W_s, w.h_t, w.W_t)]
     stream = torch.cuda.Stream()
     fws = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt_, kd.KD_BF16, beta=beta)
-    bws = kd.workspace_size(kd.KD_OP_BWD, N, V, ds, dt_, kd.KD_BF16, beta=beta, chunk_V=args.chunk_v)
+    bop = kd.KD_OP_BWD_W if args.with_dw else kd.KD_OP_BWD
+    bws = kd.workspace_size(bop, N, V, ds, dt_, kd.KD_BF16, beta=beta, chunk_V=args.chunk_v)
     with torch.cuda.stream(stream):
         ws_f = torch.empty(fws, dtype=torch.uint8, device="cuda")
         ws_b = torch.empty(bws, dtype=torch.uint8, device="cuda")
         dh = torch.empty(N, ds, dtype=torch.float32, device="cuda")
+        dW = torch.empty(V, ds, dtype=torch.float32, device="cuda") if args.with_dw else None
     torch.cuda.synchronize()
     base_mem = torch.cuda.memory_allocated()
     torch.cuda.reset_peak_memory_stats()
@@ -146,7 +153,8 @@ def main():
         loss, lse_s, lse_t, aux = kd.kd_fwd(*dev, beta, tau, workspace=ws_f, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        kd.kd_bwd(*dev, beta, tau, lse_s, lse_t, aux, chunk_V=args.chunk_v, workspace=ws_b, stream=stream, dh=dh)
+        kd.kd_bwd(*dev, beta, tau, lse_s, lse_t, aux, chunk_V=args.chunk_v, workspace=ws_b, stream=stream, dh=dh,
+                  dW=dW, want_dW=args.with_dw)
         return loss
 
     if args.calibrate_copy:  # a plain copy of known size for scaling the byte counters
@@ -178,7 +186,7 @@ def main():
     assert np.isfinite(loss.float().cpu().numpy()).all()
 
     fwd_flops = 2.0 * N * V * (ds + dt_)
-    bwd_flops = 2.0 * N * V * (ds + dt_) + 2.0 * N * V * ds
+    bwd_flops = 2.0 * N * V * (ds + dt_) + 2.0 * N * V * ds * (2 if args.with_dw else 1)
     jsd = 0.0 < beta < 1.0
     step_flops = fwd_flops * (2 if jsd else 1) + bwd_flops
     tok_s = N / (ms_step / 1e3)
@@ -206,7 +214,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: N={N} tokens (B=4 x T=8192), V={V}, d_s={ds}, d_t={dt_}, "
-                               f"beta={beta}, tau={tau}, fwd+bwd (dL/dh_s), chunk_V={args.chunk_v}",
+                               f"beta={beta}, tau={tau}, fwd+bwd (dL/dh_s{', dL/dW_s' if args.with_dw else ''}), "
+                               f"chunk_V={args.chunk_v}",
                    "global_batch": N, "seq_len": 8192, "parallelism": "single GPU"},
         "mfma_frac_step": round(step_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "step_tflops": round(step_flops / (ms_step / 1e3) / 1e12, 1),
