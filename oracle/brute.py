@@ -105,3 +105,24 @@ def three_terms_row(zs, zt, sel, tau):
     cond = math.fsum((math.exp(lp[i]) / P) * (math.log(math.exp(lp[i]) / P) - math.log(math.exp(lq[i]) / Q))
                      for i in sel)
     return binary, cond, P, Q
+
+
+def fd_grad_topk_row(zs, zt, sel, tau, label, wb, wc, we, eps=1e-6):
+    """Central finite differences of wb*binary + wc*cond + we*ce for one row
+    w.r.t. each student logit (selection and teacher fixed)."""
+    def loss(z):
+        b, c, _, _ = three_terms_row(z, zt, sel, tau)
+        out = wb * b + wc * c
+        if label is not None and label != -100:
+            m = max(z)
+            ce = m + math.log(math.fsum(math.exp(x - m) for x in z)) - z[label]
+            out += we * ce
+        return out
+    g = []
+    for i in range(len(zs)):
+        zp = list(zs)
+        zm = list(zs)
+        zp[i] += eps
+        zm[i] -= eps
+        g.append((loss(zp) - loss(zm)) / (2 * eps))
+    return g

@@ -42,7 +42,7 @@ import numpy as np
 __all__ = [
     "as_f64", "bf16_round", "bf16_neighbours", "logits", "lse", "log_softmax", "divergence",
     "kd_fwd", "grad_student_logits", "kd_bwd", "kd_bwd_w", "topk_order", "topk_three_terms", "kd_topk_fwd",
-    "fp32_dot_error_bound", "svd_teacher", "log1mexp",
+    "fp32_dot_error_bound", "svd_teacher", "log1mexp", "topk_grad_student_logits", "kd_topk_bwd",
 ]
 
 _SLAB = 8192  # vocabulary rows converted to fp64 at a time (memory only)
@@ -341,6 +341,71 @@ def kd_topk_fwd(h_s, W_s, h_t, W_t, k: int, tau: float, labels=None, with_bound:
     if with_bound:
         out["zt_exact"] = zt
         out["zt_bound"] = fp32_dot_error_bound(h_t, W_t)
+    return out
+
+
+def topk_grad_student_logits(zs, zt, sel, tau: float, labels=None, w_binary=None, w_cond=None, w_ce=None):
+    """dL/dz_s for L = sum_n w_binary[n] binary[n] + w_cond[n] cond[n] + w_ce[n] ce[n]
+    (the three terms of ``topk_three_terms``), z_s the untempered student
+    logits, with the selection and the teacher's logits held fixed; a weight
+    left as None counts as zero. Derived from the definitions, with q the
+    tempered student softmax, Q its mass on the set, P the teacher's:
+      binary: (-P/Q + (1-P)/(1-Q)) q_v (1[v in K] - Q)           (d/ds)
+      cond:   1[v in K] (q_v / Q - p_v / P)                       (d/ds)
+      ce:     softmax(z_s)_v - 1[v = label]                        (d/dz)
+    and d/dz = (d/ds) / tau. With every entry selected (k = V) the binary
+    term is identically 0 and so is its gradient. Pinned by central finite
+    differences of ``topk_three_terms``."""
+    zs = as_f64(zs)
+    zt = as_f64(zt)
+    n_rows, V = zs.shape
+    rows = np.arange(n_rows)[:, None]
+    zero = np.zeros(n_rows)
+    wb = zero if w_binary is None else np.asarray(w_binary, dtype=np.float64)
+    wc = zero if w_cond is None else np.asarray(w_cond, dtype=np.float64)
+    we = zero if w_ce is None else np.asarray(w_ce, dtype=np.float64)
+    s = zs / tau
+    t = zt / tau
+    q = np.exp(s - lse(s)[:, None])
+    p = np.exp(t - lse(t)[:, None])
+    inK = np.zeros((n_rows, V), dtype=bool)
+    inK[rows, sel] = True
+    Q = np.sum(np.where(inK, q, 0.0), axis=-1)
+    P = np.sum(np.where(inK, p, 0.0), axis=-1)
+    g = np.zeros((n_rows, V))
+    if sel.shape[1] < V:
+        B = -P / Q + (1.0 - P) / (1.0 - Q)
+        g += (wb * B)[:, None] * q * (inK - Q[:, None])
+    g += wc[:, None] * np.where(inK, q / Q[:, None] - p / P[:, None], 0.0)
+    g /= tau
+    if labels is not None:
+        lab = np.asarray(labels, dtype=np.int64)
+        valid = lab != -100
+        r = np.exp(zs - lse(zs)[:, None])
+        ce_g = r.copy()
+        ce_g[np.nonzero(valid)[0], lab[valid]] -= 1.0
+        g += np.where(valid, we, 0.0)[:, None] * ce_g
+    return g
+
+
+def kd_topk_bwd(h_s, W_s, h_t, W_t, k: int, tau: float, labels=None, w_binary=None, w_cond=None, w_ce=None):
+    """dL/dh_s for the weighted three top-k terms of ``kd_topk_fwd``.
+
+    READING: the pages train on the three terms ([Top-K KD, 一.2]) without
+    spelling out their gradient. Here it reaches the student hidden state
+    through the student logits only (the teacher and the selection made from
+    it are fixed), and the bf16 rounding of the student logits is passed
+    straight through: the derivative formulas are evaluated at the same bf16
+    logits the forward terms use."""
+    zs = logits(h_s, W_s)
+    zt = logits(h_t, W_t)
+    zs_b = bf16_round(zs)
+    zt_b = bf16_round(zt)
+    sel = topk_order(zt_b, k)
+    g = topk_grad_student_logits(zs_b, zt_b, sel, tau, labels, w_binary, w_cond, w_ce)
+    out = np.zeros((g.shape[0], W_s.shape[1]))
+    for v0 in range(0, W_s.shape[0], _SLAB):
+        out += g[:, v0:v0 + _SLAB] @ as_f64(W_s[v0:v0 + _SLAB])
     return out
 
 

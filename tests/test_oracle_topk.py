@@ -173,3 +173,56 @@ def test_svd_teacher_pins(method):
     assert np.allclose(h_r @ W_r.T, z @ W_r @ W_r.T, atol=1e-8)  # projected teacher logits
     h_f, W_f, _ = O.svd_teacher(h, W, d, method=method)
     assert np.allclose(h_f @ W_f.T, z, atol=1e-8)  # full rank reproduces the logits
+
+
+# --------------------------------------------------------------------------- top-k gradient
+@pytest.mark.parametrize("tau", (1.0, 1.7))
+def test_topk_gradient_matches_finite_differences(tau):
+    g = np.random.default_rng(21)
+    N, V, k = 4, 60, 8
+    zs, zt = g.normal(0, 2, (N, V)), g.normal(0, 2, (N, V))
+    sel = O.topk_order(zt, k)
+    labels = np.array([3, -100, 59, 17])
+    wb, wc, we = g.uniform(-1, 2, N), g.uniform(-1, 2, N), g.uniform(-1, 2, N)
+    an = O.topk_grad_student_logits(zs, zt, sel, tau, labels, wb, wc, we)
+    for r in range(N):
+        fd = brute.fd_grad_topk_row(zs[r].tolist(), zt[r].tolist(), sel[r].tolist(), tau, int(labels[r]),
+                                    wb[r], wc[r], we[r])
+        assert np.allclose(an[r], fd, atol=1e-8, rtol=1e-6), np.abs(an[r] - np.array(fd)).max()
+    # each term alone, and no labels: the CE part drops out
+    only_b = O.topk_grad_student_logits(zs, zt, sel, tau, None, wb, None, None)
+    only_c = O.topk_grad_student_logits(zs, zt, sel, tau, None, None, wc, None)
+    only_e = O.topk_grad_student_logits(zs, zt, sel, tau, labels, None, None, we)
+    assert np.allclose(only_b + only_c + only_e, an, rtol=1e-12, atol=1e-15)
+    # every term is a function of a softmax (or of log-masses): each row of the gradient sums to zero
+    assert np.all(np.abs(an.sum(-1)) < 1e-12)
+
+
+def test_topk_gradient_full_set_has_no_binary_part():
+    zs, zt = _case(5, V=40)
+    sel = O.topk_order(zt, 40)
+    wb = np.ones(zs.shape[0])
+    assert np.all(O.topk_grad_student_logits(zs, zt, sel, 1.3, None, wb, None, None) == 0.0)
+    # with the full set the conditional KL is forward KL, whose gradient is q - p
+    wc = np.ones(zs.shape[0])
+    gc = O.topk_grad_student_logits(zs, zt, sel, 1.0, None, None, wc, None)
+    assert np.allclose(gc, O.grad_student_logits(zs, zt, 0.0), atol=1e-14)
+
+
+def test_kd_topk_bwd_is_logit_gradient_times_unembedding():
+    g = np.random.default_rng(22)
+    N, V, ds, dt, k = 3, 300, 16, 12, 8
+    h_s, h_t = g.normal(size=(N, ds)), g.normal(size=(N, dt))
+    W_s, W_t = g.normal(0, 0.5, (V, ds)), g.normal(0, 0.5, (V, dt))
+    wb, wc, we = g.uniform(0, 1, N), g.uniform(0, 1, N), g.uniform(0, 1, N)
+    labels = np.array([5, 299, -100])
+    dh = O.kd_topk_bwd(h_s, W_s, h_t, W_t, k, 1.5, labels, wb, wc, we)
+    # straight-through reading: the gradient of the terms at the bf16-rounded
+    # logits, mapped back through z_s = h_s W_s^T; compared on rows one by one
+    for r in range(N):
+        zs = O.bf16_round(h_s[r] @ W_s.T)
+        zt = O.bf16_round(h_t[r] @ W_t.T)
+        sel = O.topk_order(zt[None], k)
+        fd = np.array(brute.fd_grad_topk_row(zs.tolist(), zt.tolist(), sel[0].tolist(), 1.5, int(labels[r]),
+                                             wb[r], wc[r], we[r]))
+        assert np.allclose(dh[r], fd @ W_s, rtol=1e-5, atol=1e-8)
