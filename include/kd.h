@@ -57,7 +57,7 @@ typedef enum {
 
 typedef enum { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
 
-typedef enum { KD_OP_FWD = 0, KD_OP_BWD = 1, KD_OP_TOPK = 2, KD_OP_BWD_W = 3 } kd_op;
+typedef enum { KD_OP_FWD = 0, KD_OP_BWD = 1, KD_OP_TOPK = 2, KD_OP_BWD_W = 3, KD_OP_TOPK_BWD = 4 } kd_op;
 
 /* Largest k accepted by kd_topk_fwd. */
 #define KD_TOPK_MAX 64
@@ -67,7 +67,8 @@ typedef enum { KD_OP_FWD = 0, KD_OP_BWD = 1, KD_OP_TOPK = 2, KD_OP_BWD_W = 3 } k
 /*
  * kd_workspace_size - device workspace (bytes) that `op` needs for this shape.
  *   op: KD_OP_FWD (kd_fwd), KD_OP_BWD (kd_bwd without dW_s), KD_OP_BWD_W
- *   (kd_bwd with dW_s) or KD_OP_TOPK (kd_topk_fwd).
+ *   (kd_bwd with dW_s), KD_OP_TOPK (kd_topk_fwd) or KD_OP_TOPK_BWD
+ *   (kd_topk_bwd: the same chunk buffers as KD_OP_BWD).
  *   beta is read for KD_OP_FWD, chunk_V for the backward ops, k for
  *   KD_OP_TOPK; d_s/d_t/dtype size the backward's per-chunk buffers.
  *   The backward's workspace is O(N * chunk_V) (the gradient tile G of one
@@ -160,12 +161,47 @@ kd_status kd_bwd(const void* h_s, const void* W_s, const void* h_t, const void* 
  *   binary_kl, cond_kl, p_mass, q_mass, lse_s, lse_t (device, [N] fp32,
  *            written): lse_* over the tempered bf16 logits.
  *   ce       (device, [N] fp32, written when labels != NULL; may be NULL).
+ *   lse_s1   (device, [N] fp32, written; may be NULL): natural-log LSE of the
+ *            untempered bf16 student logits (the CE's; kd_topk_bwd reads it).
  */
 kd_status kd_topk_fwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
                       int32_t d_s, int32_t d_t, int32_t k, float tau, kd_dtype dtype, const int32_t* labels,
                       int32_t* topk_idx, float* topk_val, float* topk_val_s, float* binary_kl, float* cond_kl, float* ce,
-                      float* p_mass, float* q_mass, float* lse_s, float* lse_t, void* workspace, size_t ws_bytes,
-                      void* stream);
+                      float* p_mass, float* q_mass, float* lse_s, float* lse_t, float* lse_s1, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/*
+ * kd_topk_bwd - gradient of sum_n (grad_binary[n] binary_kl[n] + grad_cond[n]
+ *   cond_kl[n] + grad_ce[n] ce[n]) with respect to h_s, for the terms of
+ *   kd_topk_fwd. Source: lpnh.cn "Top-K知识蒸馏损失实现详解", section 一.2 (the
+ *   three terms are the training loss). The pages do not spell the gradient
+ *   out; here the selection and the teacher are held fixed and the bf16
+ *   rounding of the student logits is passed straight through. With q the
+ *   tempered student softmax, r the untempered one, Q / P the student /
+ *   teacher mass on the set K and p^ the renormalised teacher on K:
+ *     dL/dz_v = [ w_b B q_v (1[v in K] - Q) + w_c 1[v in K] (q_v / Q - p^_v) ] / tau
+ *               + w_ce (r_v - 1[v = label]),      B = -P/Q + (1-P)/(1-Q)
+ *   (B = 0 when k == V), and dh_s[n] = sum_v dL/dz_v W_s[v].
+ *   Only KD_BF16 inputs; d_t and the teacher's arrays are not needed.
+ *
+ *   h_s, W_s (device, read): the forward's student inputs.
+ *   k, tau, labels: as given to kd_topk_fwd (labels may be NULL).
+ *   topk_idx, topk_val, topk_val_s, p_mass, q_mass, lse_s (device, read):
+ *            kd_topk_fwd's outputs (topk_val / topk_val_s must have been
+ *            requested there).
+ *   lse_s1   (device, [N] fp32, read): kd_topk_fwd's lse_s1; needed when
+ *            grad_ce and labels are given, else may be NULL.
+ *   grad_binary, grad_cond, grad_ce (device, [N] fp32, read; each may be NULL
+ *            = zero weights).
+ *   chunk_V: as for kd_bwd. dh_s (device, [N, d_s] fp32, 16-byte aligned,
+ *            overwritten).
+ *   workspace (device, >= kd_workspace_size(KD_OP_TOPK_BWD, ...) bytes).
+ */
+kd_status kd_topk_bwd(const void* h_s, const void* W_s, int64_t N, int64_t V, int32_t d_s, int32_t k, float tau,
+                      kd_dtype dtype, const int32_t* labels, const int32_t* topk_idx, const float* topk_val,
+                      const float* topk_val_s, const float* p_mass, const float* q_mass, const float* lse_s,
+                      const float* lse_s1, const float* grad_binary, const float* grad_cond, const float* grad_ce,
+                      int32_t chunk_V, float* dh_s, void* workspace, size_t ws_bytes, void* stream);
 
 /* kd_status_string - a static, human-readable name for a status code. */
 const char* kd_status_string(kd_status s);

@@ -388,8 +388,12 @@ def topk_grad_student_logits(zs, zt, sel, tau: float, labels=None, w_binary=None
     return g
 
 
-def kd_topk_bwd(h_s, W_s, h_t, W_t, k: int, tau: float, labels=None, w_binary=None, w_cond=None, w_ce=None):
+def kd_topk_bwd(h_s, W_s, h_t, W_t, k: int, tau: float, labels=None, w_binary=None, w_cond=None, w_ce=None,
+                sel=None):
     """dL/dh_s for the weighted three top-k terms of ``kd_topk_fwd``.
+
+    ``sel`` [rows, k], when given, is the selection to hold fixed (the one a
+    forward pass made, e.g. on a bf16 tie); by default the oracle's own.
 
     READING: the pages train on the three terms ([Top-K KD, 一.2]) without
     spelling out their gradient. Here it reaches the student hidden state
@@ -401,8 +405,9 @@ def kd_topk_bwd(h_s, W_s, h_t, W_t, k: int, tau: float, labels=None, w_binary=No
     zt = logits(h_t, W_t)
     zs_b = bf16_round(zs)
     zt_b = bf16_round(zt)
-    sel = topk_order(zt_b, k)
-    g = topk_grad_student_logits(zs_b, zt_b, sel, tau, labels, w_binary, w_cond, w_ce)
+    if sel is None:
+        sel = topk_order(zt_b, k)
+    g = topk_grad_student_logits(zs_b, zt_b, np.asarray(sel, dtype=np.int64), tau, labels, w_binary, w_cond, w_ce)
     out = np.zeros((g.shape[0], W_s.shape[1]))
     for v0 in range(0, W_s.shape[0], _SLAB):
         out += g[:, v0:v0 + _SLAB] @ as_f64(W_s[v0:v0 + _SLAB])

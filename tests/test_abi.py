@@ -107,7 +107,7 @@ def test_bwd_and_topk_validation():
     # misaligned dW
     assert lib.kd_bwd(*args, 256, FAKE, FAKE, FAKE, None, FAKE, FAKE + 2, FAKE, 1 << 40, None) == 2
     targs = [FAKE, FAKE, FAKE, FAKE, 8, 100, 64, 64]
-    outs = [FAKE] * 10
+    outs = [FAKE] * 11
     # k out of range, fp32 inputs, labels without ce
     assert lib.kd_topk_fwd(*targs, 0, 1.0, 1, None, *outs, FAKE, 1 << 40, None) == 1
     assert lib.kd_topk_fwd(*targs, 200, 1.0, 1, None, *outs, FAKE, 1 << 40, None) == 1
@@ -118,3 +118,27 @@ def test_bwd_and_topk_validation():
     o = list(outs)
     o[5] = None  # ce
     assert lib.kd_topk_fwd(*targs, 8, 1.0, 1, FAKE, *o, FAKE, 1 << 40, None) == 1
+
+
+def test_topk_bwd_validation():
+    import vocab_chunked_kl_amd as kd
+    lib = kd.load_library()
+
+    def call(**kw):
+        a = dict(h_s=FAKE, W_s=FAKE, N=8, V=100, d_s=64, k=8, tau=1.0, dtype=1, labels=None, idx=FAKE, val=FAKE,
+                 val_s=FAKE, p_mass=FAKE, q_mass=FAKE, lse_s=FAKE, lse_s1=FAKE, gb=FAKE, gc=FAKE, ge=None,
+                 chunk=256, dh=FAKE, ws=FAKE, ws_bytes=1 << 40, stream=None)
+        a.update(kw)
+        return lib.kd_topk_bwd(*[a[n] for n in ("h_s", "W_s", "N", "V", "d_s", "k", "tau", "dtype", "labels", "idx",
+                                                "val", "val_s", "p_mass", "q_mass", "lse_s", "lse_s1", "gb", "gc",
+                                                "ge", "chunk", "dh", "ws", "ws_bytes", "stream")])
+    assert call(dtype=0) == 2                    # bf16 only
+    assert call(k=0) == 1 and call(k=101) == 1   # k outside [1, min(V, 64)]
+    assert call(val_s=None) == 1                 # needs the forward's selected logits
+    assert call(ge=FAKE, labels=FAKE, lse_s1=None) == 1  # CE gradient needs the untempered LSE
+    assert call(dh=FAKE + 4) == 2                # dh_s must be 16-byte aligned
+    assert call(chunk=300) == 1
+    assert call(tau=0.0) == 1
+    need = kd.workspace_size(kd.KD_OP_TOPK_BWD, 8, 100, 64, 64, kd.KD_BF16, chunk_V=256)
+    assert need == kd.workspace_size(kd.KD_OP_BWD, 8, 100, 64, 64, kd.KD_BF16, chunk_V=256)
+    assert call(ws_bytes=need - 1) == 3

@@ -1,7 +1,9 @@
-"""GPU parity of kd_topk_fwd (top-k three-term KD over bf16 logits) against
-the fp64 oracle, through the C ABI. Selection is compared index for index;
-logits that sit within the fp32 accumulation bound of a bf16 rounding
-midpoint may round either way (tests/helpers.check_topk_rows)."""
+"""GPU parity of kd_topk_fwd (top-k three-term KD over bf16 logits) and
+kd_topk_bwd against the fp64 oracle, through the C ABI. Selection is compared
+index for index; logits that sit within the fp32 accumulation bound of a bf16
+rounding midpoint may round either way (tests/helpers.check_topk_rows). The
+gradient is compared with the oracle's gradient for the selection the GPU
+made (per row cosine >= 0.9999, max|d| / max|ref| <= 2e-2)."""
 import sys
 
 import numpy as np
@@ -9,7 +11,7 @@ import pytest
 
 import kdsynth
 from oracle import kd_oracle as O
-from tests.helpers import check_topk_rows, to_dev, workload
+from tests.helpers import assert_grad_rows, check_topk_rows, to_dev, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -96,3 +98,70 @@ def test_topk_workload_svd256_teacher_sampled():
     exact, flagged = check_topk_rows(out, w.h_s, w.W_s, h_rb, W_rb, rows, w.k, w.tau, w.labels)
     print(f"exact {exact} flagged {flagged}", flush=True)
     assert exact >= len(rows) // 2
+
+
+# --------------------------------------------------------------------------- kd_topk_bwd
+def _bwd_case(kd, torch, arrays, k, tau, labels, rows, seed, chunk_V=256):
+    h_s, W_s, h_t, W_t = arrays
+    N = h_s.shape[0]
+    rng = np.random.default_rng(seed)
+    wb, wc, we = rng.uniform(-0.5, 1.5, N), rng.uniform(-0.5, 1.5, N), rng.uniform(0.0, 1.0, N)
+    dev = [to_dev(x) for x in arrays]
+    lab = None if labels is None else torch.from_numpy(labels.astype(np.int32)).cuda()
+    out = kd.kd_topk_fwd(*dev, k, tau, labels=lab)
+    f32 = lambda a: torch.from_numpy(a.astype(np.float32)).cuda()  # noqa: E731
+    dh = kd.kd_topk_bwd(dev[0], dev[1], out, k, tau, labels=lab, grad_binary=f32(wb), grad_cond=f32(wc),
+                        grad_ce=f32(we) if labels is not None else None, chunk_V=chunk_V)
+    torch.cuda.synchronize()
+    sel = out["idx"].cpu().numpy()[rows]
+    ref = O.kd_topk_bwd(h_s[rows], W_s, h_t[rows], W_t, k, tau, None if labels is None else labels[rows],
+                        wb[rows], wc[rows], we[rows] if labels is not None else None, sel=sel)
+    assert_grad_rows(dh.cpu().numpy()[rows], ref, name="topk dh_s")
+    return out, dh
+
+
+@pytest.mark.parametrize("k", [1, 8, 64])
+@pytest.mark.parametrize("tau", [1.0, 1.5])
+def test_topk_bwd_ragged_small(k, tau):
+    kd, torch = _kd()
+    N, V, ds, dt = 150, 5000, 64, 128
+    arrays = kdsynth.small_case(21, N, V, ds, dt)
+    labels = kdsynth.uniform_labels(5, N, V, ignore_frac=0.2)
+    print(f"topk bwd ragged N={N} V={V} k={k} tau={tau}", flush=True)
+    _bwd_case(kd, torch, arrays, k, tau, labels, np.arange(N), seed=31)
+
+
+def test_topk_bwd_without_labels_and_k_equals_v():
+    kd, torch = _kd()
+    N, V = 40, 64
+    arrays = kdsynth.small_case(23, N, V, 16, 16)
+    print("topk bwd k == V, no labels", flush=True)
+    _bwd_case(kd, torch, arrays, 64, 1.0, None, np.arange(N), seed=32)
+
+
+def test_topk_bwd_workload_v248k_sampled():
+    kd, torch = _kd()
+    w = workload(5)
+    rows = kdsynth.sample_rows(w.N, 8)
+    print(f"topk bwd {w.name} N={w.N} V={w.V} rows={len(rows)}", flush=True)
+    _bwd_case(kd, torch, (w.h_s, w.W_s, w.h_t, w.W_t), w.k, w.tau, w.labels, rows, seed=33, chunk_V=16384)
+
+
+def test_topk_kd_autograd_matches_direct_call():
+    kd, torch = _kd()
+    N, V, ds, dt = 96, 3000, 64, 64
+    arrays = kdsynth.small_case(24, N, V, ds, dt)
+    labels = kdsynth.uniform_labels(7, N, V, ignore_frac=0.1)
+    dev = [to_dev(x) for x in arrays]
+    lab = torch.from_numpy(labels.astype(np.int64)).cuda()
+    xs = dev[0].clone().requires_grad_(True)
+    terms = kd.topk_kd(xs, dev[2], dev[1], dev[3], k=16, labels=lab, temperature=1.3, chunk_V=1024)
+    valid = (lab != -100).float()
+    loss = (0.7 * terms["binary"] + 1.1 * terms["cond"] + 0.3 * torch.nan_to_num(terms["ce"]) * valid).sum()
+    loss.backward()
+    out = kd.kd_topk_fwd(*dev, 16, 1.3, labels=lab.to(torch.int32))
+    g = lambda c: torch.full((N,), c, dtype=torch.float32, device="cuda")  # noqa: E731
+    direct = kd.kd_topk_bwd(dev[0], dev[1], out, 16, 1.3, labels=lab.to(torch.int32), grad_binary=g(0.7),
+                            grad_cond=g(1.1), grad_ce=0.3 * valid, chunk_V=1024)
+    torch.cuda.synchronize()
+    assert torch.allclose(xs.grad.float(), direct.to(torch.bfloat16).float(), rtol=1e-2, atol=1e-3)

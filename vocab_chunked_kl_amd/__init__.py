@@ -26,7 +26,7 @@ import os
 import torch
 
 __all__ = [
-    "KDError", "load_library", "workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd",
+    "KDError", "load_library", "workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd",
     "forward_kl", "reverse_kl", "jsd", "topk_kd", "KD_TOPK_MAX",
 ]
 
@@ -34,10 +34,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkd.so")
 KD_OK, KD_ERR_INVALID_ARG, KD_ERR_UNSUPPORTED, KD_ERR_WORKSPACE, KD_ERR_HIP = range(5)
 KD_F32, KD_BF16 = 0, 1
-KD_OP_FWD, KD_OP_BWD, KD_OP_TOPK, KD_OP_BWD_W = 0, 1, 2, 3
+KD_OP_FWD, KD_OP_BWD, KD_OP_TOPK, KD_OP_BWD_W, KD_OP_TOPK_BWD = 0, 1, 2, 3, 4
 KD_TOPK_MAX = 64
 KD_TOPK_MAX_V = 524288
-EXPORTED = ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_status_string", "kd_last_error")
+EXPORTED = ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_status_string",
+            "kd_last_error")
 
 
 class KDError(RuntimeError):
@@ -65,8 +66,10 @@ def load_library(path: str = LIB_PATH):
     lib.kd_bwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, f32, f32, ctypes.c_int, i32, vp, vp, vp, vp, vp, vp,
                            vp, sz, vp]
     lib.kd_topk_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, f32, ctypes.c_int, vp, vp, vp, vp, vp, vp,
-                                vp, vp, vp, vp, vp, vp, sz, vp]
-    for fn in ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd"):
+                                vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_topk_bwd.argtypes = [vp, vp, i64, i64, i32, i32, f32, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                vp, i32, vp, vp, sz, vp]
+    for fn in ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
@@ -188,7 +191,7 @@ def kd_topk_fwd(h_s, W_s, h_t, W_t, k: int, tau: float, labels=None, workspace=N
                val=torch.empty(N, k, dtype=torch.float32, device=dev) if with_values else None,
                val_s=torch.empty(N, k, dtype=torch.float32, device=dev) if with_values else None,
                binary=f(), cond=f(), ce=f() if labels is not None else None, p_mass=f(), q_mass=f(),
-               lse_s=f(), lse_t=f())
+               lse_s=f(), lse_t=f(), lse_s1=f())
     if labels is not None and (labels.dtype != torch.int32 or labels.numel() != N or not labels.is_contiguous()):
         raise ValueError("labels must be a contiguous int32 tensor of N elements")
     nbytes = workspace_size(KD_OP_TOPK, N, V, d_s, d_t, dt, k=k)
@@ -197,8 +200,34 @@ def kd_topk_fwd(h_s, W_s, h_t, W_t, k: int, tau: float, labels=None, workspace=N
                            _ptr(labels), _ptr(out["idx"]), _ptr(out["val"]), _ptr(out["val_s"]), _ptr(out["binary"]),
                            _ptr(out["cond"]),
                            _ptr(out["ce"]), _ptr(out["p_mass"]), _ptr(out["q_mass"]), _ptr(out["lse_s"]),
-                           _ptr(out["lse_t"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+                           _ptr(out["lse_t"]), _ptr(out["lse_s1"]), _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream(stream)))
     return out
+
+
+def kd_topk_bwd(h_s, W_s, fwd: dict, k: int, tau: float, labels=None, grad_binary=None, grad_cond=None,
+                grad_ce=None, chunk_V: int = 8192, workspace=None, stream=None, dh=None):
+    """dL/dh_s (fp32 [N, d_s]) of sum_n grad_binary[n] binary[n] + grad_cond[n] cond[n]
+    + grad_ce[n] ce[n]; ``fwd`` is the dict returned by ``kd_topk_fwd`` for the
+    same inputs (called with ``with_values=True``)."""
+    lib = load_library()
+    N, V, d_s, _, dt = _inputs(h_s, W_s, h_s, W_s)
+    dev = h_s.device
+    if fwd.get("val") is None or fwd.get("val_s") is None:
+        raise ValueError("kd_topk_bwd needs the selected logits: call kd_topk_fwd with with_values=True")
+    for name, t in (("grad_binary", grad_binary), ("grad_cond", grad_cond), ("grad_ce", grad_ce)):
+        if t is not None and (t.dtype != torch.float32 or t.numel() != N or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous fp32 tensor of {N} elements")
+    if dh is None:
+        dh = torch.empty(N, d_s, dtype=torch.float32, device=dev)
+    nbytes = workspace_size(KD_OP_TOPK_BWD, N, V, d_s, d_s, dt, chunk_V=chunk_V)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.kd_topk_bwd(_ptr(h_s), _ptr(W_s), N, V, d_s, int(k), float(tau), dt, _ptr(labels),
+                           _ptr(fwd["idx"]), _ptr(fwd["val"]), _ptr(fwd["val_s"]), _ptr(fwd["p_mass"]),
+                           _ptr(fwd["q_mass"]), _ptr(fwd["lse_s"]), _ptr(fwd.get("lse_s1")), _ptr(grad_binary),
+                           _ptr(grad_cond), _ptr(grad_ce), int(chunk_V), _ptr(dh), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream)))
+    return dh
 
 
 # ---------------------------------------------------------------------------
@@ -268,13 +297,42 @@ def jsd(xs, xt, ws, wt, beta=0.5, temperature=1.0, reduction="mean", chunk_V=204
     return _divergence(xs, xt, ws, wt, beta, temperature, reduction, chunk_V, labels, ignore_index)
 
 
-def topk_kd(xs, xt, ws, wt, k=64, labels=None, temperature=1.0, ignore_index=-100):
-    """Top-k three-term KD terms per token (no gradient): dict with ``binary``,
-    ``cond``, ``ce`` (when labels are given), masses, LSEs and the selection."""
+class _TopK(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, xs, ws, xt, wt, k, tau, lab, chunk_V, holder):
+        out = kd_topk_fwd(xs, ws, xt, wt, k, tau, labels=lab)
+        holder.update(out)
+        ctx.save_for_backward(xs, ws)
+        ctx.out, ctx.k, ctx.tau, ctx.lab, ctx.chunk_V = out, k, tau, lab, chunk_V
+        ce = out["ce"] if out["ce"] is not None else torch.zeros_like(out["binary"])
+        return out["binary"], out["cond"], ce
+
+    @staticmethod
+    def backward(ctx, g_binary, g_cond, g_ce):
+        xs, ws = ctx.saved_tensors
+        if ctx.needs_input_grad[1] or ctx.needs_input_grad[2] or ctx.needs_input_grad[3]:
+            raise NotImplementedError("the top-k terms give a gradient to the student hidden state only")
+        if not ctx.needs_input_grad[0]:
+            return (None,) * 9
+        f = lambda g: None if g is None else g.float().contiguous()  # noqa: E731
+        dh = kd_topk_bwd(xs, ws, ctx.out, ctx.k, ctx.tau, labels=ctx.lab, grad_binary=f(g_binary),
+                         grad_cond=f(g_cond), grad_ce=f(g_ce) if ctx.lab is not None else None,
+                         chunk_V=ctx.chunk_V)
+        return (dh.to(xs.dtype),) + (None,) * 8
+
+
+def topk_kd(xs, xt, ws, wt, k=64, labels=None, temperature=1.0, ignore_index=-100, chunk_V=8192):
+    """Top-k three-term KD terms per token: dict with ``binary``, ``cond``,
+    ``ce`` (when labels are given; these three carry the gradient to ``xs``),
+    masses, LSEs and the selection."""
     d_s, d_t = xs.shape[-1], xt.shape[-1]
     lab = None
     if labels is not None:
         lab = labels.reshape(-1).to(torch.int32).contiguous()
         lab = torch.where(lab == ignore_index, torch.full_like(lab, -100), lab)
-    return kd_topk_fwd(xs.reshape(-1, d_s).contiguous(), ws.contiguous(), xt.reshape(-1, d_t).contiguous(),
-                       wt.contiguous(), k, temperature, labels=lab)
+    xs2 = xs.reshape(-1, d_s).contiguous()
+    holder = {}
+    binary, cond, ce = _TopK.apply(xs2, ws.contiguous(), xt.reshape(-1, d_t).contiguous(), wt.contiguous(), int(k),
+                                   float(temperature), lab, int(chunk_V), holder)
+    holder.update(binary=binary, cond=cond, ce=ce if lab is not None else None)
+    return holder

@@ -88,6 +88,10 @@ kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t
       if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
       *bytes = kd::topk_workspace_bytes(p, k);
       return KD_OK;
+    case KD_OP_TOPK_BWD:
+      if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
+      *bytes = kd::bwd_workspace_bytes(p, chunk_V, false);
+      return KD_OK;
   }
   return fail(KD_ERR_INVALID_ARG, "unknown op");
 }
@@ -147,8 +151,8 @@ kd_status kd_bwd(const void* h_s, const void* W_s, const void* h_t, const void* 
 kd_status kd_topk_fwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
                       int32_t d_s, int32_t d_t, int32_t k, float tau, kd_dtype dtype, const int32_t* labels,
                       int32_t* topk_idx, float* topk_val, float* topk_val_s, float* binary_kl, float* cond_kl, float* ce,
-                      float* p_mass, float* q_mass, float* lse_s, float* lse_t, void* workspace, size_t ws_bytes,
-                      void* stream) {
+                      float* p_mass, float* q_mass, float* lse_s, float* lse_t, float* lse_s1, void* workspace,
+                      size_t ws_bytes, void* stream) {
   g_last_error[0] = 0;
   kd_status s = check_common(h_s, W_s, h_t, W_t, N, V, d_s, d_t, dtype);
   if (s != KD_OK) return s;
@@ -164,9 +168,37 @@ kd_status kd_topk_fwd(const void* h_s, const void* W_s, const void* h_t, const v
   if (!workspace || ws_bytes < need) return fail(KD_ERR_WORKSPACE, "workspace smaller than kd_workspace_size(TOPK)");
   if (!aligned16(workspace)) return fail(KD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
   kd::TopkIO io{h_s, W_s, h_t, W_t, k, tau, labels, topk_idx, topk_val, topk_val_s, binary_kl, cond_kl, ce, p_mass,
-                q_mass, lse_s, lse_t, workspace};
+                q_mass, lse_s, lse_t, lse_s1, workspace};
   hipError_t e = kd::run_topk(p, io, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KD_OK : hip_fail(e, "kd_topk_fwd launch");
+}
+
+kd_status kd_topk_bwd(const void* h_s, const void* W_s, int64_t N, int64_t V, int32_t d_s, int32_t k, float tau,
+                      kd_dtype dtype, const int32_t* labels, const int32_t* topk_idx, const float* topk_val,
+                      const float* topk_val_s, const float* p_mass, const float* q_mass, const float* lse_s,
+                      const float* lse_s1, const float* grad_binary, const float* grad_cond, const float* grad_ce,
+                      int32_t chunk_V, float* dh_s, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  // the teacher's arrays are not read: the student's stand in for the shape checks
+  kd_status s = check_common(h_s, W_s, h_s, W_s, N, V, d_s, d_s, dtype);
+  if (s != KD_OK) return s;
+  if (dtype != KD_BF16) return fail(KD_ERR_UNSUPPORTED, "kd_topk_bwd takes bf16 inputs only");
+  if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
+  if (bad_tau(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be positive and finite");
+  if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
+  if (256 * (int64_t)chunk_V * 2 >= kMaxTileBytes) return fail(KD_ERR_UNSUPPORTED, "chunk_V too large");
+  if (!topk_idx || !topk_val || !topk_val_s || !p_mass || !q_mass || !lse_s || !dh_s)
+    return fail(KD_ERR_INVALID_ARG, "null input or output pointer");
+  if (grad_ce && labels && !lse_s1) return fail(KD_ERR_INVALID_ARG, "lse_s1 is needed for the CE gradient");
+  if (!aligned16(dh_s)) return fail(KD_ERR_UNSUPPORTED, "dh_s must be 16-byte aligned");
+  const kd::Plan p = kd::make_plan(N, V, d_s, d_s, true);
+  const size_t need = kd::bwd_workspace_bytes(p, chunk_V, false);
+  if (!workspace || ws_bytes < need) return fail(KD_ERR_WORKSPACE, "workspace smaller than kd_workspace_size(TOPK_BWD)");
+  if (!aligned16(workspace)) return fail(KD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  kd::TopkBwdIO io{h_s, W_s, k, tau, chunk_V, labels, topk_idx, topk_val, topk_val_s, p_mass, q_mass, lse_s,
+                   grad_ce && labels ? lse_s1 : nullptr, grad_binary, grad_cond, grad_ce, dh_s, workspace};
+  hipError_t e = kd::run_topk_bwd(p, io, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KD_OK : hip_fail(e, "kd_topk_bwd launch");
 }
 
 }  // extern "C"

@@ -89,10 +89,24 @@ struct TopkIO {
   float tau;
   const int32_t* labels;
   int32_t* idx;
-  float *val, *val_s, *binary, *cond, *ce, *p_mass, *q_mass, *lse_s, *lse_t;
+  float *val, *val_s, *binary, *cond, *ce, *p_mass, *q_mass, *lse_s, *lse_t, *lse_s1;
   void* workspace;
 };
 size_t topk_workspace_bytes(const Plan& p, int32_t k);
+
+struct TopkBwdIO {
+  const void *h_s, *W_s;
+  int32_t k;
+  float tau;
+  int32_t chunk_V;
+  const int32_t* labels;
+  const int32_t* idx;
+  const float *val_t, *val_s, *p_mass, *q_mass, *lse_s, *lse_s1;
+  const float *grad_binary, *grad_cond, *grad_ce;
+  float* dh;
+  void* workspace;
+};
+hipError_t run_topk_bwd(const Plan& p, const TopkBwdIO& io, hipStream_t stream);
 hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t stream);
 
 }  // namespace kd

@@ -479,6 +479,163 @@ __global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
   sweep<kBf16, TM, TN, WM, WN, kDhBuf, kDhRB, false>(a.p, a.p, (int64_t)dt * TN, tt, tt + 1, lds, epi);
 }
 
+// ---------------------------------------------------------------------------
+// Top-k backward ([Top-K KD] 一.2 terms; gradient reading: selection and
+// teacher fixed, bf16 rounding of the student logits passed straight through).
+// dL/dz_s = dense + sparse, with q the tempered student softmax, r the
+// untempered one, Q / P the student / teacher mass on the set K:
+//   dense  (every v): -w_b B Q q_v / tau + w_ce r_v,   B = -P/Q + (1-P)/(1-Q)
+//   sparse (v in K):  (w_b B q_v + w_c (q_v / Q - p_v / P)) / tau
+//   sparse (v = y):   -w_ce
+// The sparse part is a k+1-row gather per token; the dense part is a
+// student-only recompute sweep writing G (bf16) for the dh GEMM.
+// ---------------------------------------------------------------------------
+struct TopkBwdArgs {
+  PairDesc ps;        // (W_s, h_s)
+  int64_t N, V;
+  int k;
+  float c2, inv_tau;  // log2(e) / tau, 1 / tau
+  const int32_t* labels;
+  const int32_t* idx;
+  const float *val_t, *val_s, *p_mass, *q_mass, *lse_s, *lse_s1, *gb, *gc, *ge;
+  int n_tok_tiles, n_splits, tiles_per_split, n_vtiles, vt_offset;
+  char* G;
+  int64_t ldg, g_col0;
+  float* dh;
+  int32_t d_s;
+};
+
+// B of the binary term for token n (0 when the set is the whole vocabulary).
+__device__ __forceinline__ float topk_binary_slope(const TopkBwdArgs& a, int64_t n) {
+  if ((int64_t)a.k >= a.V) return 0.f;
+  const float P = a.p_mass[n], Q = a.q_mass[n];
+  return -P / Q + (1.f - P) / (1.f - Q);
+}
+
+__device__ __forceinline__ float topk_ce_weight(const TopkBwdArgs& a, int64_t n) {
+  if (!a.ge || !a.labels) return 0.f;
+  const int32_t y = a.labels[n];
+  return (y >= 0 && y < a.V) ? a.ge[n] : 0.f;
+}
+
+__global__ __launch_bounds__(kLogitThreads, 1) void topk_bwdg_kernel(TopkBwdArgs a) {
+  constexpr int TM = kTileV, TN = kTileT, WM = kLogitWM, WN = kLogitWN;
+  constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
+  KD_RING_LDS_N(TM, TN, kLogitRB, kLogitBuf);
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  int tt, sp;
+  block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_splits, tt, sp);
+  const int vt0 = a.vt_offset + sp * a.tiles_per_split;
+  const int vt1 = min(vt0 + a.tiles_per_split, a.vt_offset + a.n_vtiles);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave % WM, wn = wave / WM;
+  const int64_t tok0 = (int64_t)tt * TN + wn * (TN / WN);
+  float Ls2[NB], L12[NB], A[NB], C[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int64_t n = tok0 + nb * 32 + (lane & 31);
+    Ls2[nb] = L12[nb] = A[nb] = C[nb] = 0.f;
+    if (n < a.N) {
+      Ls2[nb] = a.lse_s[n] * kLog2e;
+      L12[nb] = a.lse_s1 ? a.lse_s1[n] * kLog2e : 0.f;
+      const float wb = a.gb ? a.gb[n] : 0.f;
+      A[nb] = -wb * topk_binary_slope(a, n) * a.q_mass[n] * a.inv_tau;
+      C[nb] = a.lse_s1 ? topk_ce_weight(a, n) : 0.f;
+    }
+  }
+  auto epi = [&](int vt, auto& zs, auto&) {
+    const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int64_t n = tok0 + nb * 32 + (lane & 31);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          float g4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = rg * 4 + e;
+            const int64_t v = vrow0 + mb * 32 + acc_row(r, lane);
+            const float zb = __builtin_bit_cast(float, f32_to_bf16_bits(zs[mb][nb][r]) << 16);
+            const float q = fast_exp2(fmaf(zb, a.c2, -Ls2[nb]));
+            const float rr = fast_exp2(fmaf(zb, kLog2e, -L12[nb]));
+            g4[e] = (v < a.V) ? fmaf(A[nb], q, C[nb] * rr) : 0.f;
+          }
+          if (n < a.N) {
+            const int64_t col = vrow0 + mb * 32 + 8 * rg + 4 * (lane >> 5) - a.g_col0;
+            u32x2 w;
+            w.x = f32_to_bf16_bits(g4[0]) | (f32_to_bf16_bits(g4[1]) << 16);
+            w.y = f32_to_bf16_bits(g4[2]) | (f32_to_bf16_bits(g4[3]) << 16);
+            *reinterpret_cast<u32x2*>(a.G + n * a.ldg + col * 2) = w;
+          }
+        }
+    }
+  };
+  sweep<true, TM, TN, WM, WN, kLogitBuf, kLogitRB, false>(a.ps, a.ps, (int64_t)tt * TN, vt0, vt1, lds, epi);
+}
+
+// Sparse part, one wave per token: dh_s[n] = sum_j c_j W_s[idx_j] - w_ce W_s[y]
+// (overwrites dh_s; the dense chunks accumulate onto it).
+__global__ __launch_bounds__(256) void topk_sparse_kernel(TopkBwdArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * 4 + wave;
+  if (n >= a.N) return;  // whole waves only
+  const int K = a.k;
+  const bool act = lane < K;
+  const int32_t v = act ? a.idx[n * K + lane] : -1;
+  const bool ok = act && v >= 0 && v < a.V;
+  // renormalised teacher on the set, from its bf16 values
+  const float t = ok ? a.val_t[n * K + lane] * a.inv_tau : -INFINITY;
+  float mt = t;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
+  float et = ok ? expf(t - mt) : 0.f, st = et;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) st += __shfl_xor(st, o);
+  const float ph = et / st;
+  const float Q = a.q_mass[n];
+  const float q = ok ? expf(a.val_s[n * K + lane] * a.inv_tau - a.lse_s[n]) : 0.f;
+  const float wb = a.gb ? a.gb[n] : 0.f, wc = a.gc ? a.gc[n] : 0.f;
+  const float cj = ok ? (wb * topk_binary_slope(a, n) * q + wc * (q / Q - ph)) * a.inv_tau : 0.f;
+  const float wce = topk_ce_weight(a, n);
+  const int32_t y = wce != 0.f ? a.labels[n] : -1;
+  const uint16_t* W = static_cast<const uint16_t*>(static_cast<const void*>(a.ps.A));
+  // every lane runs every iteration (the shuffles need the whole wave); only
+  // the memory accesses are guarded
+  for (int base = 0; base < a.d_s; base += 64 * 8) {
+    const int d0 = base + lane * 8;
+    const bool in = d0 < a.d_s;  // d_s is a multiple of 8: then all 8 columns exist
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int j = 0; j < K; ++j) {
+      const int32_t vj = __shfl(v, j);
+      const float c = __shfl(cj, j);
+      if (vj < 0 || vj >= a.V || c == 0.f || !in) continue;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(W + (int64_t)vj * a.d_s + d0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = w[e];
+        acc[2 * e] = fmaf(c, __builtin_bit_cast(float, x << 16), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(c, __builtin_bit_cast(float, x & 0xFFFF0000u), acc[2 * e + 1]);
+      }
+    }
+    if (!in) continue;
+    if (y >= 0) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(W + (int64_t)y * a.d_s + d0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = w[e];
+        acc[2 * e] = fmaf(-wce, __builtin_bit_cast(float, x << 16), acc[2 * e]);
+        acc[2 * e + 1] = fmaf(-wce, __builtin_bit_cast(float, x & 0xFFFF0000u), acc[2 * e + 1]);
+      }
+    }
+    float* o = a.dh + n * a.d_s + d0;
+    *reinterpret_cast<floatx4*>(o) = floatx4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<floatx4*>(o + 4) = floatx4{acc[4], acc[5], acc[6], acc[7]};
+  }
+}
+
 template <bool kBf16>
 hipError_t launch_fwd_mode(int mode, dim3 grid, const LogitArgs& la, hipStream_t st) {
   switch (mode) {
@@ -674,6 +831,67 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
       dw.first = 1;
       if ((e = gemm(dw, dw.n_tok_tiles)) != hipSuccess) return e;
     }
+  }
+  return hipSuccess;
+}
+
+hipError_t run_topk_bwd(const Plan& p, const TopkBwdIO& io, hipStream_t st) {
+  char* G = static_cast<char*>(io.workspace);
+  char* WsT = G + align_up((size_t)p.N * io.chunk_V * 2, 256);
+  TopkBwdArgs a{};
+  a.ps = PairDesc{static_cast<const char*>(io.W_s), static_cast<const char*>(io.h_s), (int64_t)p.d_s * 2,
+                  (int64_t)p.d_s * 2, p.V, p.N, (int32_t)(p.d_s * 2)};
+  a.N = p.N;
+  a.V = p.V;
+  a.k = io.k;
+  a.c2 = kLog2e / io.tau;
+  a.inv_tau = 1.f / io.tau;
+  a.labels = io.labels;
+  a.idx = io.idx;
+  a.val_t = io.val_t;
+  a.val_s = io.val_s;
+  a.p_mass = io.p_mass;
+  a.q_mass = io.q_mass;
+  a.lse_s = io.lse_s;
+  a.lse_s1 = io.lse_s1;
+  a.gb = io.grad_binary;
+  a.gc = io.grad_cond;
+  a.ge = io.grad_ce;
+  a.n_tok_tiles = p.n_tok_tiles;
+  a.tiles_per_split = 1;
+  a.G = G;
+  a.ldg = (int64_t)io.chunk_V * 2;
+  a.dh = io.dh;
+  a.d_s = p.d_s;
+  hipLaunchKernelGGL(topk_sparse_kernel, dim3((unsigned)((p.N + 3) / 4)), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n_d_tiles = (p.d_s + kTileDhD - 1) / kTileDhD;
+  const int n_tok_tiles_dh = (int)((p.N + kTileDhT - 1) / kTileDhT);
+  for (int64_t c0 = 0; c0 < p.V; c0 += io.chunk_V) {
+    const int64_t ccols = (p.V - c0 < io.chunk_V) ? p.V - c0 : io.chunk_V;
+    const int ctiles = (int)((ccols + kTileV - 1) / kTileV);
+    const int64_t kcols = (int64_t)ctiles * kTileV;
+    a.vt_offset = (int)(c0 / kTileV);
+    a.n_vtiles = ctiles;
+    a.n_splits = ctiles;
+    a.g_col0 = c0;
+    hipLaunchKernelGGL(topk_bwdg_kernel, dim3(p.n_tok_tiles * ctiles), dim3(kLogitThreads), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const dim3 tgrid((unsigned)(kcols / 64), (unsigned)((p.d_s + 63) / 64));
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, tgrid, dim3(256), 0, st, static_cast<const uint16_t*>(io.W_s),
+                       reinterpret_cast<uint16_t*>(WsT), p.V, p.d_s, c0, (int64_t)io.chunk_V);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    DhArgs da{};
+    da.p = PairDesc{G, WsT, (int64_t)io.chunk_V * 2, (int64_t)io.chunk_V * 2, p.N, p.d_s, (int32_t)(kcols * 2)};
+    da.N = p.N;
+    da.d_s = p.d_s;
+    da.n_tok_tiles = n_tok_tiles_dh;
+    da.n_d_tiles = n_d_tiles;
+    da.dh = io.dh;
+    da.first = 0;  // onto the sparse part
+    hipLaunchKernelGGL(dh_kernel<true>, dim3(n_tok_tiles_dh * n_d_tiles), dim3(kDhThreads), 0, st, da);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }

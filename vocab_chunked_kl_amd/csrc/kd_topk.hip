@@ -297,7 +297,7 @@ struct MergeArgs {
   const uint32_t* lists;
   const int32_t* labels;
   int32_t* idx;
-  float *val_t, *val_s, *binary, *cond, *ce, *p_mass, *q_mass, *lse_s, *lse_t;
+  float *val_t, *val_s, *binary, *cond, *ce, *p_mass, *q_mass, *lse_s, *lse_t, *lse_s1;
   int sep1;
 };
 
@@ -426,6 +426,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
     a.q_mass[n] = all ? 1.f : Q;
     a.lse_s[n] = Ls;
     a.lse_t[n] = Lt;
+    if (a.lse_s1) a.lse_s1[n] = L1;
   }
   if (a.labels) {
     const int32_t y = a.labels[n];
@@ -466,7 +467,7 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   a.part = static_cast<float*>(io.workspace);
   a.lists = reinterpret_cast<uint32_t*>(static_cast<char*>(io.workspace) +
                                         align_up((size_t)kTopkFields * a.n_splits * p.N * sizeof(float), 256));
-  const bool sep1 = io.labels != nullptr && io.tau != 1.f;
+  const bool sep1 = (io.labels != nullptr || io.lse_s1 != nullptr) && io.tau != 1.f;
   const dim3 grid(a.n_tok_tiles * a.n_splits);
   if (sep1)
     hipLaunchKernelGGL(topk_sweep_kernel<true>, grid, dim3(kTopkThreads), 0, st, a);
@@ -490,6 +491,7 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   m.idx = io.idx;
   m.val_t = io.val;
   m.val_s = io.val_s;
+  m.lse_s1 = io.lse_s1;
   m.binary = io.binary;
   m.cond = io.cond;
   m.ce = io.ce;
