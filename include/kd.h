@@ -203,6 +203,28 @@ kd_status kd_topk_bwd(const void* h_s, const void* W_s, int64_t N, int64_t V, in
                       const float* lse_s1, const float* grad_binary, const float* grad_cond, const float* grad_ce,
                       int32_t chunk_V, float* dh_s, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * kd_gather_rows / kd_scatter_rows - row gather and scatter for token masking.
+ *   Source: lpnh.cn "Top-K知识蒸馏损失实现详解", section 二.4 (gather the hidden
+ *   states at the positions that carry a loss before the unembedding, so the
+ *   masked positions cost nothing). Gather the hidden states of the tokens
+ *   whose label is not ignored, call kd_fwd / kd_bwd on the gathered rows,
+ *   and scatter dL/dh_s back; the work is proportional to the kept tokens.
+ *   kd_gather_rows:  dst[i, :] = src[rows[i], :] for i < n_rows; an index
+ *                    outside [0, n_src) gives a row of zeros.
+ *   kd_scatter_rows: dst[rows[i], :] = src[i, :] for i < n_rows; indices outside
+ *                    [0, n_dst) are skipped; other rows of dst are untouched;
+ *                    duplicate indices leave one of their rows (unspecified).
+ *   src, dst, rows (device): row-major arrays of row_bytes bytes per row
+ *   (a positive multiple of 4), 4-byte aligned (16-byte alignment and rows of
+ *   16-byte multiples take the wide path); rows is int32 [n_rows]. n_rows = 0
+ *   is a no-op.
+ */
+kd_status kd_gather_rows(const void* src, int64_t n_src, int64_t row_bytes, const int32_t* rows, int64_t n_rows,
+                         void* dst, void* stream);
+kd_status kd_scatter_rows(const void* src, int64_t n_rows, int64_t row_bytes, const int32_t* rows, void* dst,
+                          int64_t n_dst, void* stream);
+
 /* kd_status_string - a static, human-readable name for a status code. */
 const char* kd_status_string(kd_status s);
 

@@ -38,7 +38,9 @@ def close(gpu, ref, rtol=RTOL, atol=ATOL):
     err = np.abs(gpu - ref)
     lim = rtol * np.abs(ref) + atol
     bad = ~(err <= lim)
-    return (not bad.any()), float(np.max(err / lim)) if err.size else 0.0, np.nonzero(bad)[0][:8]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        worst = float(np.max(err / lim)) if err.size else 0.0
+    return (not bad.any()), worst, np.nonzero(bad)[0][:8]
 
 
 def assert_close(name, gpu, ref, rtol=RTOL, atol=ATOL):

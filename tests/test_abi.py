@@ -142,3 +142,16 @@ def test_topk_bwd_validation():
     need = kd.workspace_size(kd.KD_OP_TOPK_BWD, 8, 100, 64, 64, kd.KD_BF16, chunk_V=256)
     assert need == kd.workspace_size(kd.KD_OP_BWD, 8, 100, 64, 64, kd.KD_BF16, chunk_V=256)
     assert call(ws_bytes=need - 1) == 3
+
+
+def test_gather_scatter_validation():
+    import vocab_chunked_kl_amd as kd
+    lib = kd.load_library()
+    # n_rows = 0 is a no-op even with null pointers; bad sizes / pointers fail before any launch
+    assert lib.kd_gather_rows(None, 10, 64, None, 0, None, None) == 0
+    assert lib.kd_scatter_rows(None, 0, 64, None, None, 10, None) == 0
+    assert lib.kd_gather_rows(FAKE, 10, 64, None, 4, FAKE, None) == 1
+    assert lib.kd_gather_rows(FAKE, 10, 62, FAKE, 4, FAKE, None) == 1
+    assert lib.kd_gather_rows(FAKE, -1, 64, FAKE, 4, FAKE, None) == 1
+    assert lib.kd_scatter_rows(FAKE, 4, 0, FAKE, FAKE, 10, None) == 1
+    assert lib.kd_scatter_rows(FAKE + 2, 4, 64, FAKE, FAKE, 10, None) == 2

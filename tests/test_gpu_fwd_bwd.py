@@ -235,3 +235,73 @@ def test_weight_gradient_identities_v152k_n32k(beta):
     w = workload(3)
     _say(f"dW identities {w.name} N={w.N} V={w.V} beta={beta}")
     _identity_check(kd, torch, w, beta, 16384)
+
+
+# --------------------------------------------------------------------------- token masking
+def test_gather_scatter_rows_exact():
+    kd, torch = _kd()
+    g = np.random.default_rng(41)
+    N, d = 300, 200  # bf16 rows of 400 bytes: the 16-byte path
+    x = torch.from_numpy(g.integers(0, 1 << 16, size=(N, d), dtype=np.uint16).view(np.int16)).cuda()
+    rows_np = np.array([5, 0, 299, 17, 300, -1, 150], dtype=np.int32)  # two indices out of range
+    rows = torch.from_numpy(rows_np).cuda()
+    y = kd.kd_gather_rows(x, rows)
+    want = np.zeros((len(rows_np), d), dtype=np.int16)
+    ok = (rows_np >= 0) & (rows_np < N)
+    want[ok] = x.cpu().numpy()[rows_np[ok]]
+    assert np.array_equal(y.cpu().numpy(), want)
+    z = kd.kd_scatter_rows(y, rows, N)
+    back = np.zeros((N, d), dtype=np.int16)
+    back[rows_np[ok]] = want[ok]
+    assert np.array_equal(z.cpu().numpy(), back)
+    # 4-byte path (fp32 rows of one value)
+    v = torch.arange(7, dtype=torch.float32, device="cuda").reshape(7, 1)
+    w = kd.kd_scatter_rows(v, rows, N)
+    exp = np.zeros((N, 1), dtype=np.float32)
+    exp[rows_np[ok], 0] = np.arange(7, dtype=np.float32)[ok]
+    assert np.array_equal(w.cpu().numpy(), exp)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, 1.0])
+def test_masked_tokens_are_skipped_not_changed(beta):
+    kd, torch = _kd()
+    N, V, ds, dt = 300, 1000, 64, 200
+    arrays = kdsynth.small_case(11, N, V, ds, dt)
+    labels = kdsynth.uniform_labels(9, N, V, ignore_frac=0.4)
+    valid = labels != -100
+    _say(f"masked N={N} kept={int(valid.sum())} beta={beta}")
+    dev = [to_dev(x) for x in arrays]
+    lab = torch.from_numpy(labels.astype(np.int64)).cuda()
+    # full computation of every row, as the reference for the kept rows
+    loss, lse_s, lse_t, aux = kd.kd_fwd(*dev, beta, 1.5)
+    gl = torch.from_numpy((valid / valid.sum()).astype(np.float32)).cuda()
+    dh_full = kd.kd_bwd(*dev, beta, 1.5, lse_s, lse_t, aux, grad_loss=gl, chunk_V=512)
+    # the loss on the kept rows only
+    xs = dev[0].clone().requires_grad_(True)
+    per_tok = kd.jsd(xs, dev[2], dev[1], dev[3], beta=beta, temperature=1.5, reduction="none", chunk_V=512,
+                     labels=lab)
+    mean = kd.jsd(xs, dev[2], dev[1], dev[3], beta=beta, temperature=1.5, reduction="mean", chunk_V=512, labels=lab)
+    mean.backward()
+    torch.cuda.synchronize()
+    pt = per_tok.detach().cpu().numpy()
+    assert np.array_equal(pt[valid], loss.cpu().numpy()[valid])  # same arithmetic per kept row
+    assert np.all(pt[~valid] == 0.0)
+    m = float(mean.detach())
+    assert abs(m - float(loss.cpu().numpy()[valid].mean())) <= 1e-6 * (1 + abs(m))
+    gx = xs.grad.float().cpu().numpy()
+    assert np.all(gx[~valid] == 0.0)
+    assert np.allclose(gx[valid], dh_full.to(torch.bfloat16).float().cpu().numpy()[valid], rtol=1e-6, atol=0)
+
+
+def test_all_tokens_masked():
+    kd, torch = _kd()
+    arrays = kdsynth.small_case(12, 64, 500, 32, 32)
+    dev = [to_dev(x) for x in arrays]
+    lab = torch.full((64,), -100, dtype=torch.int64, device="cuda")
+    xs = dev[0].clone().requires_grad_(True)
+    m = kd.reverse_kl(xs, dev[2], dev[1], dev[3], labels=lab)
+    m.backward()
+    assert float(m) == 0.0 and float(xs.grad.float().abs().sum()) == 0.0
+    n = kd.reverse_kl(dev[0], dev[2], dev[1], dev[3], labels=lab, reduction="none")
+    assert n.shape == (64,) and float(n.abs().sum()) == 0.0

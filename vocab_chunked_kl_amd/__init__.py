@@ -27,6 +27,7 @@ import torch
 
 __all__ = [
     "KDError", "load_library", "workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd",
+    "kd_gather_rows", "kd_scatter_rows",
     "forward_kl", "reverse_kl", "jsd", "topk_kd", "KD_TOPK_MAX",
 ]
 
@@ -37,8 +38,8 @@ KD_F32, KD_BF16 = 0, 1
 KD_OP_FWD, KD_OP_BWD, KD_OP_TOPK, KD_OP_BWD_W, KD_OP_TOPK_BWD = 0, 1, 2, 3, 4
 KD_TOPK_MAX = 64
 KD_TOPK_MAX_V = 524288
-EXPORTED = ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_status_string",
-            "kd_last_error")
+EXPORTED = ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_gather_rows",
+            "kd_scatter_rows", "kd_status_string", "kd_last_error")
 
 
 class KDError(RuntimeError):
@@ -69,7 +70,10 @@ def load_library(path: str = LIB_PATH):
                                 vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_topk_bwd.argtypes = [vp, vp, i64, i64, i32, i32, f32, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, i32, vp, vp, sz, vp]
-    for fn in ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd"):
+    lib.kd_gather_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
+    lib.kd_scatter_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp]
+    for fn in ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_gather_rows",
+               "kd_scatter_rows"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
@@ -230,6 +234,37 @@ def kd_topk_bwd(h_s, W_s, fwd: dict, k: int, tau: float, labels=None, grad_binar
     return dh
 
 
+def _check_rows(rows):
+    if rows.dtype != torch.int32 or rows.dim() != 1 or not rows.is_contiguous() or not rows.is_cuda:
+        raise ValueError("rows must be a contiguous 1-D int32 GPU tensor")
+
+
+def kd_gather_rows(src, rows, stream=None):
+    """dst[i] = src[rows[i]] for a contiguous 2-D ``src`` (zeros for indices
+    outside [0, len(src)))."""
+    lib = load_library()
+    _check_rows(rows)
+    if src.dim() != 2 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous 2-D tensor")
+    dst = torch.empty(rows.numel(), src.shape[1], dtype=src.dtype, device=src.device)
+    _check(lib.kd_gather_rows(_ptr(src), src.shape[0], src.shape[1] * src.element_size(), _ptr(rows), rows.numel(),
+                              _ptr(dst), _stream(stream)))
+    return dst
+
+
+def kd_scatter_rows(src, rows, n_dst: int, dst=None, stream=None):
+    """dst[rows[i]] = src[i]; ``dst`` (default: zeros of n_dst rows) keeps its other rows."""
+    lib = load_library()
+    _check_rows(rows)
+    if src.dim() != 2 or not src.is_contiguous():
+        raise ValueError("src must be a contiguous 2-D tensor")
+    if dst is None:
+        dst = torch.zeros(n_dst, src.shape[1], dtype=src.dtype, device=src.device)
+    _check(lib.kd_scatter_rows(_ptr(src), rows.numel(), src.shape[1] * src.element_size(), _ptr(rows), _ptr(dst),
+                               n_dst, _stream(stream)))
+    return dst
+
+
 # ---------------------------------------------------------------------------
 # autograd losses
 # ---------------------------------------------------------------------------
@@ -259,18 +294,56 @@ class _KD(torch.autograd.Function):
                 None, None, None, None, None)
 
 
+class _Rows(torch.autograd.Function):
+    """Row gather (forward) / scatter (backward) of the tokens that carry a loss."""
+
+    @staticmethod
+    def forward(ctx, x, rows):
+        ctx.save_for_backward(rows)
+        ctx.n = x.shape[0]
+        return kd_gather_rows(x, rows)
+
+    @staticmethod
+    def backward(ctx, g):
+        (rows,) = ctx.saved_tensors
+        return kd_scatter_rows(g.contiguous(), rows, ctx.n), None
+
+
+class _Unrows(torch.autograd.Function):
+    """Row scatter into zeros (forward) / gather (backward)."""
+
+    @staticmethod
+    def forward(ctx, x, rows, n):
+        ctx.save_for_backward(rows)
+        return kd_scatter_rows(x, rows, n)
+
+    @staticmethod
+    def backward(ctx, g):
+        (rows,) = ctx.saved_tensors
+        return kd_gather_rows(g.contiguous(), rows), None, None
+
+
 def _divergence(xs, xt, ws, wt, beta, temperature, reduction, chunk_V, labels, ignore_index):
     d_s, d_t = xs.shape[-1], xt.shape[-1]
     lead = xs.shape[:-1]
     xs2 = xs.reshape(-1, d_s).contiguous()
     xt2 = xt.reshape(-1, d_t).contiguous()
-    per_tok = _KD.apply(xs2, ws.contiguous(), xt2, wt.contiguous(), float(beta), float(temperature), int(chunk_V))
+    rows = None
     if labels is not None:
-        valid = (labels.reshape(-1) != ignore_index).to(per_tok.dtype)
-        per_tok = per_tok * valid
-        count = valid.sum()
-    else:
-        count = torch.tensor(float(per_tok.numel()), device=per_tok.device)
+        valid = labels.reshape(-1) != ignore_index
+        if not bool(valid.all()):
+            # only the tokens that carry a loss are computed ([Top-K KD] 二.4)
+            rows = torch.nonzero(valid).reshape(-1).to(torch.int32)
+            if rows.numel() == 0:  # nothing carries a loss: zero, still attached to the inputs
+                zero = (xs2.sum() + xt2.sum() + ws.sum() + wt.sum()).float() * 0.0
+                if reduction == "none":
+                    return (torch.zeros(xs2.shape[0], device=xs.device) + zero).reshape(lead)
+                return zero
+            xs2, xt2 = _Rows.apply(xs2, rows), _Rows.apply(xt2, rows)
+    per_tok = _KD.apply(xs2, ws.contiguous(), xt2, wt.contiguous(), float(beta), float(temperature), int(chunk_V))
+    count = torch.tensor(float(per_tok.numel()), device=per_tok.device)
+    if rows is not None and reduction == "none":  # back to one value per position, 0 where ignored
+        per_tok = _Unrows.apply(per_tok.reshape(-1, 1).contiguous(), rows, labels.numel()).reshape(-1)
     if reduction == "none":
         return per_tok.reshape(lead)
     if reduction == "sum":

@@ -201,4 +201,28 @@ kd_status kd_topk_bwd(const void* h_s, const void* W_s, int64_t N, int64_t V, in
   return e == hipSuccess ? KD_OK : hip_fail(e, "kd_topk_bwd launch");
 }
 
+kd_status kd_gather_rows(const void* src, int64_t n_src, int64_t row_bytes, const int32_t* rows, int64_t n_rows,
+                         void* dst, void* stream) {
+  g_last_error[0] = 0;
+  if (n_rows < 0 || n_src < 0) return fail(KD_ERR_INVALID_ARG, "negative row count");
+  if (n_rows == 0) return KD_OK;
+  if (!src || !rows || !dst) return fail(KD_ERR_INVALID_ARG, "null pointer (src, rows, dst)");
+  if (row_bytes <= 0 || row_bytes % 4) return fail(KD_ERR_INVALID_ARG, "row_bytes must be a positive multiple of 4");
+  if (!aligned4(src) || !aligned4(dst) || !aligned4(rows)) return fail(KD_ERR_UNSUPPORTED, "pointers must be 4-byte aligned");
+  hipError_t e = kd::run_copy_rows(src, dst, rows, n_rows, n_src, row_bytes, false, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KD_OK : hip_fail(e, "kd_gather_rows launch");
+}
+
+kd_status kd_scatter_rows(const void* src, int64_t n_rows, int64_t row_bytes, const int32_t* rows, void* dst,
+                          int64_t n_dst, void* stream) {
+  g_last_error[0] = 0;
+  if (n_rows < 0 || n_dst < 0) return fail(KD_ERR_INVALID_ARG, "negative row count");
+  if (n_rows == 0) return KD_OK;
+  if (!src || !rows || !dst) return fail(KD_ERR_INVALID_ARG, "null pointer (src, rows, dst)");
+  if (row_bytes <= 0 || row_bytes % 4) return fail(KD_ERR_INVALID_ARG, "row_bytes must be a positive multiple of 4");
+  if (!aligned4(src) || !aligned4(dst) || !aligned4(rows)) return fail(KD_ERR_UNSUPPORTED, "pointers must be 4-byte aligned");
+  hipError_t e = kd::run_copy_rows(src, dst, rows, n_rows, n_dst, row_bytes, true, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KD_OK : hip_fail(e, "kd_scatter_rows launch");
+}
+
 }  // extern "C"

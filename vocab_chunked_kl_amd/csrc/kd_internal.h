@@ -107,6 +107,11 @@ struct TopkBwdIO {
   void* workspace;
 };
 hipError_t run_topk_bwd(const Plan& p, const TopkBwdIO& io, hipStream_t stream);
+
+// dst[i] = src[rows[i]] (gather) or dst[rows[i]] = src[i] (scatter), rows of
+// row_bytes bytes; n_other = rows of the indexed array.
+hipError_t run_copy_rows(const void* src, void* dst, const int32_t* rows, int64_t n_rows, int64_t n_other,
+                         int64_t row_bytes, bool scatter, hipStream_t stream);
 hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t stream);
 
 }  // namespace kd

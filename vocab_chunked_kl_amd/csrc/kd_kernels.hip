@@ -636,6 +636,37 @@ __global__ __launch_bounds__(256) void topk_sparse_kernel(TopkBwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Row gather / scatter ([Top-K KD] 二.4: gather the hidden states of the
+// positions that carry a loss before the unembedding). One workgroup per row,
+// 16-byte words when rows and pointers allow, else 4-byte words. An index
+// outside [0, n_other) gathers a row of zeros / is skipped by the scatter.
+// ---------------------------------------------------------------------------
+template <typename W>
+__global__ __launch_bounds__(256) void copy_rows_kernel(const char* __restrict__ src, char* __restrict__ dst,
+                                                        const int32_t* __restrict__ rows, int64_t n_rows,
+                                                        int64_t n_other, int64_t row_bytes, int scatter) {
+  const int64_t words = row_bytes / (int64_t)sizeof(W);
+  for (int64_t i = blockIdx.x; i < n_rows; i += gridDim.x) {
+    const int64_t r = rows[i];
+    const bool ok = r >= 0 && r < n_other;
+    if (scatter) {
+      if (!ok) continue;
+      const W* s = reinterpret_cast<const W*>(src + i * row_bytes);
+      W* d = reinterpret_cast<W*>(dst + r * row_bytes);
+      for (int64_t w = threadIdx.x; w < words; w += blockDim.x) d[w] = s[w];
+    } else {
+      W* d = reinterpret_cast<W*>(dst + i * row_bytes);
+      if (!ok) {
+        for (int64_t w = threadIdx.x; w < words; w += blockDim.x) d[w] = W{};
+        continue;
+      }
+      const W* s = reinterpret_cast<const W*>(src + r * row_bytes);
+      for (int64_t w = threadIdx.x; w < words; w += blockDim.x) d[w] = s[w];
+    }
+  }
+}
+
 template <bool kBf16>
 hipError_t launch_fwd_mode(int mode, dim3 grid, const LogitArgs& la, hipStream_t st) {
   switch (mode) {
@@ -894,6 +925,20 @@ hipError_t run_topk_bwd(const Plan& p, const TopkBwdIO& io, hipStream_t st) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t run_copy_rows(const void* src, void* dst, const int32_t* rows, int64_t n_rows, int64_t n_other,
+                         int64_t row_bytes, bool scatter, hipStream_t st) {
+  if (n_rows == 0) return hipSuccess;
+  const unsigned grid = (unsigned)(n_rows < 65536 ? n_rows : 65536);
+  const bool wide = (row_bytes % 16 == 0) && ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) == 0;
+  if (wide)
+    hipLaunchKernelGGL(copy_rows_kernel<u32x4>, dim3(grid), dim3(256), 0, st, static_cast<const char*>(src),
+                       static_cast<char*>(dst), rows, n_rows, n_other, row_bytes, scatter ? 1 : 0);
+  else
+    hipLaunchKernelGGL(copy_rows_kernel<uint32_t>, dim3(grid), dim3(256), 0, st, static_cast<const char*>(src),
+                       static_cast<char*>(dst), rows, n_rows, n_other, row_bytes, scatter ? 1 : 0);
+  return hipGetLastError();
 }
 
 }  // namespace kd
