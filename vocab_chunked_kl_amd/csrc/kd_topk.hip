@@ -119,28 +119,44 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
   }
 
   // merge token t's candidate buffer into its state (one wave)
+  // merge token t's candidate buffer into its state (one wave): the <= 96
+  // words (S then B, zero-padded to 128, two per lane: element i = lane + 64 h)
+  // are sorted descending by a bitonic network in registers (words are
+  // distinct and nonzero, so the zeros sink), and the first min(total, k)
+  // become the new state
   auto merge_token = [&](int t) {
     const int cs = cntS[t];
     const int cb = min(cntB[t], kCandCap);
     const int total = cs + cb;
-    const uint32_t e0 = lane < cs ? S[t][lane] : (lane - cs < cb ? B[t][lane - cs] : 0u);
+    uint32_t e0 = lane < cs ? S[t][lane] : (lane - cs < cb ? B[t][lane - cs] : 0u);
     const int j1 = lane + 64;
-    const uint32_t e1 = j1 < cs ? S[t][j1] : (j1 - cs < cb && j1 >= cs ? B[t][j1 - cs] : 0u);
-    int r0 = 0, r1 = 0;
-    for (int i = 0; i < total; ++i) {
-      const uint32_t x = i < cs ? S[t][i] : B[t][i - cs];
-      r0 += x > e0;
-      r1 += x > e1;
+    uint32_t e1 = j1 < cs ? S[t][j1] : (j1 - cs < cb && j1 >= cs ? B[t][j1 - cs] : 0u);
+#pragma unroll
+    for (int k = 2; k <= 128; k <<= 1) {
+#pragma unroll
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        if (j == 64) {  // partner is the lane's other element; k = 128: descending
+          const uint32_t hi = max(e0, e1), lo = min(e0, e1);
+          e0 = hi;
+          e1 = lo;
+        } else {
+          const uint32_t p0 = __shfl_xor(e0, j), p1 = __shfl_xor(e1, j);
+          const bool lower = (lane & j) == 0;
+          const bool desc0 = (lane & k) == 0;
+          const bool desc1 = ((lane + 64) & k) == 0;
+          e0 = (lower == desc0) ? max(e0, p0) : min(e0, p0);
+          e1 = (lower == desc1) ? max(e1, p1) : min(e1, p1);
+        }
+      }
     }
-    if (lane < total && r0 < K) S[t][r0] = e0;
-    if (j1 < total && r1 < K) S[t][r1] = e1;
     const int ns = min(total, K);
+    if (lane < ns) S[t][lane] = e0;
+    const uint32_t th = __shfl(e0, K - 1);
     if (lane == 0) {
       cntS[t] = ns;
       cntB[t] = 0;
+      theta[t] = ns == K ? th : 0u;
     }
-    const uint32_t th = S[t][K - 1];
-    if (lane == 0) theta[t] = ns == K ? th : 0u;
   };
 
   auto epi = [&](int vt, auto& zs, auto& zt) {
