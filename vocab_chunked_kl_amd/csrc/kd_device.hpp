@@ -25,7 +25,6 @@ typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -80,9 +79,6 @@ __device__ __forceinline__ void block_coords(int L, int n_tok_tiles, int n_split
 // contiguous run of logical tiles so that blocks sharing operand rows meet in
 // that XCD's L2. Identity when the grid is not a multiple of 8.
 __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
-#ifdef KD_NO_XCD_REMAP
-  return b;
-#endif
   if (nblocks & 7) return b;
   return (b & 7) * (nblocks >> 3) + (b >> 3);
 }
