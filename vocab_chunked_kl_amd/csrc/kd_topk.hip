@@ -30,7 +30,7 @@ namespace {
 
 constexpr float kNegInf = -INFINITY;
 constexpr int kTopkSplit = 65536;  // vocabulary entries per split: the in-split index fits 16 bits
-constexpr int kCandCap = 32;       // candidate buffer entries per token per round
+constexpr int kCandCap = 16;       // candidate buffer entries per token per round
 constexpr int kTopkFields = 6;     // m_s, l_s, m_t, l_t, m_1, l_1 (untempered student)
 
 struct TopkArgs {
@@ -71,10 +71,11 @@ __device__ __forceinline__ void merge2(float& m, float& l, float m2, float l2) {
   m = mm;
 }
 
-#define KD_RING2_LDS(TM, TN)                                                  \
+#define KD_RING3_LDS(TM, TN)                                                  \
   __shared__ __attribute__((aligned(16))) char ring0_[Ring<TM, TN>::kBytes]; \
   __shared__ __attribute__((aligned(16))) char ring1_[Ring<TM, TN>::kBytes]; \
-  const RingLds<2> lds{{ring0_, ring1_}}
+  __shared__ __attribute__((aligned(16))) char ring2_[Ring<TM, TN>::kBytes]; \
+  const RingLds<3> lds{{ring0_, ring1_, ring2_}}
 
 // Wave grid of the top-k sweep: 4 vocabulary slices x 2 token halves.
 constexpr int kTopkWM = 4, kTopkWN = 2, kTopkThreads = 64 * kTopkWM * kTopkWN;
@@ -87,12 +88,14 @@ template <bool kSep1>
 __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a) {
   constexpr int TM = kTileV, TN = kTopkT, WM = kTopkWM, WN = kTopkWN, NW = WM * WN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
-  KD_RING2_LDS(TM, TN);
-  __shared__ uint32_t S[TN][KD_TOPK_MAX];  // running top-k words, descending
+  // LDS: a three-stage ring, the candidate buffers and per-token counters.
+  // The running top-k lists live in the per-split output rows of the
+  // workspace (each token's row is read and written only by the wave that
+  // merges it), which leaves LDS room for the third ring stage.
+  KD_RING3_LDS(TM, TN);
   __shared__ uint32_t B[TN][kCandCap];     // candidate buffer
   __shared__ int cntS[TN], cntB[TN];
   __shared__ uint32_t theta[TN];           // k-th word once full, else 0
-  __shared__ float red[(WM - 1) * kTopkFields * TN];
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
@@ -118,8 +121,7 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
     ls[nb] = lt[nb] = l1[nb] = 0.f;
   }
 
-  // merge token t's candidate buffer into its state (one wave)
-  // merge token t's candidate buffer into its state (one wave): the <= 96
+  // merge token t's candidate buffer into its state (one wave): the <= 80
   // words (S then B, zero-padded to 128, two per lane: element i = lane + 64 h)
   // are sorted descending by a bitonic network in registers (words are
   // distinct and nonzero, so the zeros sink), and the first min(total, k)
@@ -128,9 +130,10 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
     const int cs = cntS[t];
     const int cb = min(cntB[t], kCandCap);
     const int total = cs + cb;
-    uint32_t e0 = lane < cs ? S[t][lane] : (lane - cs < cb ? B[t][lane - cs] : 0u);
+    uint32_t* Sg = a.lists + ((int64_t)sp * a.N + (int64_t)tt * TN + t) * K;  // token < N (see below)
+    uint32_t e0 = lane < cs ? Sg[lane] : (lane - cs < cb ? B[t][lane - cs] : 0u);
     const int j1 = lane + 64;
-    uint32_t e1 = j1 < cs ? S[t][j1] : (j1 - cs < cb && j1 >= cs ? B[t][j1 - cs] : 0u);
+    uint32_t e1 = j1 - cs < cb ? B[t][j1 - cs] : 0u;  // cs <= 64 <= j1
 #pragma unroll
     for (int k = 2; k <= 128; k <<= 1) {
 #pragma unroll
@@ -150,7 +153,7 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
       }
     }
     const int ns = min(total, K);
-    if (lane < ns) S[t][lane] = e0;
+    if (lane < K) Sg[lane] = lane < ns ? e0 : 0u;  // the row stays fully defined
     const uint32_t th = __shfl(e0, K - 1);
     if (lane == 0) {
       cntS[t] = ns;
@@ -220,6 +223,7 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
       for (int nb = 0; nb < NB; ++nb) {
         const int col = wn * (TN / WN) + nb * 32 + (lane & 31);
         const uint32_t th = theta[col];
+        const bool tok_ok = (int64_t)tt * TN + col < a.N;  // tokens past N have no list row
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
             const int rel = rel0 + mb * 32 + acc_row(r, lane);
             const bool ok = full || (vbase + rel < a.V);
             const uint32_t w = (bf16_key(zt[mb][nb][r]) << 16) | (0xFFFFu - (uint32_t)rel);
-            if (ok && w > th && !((done[nb][bit >> 5] >> (bit & 31)) & 1u)) {
+            if (ok && tok_ok && w > th && !((done[nb][bit >> 5] >> (bit & 31)) & 1u)) {
               const int slot = atomicAdd(&cntB[col], 1);
               if (slot < kCandCap) {
                 B[col][slot] = w;
@@ -246,7 +250,10 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
       if (!any) break;
     }
   };
-  sweep<true, TM, TN, WM, WN, 2, 128, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<true, TM, TN, WM, WN, 3, 128, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  // the ring is drained: its first buffer holds the cross-wave LSE records
+  float* red = reinterpret_cast<float*>(lds.b[0]);
+  static_assert((WM - 1) * kTopkFields * TN * sizeof(float) <= Ring<TM, TN>::kBytes, "records fit one stage");
 
   // LSE partials: lanes l and l^32, then the WM vocabulary-slice waves
 #pragma unroll
@@ -292,11 +299,12 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
       }
     }
   }
-  // the top-k list of each token (padded with 0 words when the split is short)
+  // the lists are in place; a token that never received a candidate (only
+  // possible for a split with no valid entry) gets a row of empty words
   for (int i = tid; i < TN * K; i += kTopkThreads) {
     const int t = i / K, j = i - t * K;
     const int64_t n = (int64_t)tt * TN + t;
-    if (n < a.N) a.lists[((int64_t)sp * a.N + n) * K + j] = j < cntS[t] ? S[t][j] : 0u;
+    if (n < a.N && cntS[t] == 0) a.lists[((int64_t)sp * a.N + n) * K + j] = 0u;
   }
 }
 
