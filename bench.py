@@ -135,7 +135,7 @@ def main():
     N, V, ds, dt_, tau, beta = w.N, w.V, w.d_s, w.d_t, w.tau, args.beta
     dev = [to_dev(x) for x in (w.h_s, w.W_s, w.h_t, w.W_t)]
     stream = torch.cuda.Stream()
-    fws = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt_, kd.KD_BF16, beta=beta)
+    fws = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt_, kd.KD_BF16, beta=0.5)  # covers every beta
     bop = kd.KD_OP_BWD_W if args.with_dw else kd.KD_OP_BWD
     bws = kd.workspace_size(bop, N, V, ds, dt_, kd.KD_BF16, beta=beta, chunk_V=args.chunk_v)
     with torch.cuda.stream(stream):
@@ -183,6 +183,28 @@ def main():
     ms_step = total_ms / args.steps
     fwd_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     peak_extra = torch.cuda.max_memory_allocated() - base_mem
+
+    # the other points of the beta sweep of this workload, one warm step then two timed steps each
+    # (reported beside the headline step, which is the configured beta)
+    sweep_ms = {}
+    for b in (0.0, 0.5, 1.0):
+        bws_b = kd.workspace_size(bop, N, V, ds, dt_, kd.KD_BF16, beta=b, chunk_V=args.chunk_v)
+        fws_b = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt_, kd.KD_BF16, beta=b)
+        if bws_b > ws_b.numel() or fws_b > ws_f.numel():
+            continue
+        with torch.cuda.stream(stream):
+            def one():
+                l, a1, a2, a3 = kd.kd_fwd(*dev, b, tau, workspace=ws_f, stream=stream)
+                kd.kd_bwd(*dev, b, tau, a1, a2, a3, chunk_V=args.chunk_v, workspace=ws_b, stream=stream, dh=dh,
+                          dW=dW, want_dW=args.with_dw)
+            one()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            one()
+            one()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        sweep_ms[str(b)] = round(e0.elapsed_time(e1) / 2, 3)
     assert np.isfinite(loss.float().cpu().numpy()).all()
 
     fwd_flops = 2.0 * N * V * (ds + dt_)
@@ -223,6 +245,7 @@ def main():
         "bwd_ms": round(ms_step - fwd_ms, 3),
         "workspace_bytes": {"fwd": fws, "bwd": bws, "peak_alloc_delta": int(peak_extra)},
         "wall_s_timed": round(wall, 3),
+        "beta_sweep_ms_per_step": sweep_ms,
         "roofline": {"kernel": "fwd_kernel (forward sweep: both logit GEMMs + online LSE/KL)",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
