@@ -4,7 +4,8 @@ TEST INFRASTRUCTURE (same import rule as ``kd_oracle``). It recomputes the
 same definitions element by element, with no numpy, so that a slip in the
 vectorised oracle (an axis, a broadcast, a dropped term) shows up as a
 disagreement. Definitions as cited in ``kd_oracle``: [White-box OPD, 2.3] for
-the beta family and the temperature, [Top-K KD, 一.2] for the three terms.
+the beta family and the temperature, [Top-K KD, 一.2] for the three terms,
+[White-box OPD, 2.4] for the tail bucket.
 """
 from __future__ import annotations
 
@@ -125,4 +126,42 @@ def fd_grad_topk_row(zs, zt, sel, tau, label, wb, wc, we, eps=1e-6):
         zp[i] += eps
         zm[i] -= eps
         g.append((loss(zp) - loss(zm)) / (2 * eps))
+    return g
+
+
+def tail_loss_row(zs, zt, sup, beta, tau):
+    """Beta-divergence over the buckets {each support entry} + {the rest}
+    for one row ((already rounded) logits; sup: support indices)."""
+    s = [z / tau for z in zs]
+    t = [z / tau for z in zt]
+    lq, _ = log_softmax(s)
+    lp, _ = log_softmax(t)
+    pb = [math.exp(lp[i]) for i in sup]
+    qb = [math.exp(lq[i]) for i in sup]
+    if len(set(sup)) < len(zs):
+        rest = [i for i in range(len(zs)) if i not in set(sup)]
+        pb.append(math.fsum(math.exp(lp[i]) for i in rest))
+        qb.append(math.fsum(math.exp(lq[i]) for i in rest))
+    terms = []
+    for p, q in zip(pb, qb):
+        if beta == 0.0:
+            terms.append(p * math.log(p / q))
+        elif beta == 1.0:
+            terms.append(q * math.log(q / p))
+        else:
+            m = beta * p + (1.0 - beta) * q
+            terms.append(beta * p * math.log(p / m) + (1.0 - beta) * q * math.log(q / m))
+    return math.fsum(terms)
+
+
+def fd_grad_tail_row(zs, zt, sup, beta, tau, eps=1e-6):
+    """Central finite differences of ``tail_loss_row`` w.r.t. each student
+    logit (support and teacher fixed)."""
+    g = []
+    for i in range(len(zs)):
+        zp = list(zs)
+        zm = list(zs)
+        zp[i] += eps
+        zm[i] -= eps
+        g.append((tail_loss_row(zp, zt, sup, beta, tau) - tail_loss_row(zm, zt, sup, beta, tau)) / (2 * eps))
     return g

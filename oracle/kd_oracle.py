@@ -24,7 +24,9 @@ sums). Sources, cited by page title and section:
   0<beta<1 beta*KL(teacher||m) + (1-beta)*KL(student||m) with
   m = (1-beta)*student + beta*teacher; temperature divides logits before the
   softmax; log-domain arithmetic, logsumexp for the mixture; per-token mean),
-  section 2.4 (tail bucket log(1 - sum of top-k probabilities)), section 6
+  section 2.4 (tail bucket log(1 - sum of top-k probabilities); the support
+  is the teacher's top-k, the student's or their union depending on beta, and
+  with one kept entry the sampled token plus the teacher's top-1), section 6
   (CPU test plan).
 * [Top-K KD]  lpnh.cn "Top-K知识蒸馏损失实现详解": section 一.2 (binary KL on the
   mass inside/outside the top-k set, conditional KL on the renormalised shape
@@ -43,6 +45,8 @@ __all__ = [
     "as_f64", "bf16_round", "bf16_neighbours", "logits", "lse", "log_softmax", "divergence",
     "kd_fwd", "grad_student_logits", "kd_bwd", "kd_bwd_w", "topk_order", "topk_three_terms", "kd_topk_fwd",
     "fp32_dot_error_bound", "svd_teacher", "log1mexp", "topk_grad_student_logits", "kd_topk_bwd",
+    "SUPPORT_TEACHER", "SUPPORT_STUDENT", "SUPPORT_LABEL", "tail_default_support", "tail_support_size",
+    "tail_support", "tail_divergence", "kd_tail_fwd", "tail_grad_student_logits", "kd_tail_bwd",
 ]
 
 _SLAB = 8192  # vocabulary rows converted to fp64 at a time (memory only)
@@ -408,6 +412,216 @@ def kd_topk_bwd(h_s, W_s, h_t, W_t, k: int, tau: float, labels=None, w_binary=No
     if sel is None:
         sel = topk_order(zt_b, k)
     g = topk_grad_student_logits(zs_b, zt_b, np.asarray(sel, dtype=np.int64), tau, labels, w_binary, w_cond, w_ce)
+    out = np.zeros((g.shape[0], W_s.shape[1]))
+    for v0 in range(0, W_s.shape[0], _SLAB):
+        out += g[:, v0:v0 + _SLAB] @ as_f64(W_s[v0:v0 + _SLAB])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# top-k support with a tail bucket
+# ---------------------------------------------------------------------------
+SUPPORT_TEACHER, SUPPORT_STUDENT, SUPPORT_LABEL = 1, 2, 4
+
+
+def tail_default_support(k: int, beta: float, with_labels: bool) -> int:
+    """Which entries make up the support of the tail-bucket divergence.
+
+    [White-box OPD, 2.4] With a single kept entry the support is the sampled
+    token (here: the label) together with the teacher's top-1; with more, it is
+    the teacher's top-k, the student's top-k or the union of the two with
+    duplicates removed, depending on beta.
+    READING: the page names the three sets without pairing each with a beta
+    value; here each follows the distribution that weights the divergence:
+    beta = 0 (forward KL, a teacher-weighted sum) takes the teacher's top-k,
+    beta = 1 (reverse KL, student-weighted) the student's, and 0 < beta < 1
+    (both weight it) the union. Returns a mask of SUPPORT_* bits."""
+    if k == 1:
+        return SUPPORT_TEACHER | (SUPPORT_LABEL if with_labels else 0)
+    if beta == 0.0:
+        return SUPPORT_TEACHER
+    if beta == 1.0:
+        return SUPPORT_STUDENT
+    return SUPPORT_TEACHER | SUPPORT_STUDENT
+
+
+def tail_support_size(k: int, support: int) -> int:
+    """Slots per row of a support array: k per selected model, one for the label."""
+    return k * bool(support & SUPPORT_TEACHER) + k * bool(support & SUPPORT_STUDENT) + bool(support & SUPPORT_LABEL)
+
+
+def tail_support(zs_b, zt_b, k: int, support: int, labels=None) -> np.ndarray:
+    """Support indices per row, [rows, tail_support_size(k, support)], -1 padded.
+
+    Order: the teacher's top-k (``topk_order`` of its bf16 logits), then those
+    of the student's top-k not already present (in the student's order), then
+    the label when it is a vocabulary index not already present. An ignored
+    label (-100) adds nothing."""
+    if not 1 <= support <= 7 or not support & (SUPPORT_TEACHER | SUPPORT_STUDENT):
+        raise ValueError("support must select the teacher's or the student's top-k")
+    n_rows, V = zs_b.shape
+    out = np.full((n_rows, tail_support_size(k, support)), -1, dtype=np.int64)
+    selt = topk_order(zt_b, k) if support & SUPPORT_TEACHER else None
+    sels = topk_order(zs_b, k) if support & SUPPORT_STUDENT else None
+    for r in range(n_rows):
+        row = []
+        if selt is not None:
+            row += selt[r].tolist()
+        if sels is not None:
+            row += [v for v in sels[r].tolist() if v not in row]
+        if support & SUPPORT_LABEL and labels is not None:
+            y = int(labels[r])
+            if 0 <= y < V and y not in row:
+                row.append(y)
+        out[r, :len(row)] = row
+    return out
+
+
+def _divergence_logprobs(lp, lq, beta: float):
+    """The beta table of [White-box OPD, 2.3] on given log-probabilities
+    (entries of zero mass contribute nothing). Returns (loss, aux) as
+    ``divergence`` does."""
+    p = np.exp(lp)
+    q = np.exp(lq)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        if beta == 0.0:
+            loss = np.sum(np.where(p > 0, p * (lp - lq), 0.0))
+            return loss, loss
+        if beta == 1.0:
+            loss = np.sum(np.where(q > 0, q * (lq - lp), 0.0))
+            return loss, loss
+        lm = np.logaddexp(np.log(beta) + lp, np.log1p(-beta) + lq)
+        kl_pm = np.sum(np.where(p > 0, p * (lp - lm), 0.0))
+        kl_qm = np.sum(np.where(q > 0, q * (lq - lm), 0.0))
+    return beta * kl_pm + (1.0 - beta) * kl_qm, kl_qm
+
+
+def _tail_buckets(lp_row, lq_row, S):
+    """Bucket log-probabilities: one per support entry, then the tail bucket
+    log(1 - sum over the support) ([White-box OPD, 2.4]) when the support
+    leaves part of the vocabulary out."""
+    lpS = lp_row[S]
+    lqS = lq_row[S]
+    if len(S) == lp_row.shape[0]:
+        return lpS, lqS, False
+    lp_tail = log1mexp(min(float(lse(lpS)), 0.0))
+    lq_tail = log1mexp(min(float(lse(lqS)), 0.0))
+    return np.append(lpS, lp_tail), np.append(lqS, lq_tail), True
+
+
+def tail_divergence(zs_b, zt_b, sup, beta: float, tau: float):
+    """Beta-divergence over the support buckets plus a tail bucket.
+
+    [White-box OPD, 2.4] The divergence is taken on |S| + 1 buckets: each
+    support entry keeps its own (tempered, full-vocabulary) probability under
+    each model, and one more bucket holds the mass outside the support, so
+    that neither distribution loses mass; the beta family is that of
+    [White-box OPD, 2.3]. ``sup`` [rows, slots] holds vocabulary indices,
+    -1 padded. Returns dict(loss, aux, p_mass, q_mass, lse_s, lse_t) with
+    p_mass / q_mass the support's mass under teacher / student and aux the
+    gradient's centring scalar as in ``divergence``."""
+    s = as_f64(zs_b) / tau
+    t = as_f64(zt_b) / tau
+    L_s, L_t = lse(s), lse(t)
+    lq = s - L_s[:, None]
+    lp = t - L_t[:, None]
+    n_rows = s.shape[0]
+    out = {f: np.zeros(n_rows) for f in ("loss", "aux", "p_mass", "q_mass")}
+    for r in range(n_rows):
+        S = np.asarray(sup[r])
+        S = S[S >= 0]
+        lpb, lqb, _ = _tail_buckets(lp[r], lq[r], S)
+        out["loss"][r], out["aux"][r] = _divergence_logprobs(lpb, lqb, beta)
+        out["p_mass"][r] = np.exp(lse(lp[r, S]))
+        out["q_mass"][r] = np.exp(lse(lq[r, S]))
+    out["lse_s"] = L_s
+    out["lse_t"] = L_t
+    return out
+
+
+def kd_tail_fwd(h_s, W_s, h_t, W_t, k: int, beta: float, tau: float, support=None, labels=None,
+                with_bound: bool = False):
+    """Tail-bucket divergence from hidden states.
+
+    Both models' logits are rounded to bf16 (as for the three-term split,
+    [Top-K KD, 二.1]); the support is picked by ``tail_support`` (by default
+    with the rule of ``tail_default_support``) and the divergence is
+    ``tail_divergence``. Returns its dict plus ``sup`` and the bf16 logits at
+    the support, ``val_t`` / ``val_s`` (NaN in padding slots); with
+    ``with_bound`` also both models' exact logits and fp32 error bounds."""
+    if support is None:
+        support = tail_default_support(k, beta, labels is not None)
+    zs = logits(h_s, W_s)
+    zt = logits(h_t, W_t)
+    zs_b = bf16_round(zs)
+    zt_b = bf16_round(zt)
+    sup = tail_support(zs_b, zt_b, k, support, labels)
+    out = tail_divergence(zs_b, zt_b, sup, beta, tau)
+    rows = np.arange(sup.shape[0])[:, None]
+    safe = np.maximum(sup, 0)
+    out["sup"] = sup
+    out["val_t"] = np.where(sup >= 0, zt_b[rows, safe], np.nan)
+    out["val_s"] = np.where(sup >= 0, zs_b[rows, safe], np.nan)
+    if with_bound:
+        out["zs_exact"], out["zt_exact"] = zs, zt
+        out["zs_bound"] = fp32_dot_error_bound(h_s, W_s)
+        out["zt_bound"] = fp32_dot_error_bound(h_t, W_t)
+    return out
+
+
+def tail_grad_student_logits(zs, zt, sup, beta: float, tau: float) -> np.ndarray:
+    """dL/dz_s of ``tail_divergence`` (untempered student logits; the support
+    and the teacher held fixed).
+
+    Derived by the chain rule through the bucket masses: with q the tempered
+    student softmax over the vocabulary, b(v) the bucket of entry v (its own
+    for a support entry, the tail otherwise) and a_b = dL/dq_b,
+      dL/ds_v = q_v (a_b(v) - sum_b q_b a_b),    dL/dz = (dL/ds) / tau,
+    where beta = 0: a_b = -p_b / q_b;  beta = 1: a_b = log q_b - log p_b + 1;
+    0 < beta < 1: a_b = (1 - beta)(log q_b - log m_b). Pinned by central
+    finite differences of the pure-Python bucket loss."""
+    s = as_f64(zs) / tau
+    t = as_f64(zt) / tau
+    lq = s - lse(s)[:, None]
+    lp = t - lse(t)[:, None]
+    q = np.exp(lq)
+    g = np.zeros_like(s)
+    for r in range(s.shape[0]):
+        S = np.asarray(sup[r])
+        S = S[S >= 0]
+        lpb, lqb, has_tail = _tail_buckets(lp[r], lq[r], S)
+        pb, qb = np.exp(lpb), np.exp(lqb)
+        if beta == 0.0:
+            a = -pb / qb
+        elif beta == 1.0:
+            a = lqb - lpb + 1.0
+        else:
+            lm = np.logaddexp(np.log(beta) + lpb, np.log1p(-beta) + lqb)
+            a = (1.0 - beta) * (lqb - lm)
+        c = np.sum(qb * a)
+        bucket_a = np.full(s.shape[1], a[-1] if has_tail else 0.0)
+        bucket_a[S] = a[:len(S)]
+        g[r] = q[r] * (bucket_a - c)
+    return g / tau
+
+
+def kd_tail_bwd(h_s, W_s, h_t, W_t, k: int, beta: float, tau: float, support=None, labels=None, grad_loss=None,
+                sup=None) -> np.ndarray:
+    """dL/dh_s of the tail-bucket divergence, grad_loss[n] weighting row n.
+
+    ``sup``, when given, is the support to hold fixed (the one a forward pass
+    picked); by default the oracle's own. READING: as for the three top-k
+    terms, the support and the teacher are held fixed and the bf16 rounding of
+    the student logits is passed straight through."""
+    zs_b = bf16_round(logits(h_s, W_s))
+    zt_b = bf16_round(logits(h_t, W_t))
+    if sup is None:
+        if support is None:
+            support = tail_default_support(k, beta, labels is not None)
+        sup = tail_support(zs_b, zt_b, k, support, labels)
+    g = tail_grad_student_logits(zs_b, zt_b, sup, beta, tau)
+    if grad_loss is not None:
+        g = g * np.asarray(grad_loss, dtype=np.float64)[:, None]
     out = np.zeros((g.shape[0], W_s.shape[1]))
     for v0 in range(0, W_s.shape[0], _SLAB):
         out += g[:, v0:v0 + _SLAB] @ as_f64(W_s[v0:v0 + _SLAB])
