@@ -57,20 +57,37 @@ typedef enum {
 
 typedef enum { KD_F32 = 0, KD_BF16 = 1 } kd_dtype;
 
-typedef enum { KD_OP_FWD = 0, KD_OP_BWD = 1, KD_OP_TOPK = 2, KD_OP_BWD_W = 3, KD_OP_TOPK_BWD = 4 } kd_op;
+typedef enum {
+  KD_OP_FWD = 0,
+  KD_OP_BWD = 1,
+  KD_OP_TOPK = 2,
+  KD_OP_BWD_W = 3,
+  KD_OP_TOPK_BWD = 4,
+  KD_OP_TAIL = 5,
+  KD_OP_TAIL_BWD = 6
+} kd_op;
+
+/* Support bits of the tail-bucket divergence (kd_tail_fwd / kd_tail_bwd). */
+#define KD_SUPPORT_TEACHER 1 /* the teacher's top-k */
+#define KD_SUPPORT_STUDENT 2 /* the student's top-k */
+#define KD_SUPPORT_LABEL 4   /* the label token */
 
 /* Largest k accepted by kd_topk_fwd. */
 #define KD_TOPK_MAX 64
-/* Largest vocabulary accepted by kd_topk_fwd (8 splits of 65536 entries). */
+/* Largest vocabulary accepted by kd_topk_fwd and kd_tail_fwd (8 splits of
+ * 65536 entries). */
 #define KD_TOPK_MAX_V 524288
 
 /*
  * kd_workspace_size - device workspace (bytes) that `op` needs for this shape.
  *   op: KD_OP_FWD (kd_fwd), KD_OP_BWD (kd_bwd without dW_s), KD_OP_BWD_W
- *   (kd_bwd with dW_s), KD_OP_TOPK (kd_topk_fwd) or KD_OP_TOPK_BWD
- *   (kd_topk_bwd: the same chunk buffers as KD_OP_BWD).
- *   beta is read for KD_OP_FWD, chunk_V for the backward ops, k for
- *   KD_OP_TOPK; d_s/d_t/dtype size the backward's per-chunk buffers.
+ *   (kd_bwd with dW_s), KD_OP_TOPK (kd_topk_fwd), KD_OP_TOPK_BWD
+ *   (kd_topk_bwd: KD_OP_BWD's chunk buffers plus O(N k) floats), KD_OP_TAIL
+ *   (kd_tail_fwd, any support) or KD_OP_TAIL_BWD (kd_tail_bwd, any support:
+ *   KD_OP_BWD's buffers plus O(N k) floats).
+ *   beta is read for KD_OP_FWD, chunk_V for the backward ops, k for the
+ *   top-k and tail ops; d_s/d_t/dtype size the backward's per-chunk
+ *   buffers.
  *   The backward's workspace is O(N * chunk_V) (the gradient tile G of one
  *   vocabulary chunk, in the input dtype) plus O(chunk_V * d_s) for one
  *   transposed chunk of W_s; KD_OP_BWD_W adds a transposed copy of G and of
@@ -201,6 +218,77 @@ kd_status kd_topk_bwd(const void* h_s, const void* W_s, int64_t N, int64_t V, in
                       kd_dtype dtype, const int32_t* labels, const int32_t* topk_idx, const float* topk_val,
                       const float* topk_val_s, const float* p_mass, const float* q_mass, const float* lse_s,
                       const float* lse_s1, const float* grad_binary, const float* grad_cond, const float* grad_ce,
+                      int32_t chunk_V, float* dh_s, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * kd_tail_fwd - beta-divergence over a top-k support plus one tail bucket.
+ *   Source: ars-opd-rebuild "03 · 层 2：White-box OPD 基线", section 2.4 (the
+ *   divergence is taken on the k kept entries plus a tail bucket that holds
+ *   all the probability mass outside them, log(1 - sum of the kept
+ *   probabilities); the kept set is the teacher's top-k, the student's top-k
+ *   or their union with duplicates removed depending on beta, and with a
+ *   single kept entry the sampled token together with the teacher's top-1)
+ *   and section 2.3 (the beta family and the temperature).
+ *   Logits of both models are rounded to bf16 (nearest, ties to even), as for
+ *   kd_topk_fwd. With S the support, p / q the tempered teacher / student
+ *   softmax over the whole vocabulary, the buckets are {v} for v in S and
+ *   the tail T = V \ S (P_T = 1 - sum_S p, Q_T likewise):
+ *     beta = 0:     loss = sum_b p_b log(p_b / q_b)
+ *     beta = 1:     loss = sum_b q_b log(q_b / p_b)
+ *     0 < beta < 1: loss = beta sum_b p_b log(p_b / m_b)
+ *                          + (1 - beta) sum_b q_b log(q_b / m_b),
+ *                   m_b = beta p_b + (1 - beta) q_b,
+ *   with no tail bucket when S covers the vocabulary. A tail mass below fp32
+ *   resolution is held at 2^-24. Only KD_BF16 inputs.
+ *
+ *   support  KD_SUPPORT_* bits; the teacher's or the student's bit (or both)
+ *            must be set. The support lists, in order, the teacher's top-k
+ *            (bf16 logit descending, index ascending), the student's top-k
+ *            entries not already listed, and the label when KD_SUPPORT_LABEL
+ *            is set, the label is in [0, V) and not already listed. The
+ *            usual choices: k == 1: TEACHER | LABEL; else beta == 0: TEACHER,
+ *            beta == 1: STUDENT, 0 < beta < 1: TEACHER | STUDENT.
+ *   k in [1, min(V, KD_TOPK_MAX)]; V <= KD_TOPK_MAX_V (else KD_ERR_UNSUPPORTED).
+ *   labels   (device, [N] int32, read): required with KD_SUPPORT_LABEL,
+ *            else ignored (may be NULL); -100 (or any value outside [0, V))
+ *            adds no entry.
+ *   sup_idx  (device, [N, smax] int32, written), smax = k per ranked model
+ *            + 1 with KD_SUPPORT_LABEL: the support, -1 in unused slots.
+ *   sup_t, sup_s (device, [N, smax] fp32, written): the bf16 teacher /
+ *            student logits (untempered) at sup_idx; NaN in unused slots.
+ *   loss, lse_s, lse_t (device, [N] fp32, written); lse_* over the tempered
+ *            bf16 logits. p_mass, q_mass (device, [N] fp32, written; may be
+ *            NULL): sum_S p and sum_S q.
+ *   workspace (device, >= kd_workspace_size(KD_OP_TAIL, ...) bytes). Each
+ *            ranked model costs one sweep over the vocabulary.
+ */
+kd_status kd_tail_fwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
+                      int32_t d_s, int32_t d_t, int32_t k, int32_t support, float beta, float tau, kd_dtype dtype,
+                      const int32_t* labels, int32_t* sup_idx, float* sup_t, float* sup_s, float* loss, float* p_mass,
+                      float* q_mass, float* lse_s, float* lse_t, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * kd_tail_bwd - gradient of sum_n grad_loss[n] loss[n] of kd_tail_fwd with
+ *   respect to h_s. Source: as kd_tail_fwd (the pages do not spell the
+ *   gradient out). The support and the teacher are held fixed and the bf16
+ *   rounding of the student logits is passed straight through. With b(v) the
+ *   bucket of v and a_b = dloss/dq_b (beta = 0: -p_b / q_b; beta = 1:
+ *   log(q_b / p_b) + 1; else (1 - beta) log(q_b / m_b)):
+ *     dloss/dz_v = q_v (a_b(v) - sum_b q_b a_b) / tau,
+ *   and dh_s[n] = grad_loss[n] sum_v dloss/dz_v W_s[v]. Only KD_BF16 inputs;
+ *   the teacher's arrays are not needed.
+ *
+ *   h_s, W_s (device, read): the forward's student inputs.
+ *   k, support, beta, tau: as given to kd_tail_fwd (k and support fix smax).
+ *   sup_idx, sup_t, sup_s, lse_s, lse_t (device, read): kd_tail_fwd's outputs.
+ *   grad_loss (device, [N] fp32, read; may be NULL = all ones).
+ *   chunk_V: as for kd_bwd. dh_s (device, [N, d_s] fp32, 16-byte aligned,
+ *            overwritten).
+ *   workspace (device, >= kd_workspace_size(KD_OP_TAIL_BWD, ...) bytes).
+ */
+kd_status kd_tail_bwd(const void* h_s, const void* W_s, int64_t N, int64_t V, int32_t d_s, int32_t k, int32_t support,
+                      float beta, float tau, kd_dtype dtype, const int32_t* sup_idx, const float* sup_t,
+                      const float* sup_s, const float* lse_s, const float* lse_t, const float* grad_loss,
                       int32_t chunk_V, float* dh_s, void* workspace, size_t ws_bytes, void* stream);
 
 /*

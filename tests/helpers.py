@@ -181,3 +181,80 @@ def check_topk_rows(out, h_s, W_s, h_t, W_t, rows, k, tau, labels=None, factor=8
                     oks_ce.append(close(np.array([g]), np.array([ce_ref]))[0])
                 assert any(oks_ce), f"row {i} ce {g} vs {O.lse(zs_b) - rs[y]}"
     return exact, flagged
+
+
+def check_tail_rows(out, h_s, W_s, h_t, W_t, rows, k, beta, tau, support, labels=None, factor=8.0):
+    """Acceptance of kd_tail_fwd on ``rows`` against the fp64 oracle.
+
+    As for the top-k terms, a logit within the fp32 accumulation bound of a
+    bf16 rounding midpoint may round either way (``ambiguous``). Per row:
+      * the support holds distinct vocabulary indices in a prefix, -1 / NaN
+        after it, and its size is what the support bits allow;
+      * every returned teacher / student value is the oracle's rounding, or
+        the other neighbour for an ambiguous logit;
+      * the ranked model's list (the teacher's when its bit is set, else the
+        student's) is ordered by (value desc, index asc) and no other entry
+        can outrank its last element under any admissible rounding;
+      * the support equals the oracle's own unless an ambiguous logit is
+        involved (returned as ``flagged``);
+      * loss, masses and LSEs match the oracle's tail divergence evaluated on
+        the kernel's support and its own roundings of the support's logits.
+    Returns (exact_rows, flagged_rows)."""
+    from oracle import kd_oracle as O
+    T, S, L = O.SUPPORT_TEACHER, O.SUPPORT_STUDENT, O.SUPPORT_LABEL
+    V = W_t.shape[0]
+    sup = out["sup_idx"].cpu().numpy()[rows]
+    vt = out["sup_t"].cpu().numpy()[rows].astype(np.float64)
+    vs = out["sup_s"].cpu().numpy()[rows].astype(np.float64)
+    res = {f: out[f].cpu().numpy()[rows] for f in ("loss", "p_mass", "q_mass", "lse_s", "lse_t")}
+    zt = O.logits(h_t[rows], W_t)
+    zs = O.logits(h_s[rows], W_s)
+    bt = O.fp32_dot_error_bound(h_t[rows], W_t, factor)
+    bs = O.fp32_dot_error_bound(h_s[rows], W_s, factor)
+    exact = flagged = 0
+    v_idx = np.arange(V)
+    for i in range(len(rows)):
+        rt, rs = O.bf16_round(zt[i]), O.bf16_round(zs[i])
+        lo_t, hi_t, mid_t = O.bf16_neighbours(zt[i])
+        lo_s, hi_s, mid_s = O.bf16_neighbours(zs[i])
+        amb_t = np.abs(zt[i] - mid_t) <= bt[i]
+        amb_s = np.abs(zs[i] - mid_s) <= bs[i]
+        alt_t = np.where(rt == lo_t, hi_t, lo_t)
+        alt_s = np.where(rs == lo_s, hi_s, lo_s)
+        n = int(np.sum(sup[i] >= 0))
+        row = sup[i, :n].astype(np.int64)
+        assert np.all(sup[i, n:] == -1) and np.all(np.isnan(vt[i, n:])) and np.all(np.isnan(vs[i, n:])), \
+            f"row {i}: padding"
+        assert len(set(row.tolist())) == n and (n == 0 or (row.min() >= 0 and row.max() < V)), f"row {i}: indices"
+        lab = None if labels is None else int(labels[rows[i]])
+        ranked = (support & T) + (support & S) // 2
+        assert k <= n <= k * ranked + (1 if support & L else 0), f"row {i}: support size {n}"
+        okt = (vt[i, :n] == rt[row]) | (amb_t[row] & (vt[i, :n] == alt_t[row]))
+        oks = (vs[i, :n] == rs[row]) | (amb_s[row] & (vs[i, :n] == alt_s[row]))
+        assert okt.all(), f"row {i}: teacher values {vt[i, :n][~okt][:4]} vs {rt[row][~okt][:4]}"
+        assert oks.all(), f"row {i}: student values {vs[i, :n][~oks][:4]} vs {rs[row][~oks][:4]}"
+        if support & L and lab is not None and 0 <= lab < V:
+            assert lab in row.tolist(), f"row {i}: label {lab} missing"
+        # the first ranked list: ordered, and nothing outranks its last element
+        vals, r_, amb, alt = (vt[i], rt, amb_t, alt_t) if support & T else (vs[i], rs, amb_s, alt_s)
+        head = row[:k]
+        for j in range(k - 1):
+            assert (vals[j] > vals[j + 1]) or (vals[j] == vals[j + 1] and head[j] < head[j + 1]), f"row {i}: order {j}"
+        rest = np.ones(V, bool)
+        rest[head] = False
+        minkey = np.where(amb, np.minimum(r_, alt), r_)
+        above = rest & ((minkey > vals[k - 1]) | ((minkey == vals[k - 1]) & (v_idx < head[-1])))
+        assert not above.any(), f"row {i}: entries {v_idx[above][:5]} must outrank the last ranked entry"
+        ref_sup = O.tail_support(rs[None], rt[None], k, support, None if lab is None else np.array([lab]))[0]
+        if np.array_equal(ref_sup[ref_sup >= 0], row):
+            exact += 1
+        else:
+            flagged += 1
+            assert (amb_t | amb_s).any(), f"row {i}: support differs without ambiguity"
+        zt_b, zs_b = rt.copy(), rs.copy()
+        zt_b[row] = vt[i, :n]
+        zs_b[row] = vs[i, :n]
+        ref = O.tail_divergence(zs_b[None], zt_b[None], row[None], beta, tau)
+        for f in ("loss", "p_mass", "q_mass", "lse_s", "lse_t"):
+            assert_close(f"row {i} {f}", res[f][i:i + 1], ref[f])
+    return exact, flagged

@@ -139,8 +139,11 @@ def test_topk_bwd_validation():
     assert call(dh=FAKE + 4) == 2                # dh_s must be 16-byte aligned
     assert call(chunk=300) == 1
     assert call(tau=0.0) == 1
-    need = kd.workspace_size(kd.KD_OP_TOPK_BWD, 8, 100, 64, 64, kd.KD_BF16, chunk_V=256)
-    assert need == kd.workspace_size(kd.KD_OP_BWD, 8, 100, 64, 64, kd.KD_BF16, chunk_V=256)
+    need = kd.workspace_size(kd.KD_OP_TOPK_BWD, 8, 100, 64, 64, kd.KD_BF16, chunk_V=256, k=8)
+    al = lambda x: -(-x // 256) * 256  # noqa: E731
+    # chunk buffers + two per-token coefficients + the (k + 1)-entry list's indices and values
+    assert need == kd.workspace_size(kd.KD_OP_BWD, 8, 100, 64, 64, kd.KD_BF16, chunk_V=256) + 2 * al(8 * 4) + \
+        2 * al(8 * 9 * 4)
     assert call(ws_bytes=need - 1) == 3
 
 
@@ -155,3 +158,51 @@ def test_gather_scatter_validation():
     assert lib.kd_gather_rows(FAKE, -1, 64, FAKE, 4, FAKE, None) == 1
     assert lib.kd_scatter_rows(FAKE, 4, 0, FAKE, FAKE, 10, None) == 1
     assert lib.kd_scatter_rows(FAKE + 2, 4, 64, FAKE, FAKE, 10, None) == 2
+
+
+def test_tail_validation_and_workspace():
+    import vocab_chunked_kl_amd as kd
+    lib = kd.load_library()
+    al = lambda x: -(-x // 256) * 256  # noqa: E731
+    N, V = 300, 151936
+    S = -(-V // 65536)
+    # LSE partials (6 floats per token per 65536-entry split) + one list area per ranked model
+    assert kd.workspace_size(kd.KD_OP_TAIL, N, V, 64, 64, kd.KD_BF16, k=16) == \
+        al(6 * S * N * 4) + 2 * al(S * N * 16 * 4)
+    # chunk buffers + one per-token coefficient + values for the largest support (2k + 1)
+    assert kd.workspace_size(kd.KD_OP_TAIL_BWD, N, V, 64, 64, kd.KD_BF16, chunk_V=256, k=16) == \
+        kd.workspace_size(kd.KD_OP_BWD, N, V, 64, 64, kd.KD_BF16, chunk_V=256) + al(N * 4) + al(N * 33 * 4)
+
+    def fwd(**kw):
+        a = dict(h_s=FAKE, W_s=FAKE, h_t=FAKE, W_t=FAKE, N=8, V=100, d_s=64, d_t=64, k=4, support=1, beta=0.0,
+                 tau=1.0, dtype=1, labels=None, sup_idx=FAKE, sup_t=FAKE, sup_s=FAKE, loss=FAKE, p_mass=None,
+                 q_mass=None, lse_s=FAKE, lse_t=FAKE, ws=FAKE, ws_bytes=1 << 40, stream=None)
+        a.update(kw)
+        return lib.kd_tail_fwd(*[a[n] for n in ("h_s", "W_s", "h_t", "W_t", "N", "V", "d_s", "d_t", "k", "support",
+                                                "beta", "tau", "dtype", "labels", "sup_idx", "sup_t", "sup_s", "loss",
+                                                "p_mass", "q_mass", "lse_s", "lse_t", "ws", "ws_bytes", "stream")])
+    assert fwd(dtype=0) == 2
+    assert fwd(k=0) == 1 and fwd(k=65) == 1 and fwd(k=101, V=100) == 1
+    assert fwd(support=0) == 1 and fwd(support=4, labels=FAKE) == 1 and fwd(support=8) == 1
+    assert fwd(support=5) == 1                   # the label bit needs labels
+    assert fwd(beta=1.5) == 1 and fwd(tau=-1.0) == 1
+    assert fwd(V=kd.KD_TOPK_MAX_V + 1) == 2
+    assert fwd(sup_s=None) == 1 and fwd(loss=None) == 1
+    need = kd.workspace_size(kd.KD_OP_TAIL, 8, 100, 64, 64, kd.KD_BF16, k=4)
+    assert fwd(ws_bytes=need - 1) == 3
+
+    def bwd(**kw):
+        a = dict(h_s=FAKE, W_s=FAKE, N=8, V=100, d_s=64, k=4, support=2, beta=1.0, tau=1.0, dtype=1, sup_idx=FAKE,
+                 sup_t=FAKE, sup_s=FAKE, lse_s=FAKE, lse_t=FAKE, grad=None, chunk=256, dh=FAKE, ws=FAKE,
+                 ws_bytes=1 << 40, stream=None)
+        a.update(kw)
+        return lib.kd_tail_bwd(*[a[n] for n in ("h_s", "W_s", "N", "V", "d_s", "k", "support", "beta", "tau", "dtype",
+                                                "sup_idx", "sup_t", "sup_s", "lse_s", "lse_t", "grad", "chunk", "dh",
+                                                "ws", "ws_bytes", "stream")])
+    assert bwd(dtype=0) == 2
+    assert bwd(support=4) == 1 and bwd(k=0) == 1
+    assert bwd(lse_t=None) == 1 and bwd(sup_idx=None) == 1
+    assert bwd(dh=FAKE + 4) == 2
+    assert bwd(chunk=100) == 1 and bwd(chunk=1 << 22) == 2
+    need = kd.workspace_size(kd.KD_OP_TAIL_BWD, 8, 100, 64, 64, kd.KD_BF16, chunk_V=256, k=4)
+    assert bwd(ws_bytes=need - 1) == 3

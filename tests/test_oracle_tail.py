@@ -188,3 +188,44 @@ def test_kd_tail_fwd_and_bwd_from_hidden_states():
             gz = brute.fd_grad_tail_row(zs[n], zt[n], row, beta, 1.3)
             want = [math.fsum(gz[v] * W_s[v][i] for v in range(V)) * [1.0, 0.5, 2.0][n] for i in range(d)]
             assert np.allclose(dh[n], want, rtol=1e-6, atol=1e-8)
+
+
+def test_gpu_acceptance_check_accepts_the_oracle_and_rejects_planted_mistakes():
+    # the parity helper used by the GPU tests, fed the oracle's own output
+    torch = pytest.importorskip("torch")
+    import kdsynth
+    from tests.helpers import check_tail_rows
+    N, V = 12, 300
+    arrays = kdsynth.small_case(41, N, V, 16, 16)
+    labels = kdsynth.uniform_labels(8, N, V, ignore_frac=0.2)
+    for k, beta, sup in ((1, 0.5, T | L), (8, 0.5, T | S), (8, 1.0, S), (6, 0.0, T | S | L)):
+        ref = O.kd_tail_fwd(*arrays, k, beta, 1.5, support=sup, labels=labels)
+        out = dict(sup_idx=torch.from_numpy(ref["sup"].astype(np.int32)),
+                   sup_t=torch.from_numpy(ref["val_t"].astype(np.float32)),
+                   sup_s=torch.from_numpy(ref["val_s"].astype(np.float32)),
+                   **{f: torch.from_numpy(ref[f].astype(np.float32))
+                      for f in ("loss", "p_mass", "q_mass", "lse_s", "lse_t")})
+        exact, flagged = check_tail_rows(out, *arrays, np.arange(N), k, beta, 1.5, sup, labels)
+        assert exact == N and flagged == 0
+        bad = dict(out, loss=out["loss"] * 1.01)
+        with pytest.raises(AssertionError):
+            check_tail_rows(bad, *arrays, np.arange(N), k, beta, 1.5, sup, labels)
+        if k > 1:  # two ranked entries exchanged
+            swapped = out["sup_idx"].clone()
+            swapped[:, [0, 1]] = swapped[:, [1, 0]]
+            with pytest.raises(AssertionError):
+                check_tail_rows(dict(out, sup_idx=swapped), *arrays, np.arange(N), k, beta, 1.5, sup, labels)
+    # a loss without its tail bucket is rejected
+    ref = O.kd_tail_fwd(*arrays, 8, 0.0, 1.0, support=T)
+    s = O.bf16_round(O.logits(arrays[0], arrays[1]))
+    t = O.bf16_round(O.logits(arrays[2], arrays[3]))
+    lq, lp = O.log_softmax(s), O.log_softmax(t)
+    rows = np.arange(N)[:, None]
+    no_tail = np.sum(np.exp(lp[rows, ref["sup"]]) * (lp[rows, ref["sup"]] - lq[rows, ref["sup"]]), axis=1)
+    out = dict(sup_idx=torch.from_numpy(ref["sup"].astype(np.int32)),
+               sup_t=torch.from_numpy(ref["val_t"].astype(np.float32)),
+               sup_s=torch.from_numpy(ref["val_s"].astype(np.float32)),
+               loss=torch.from_numpy(no_tail.astype(np.float32)),
+               **{f: torch.from_numpy(ref[f].astype(np.float32)) for f in ("p_mass", "q_mass", "lse_s", "lse_t")})
+    with pytest.raises(AssertionError):
+        check_tail_rows(out, *arrays, np.arange(N), 8, 0.0, 1.0, T)

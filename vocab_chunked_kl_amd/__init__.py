@@ -27,19 +27,21 @@ import torch
 
 __all__ = [
     "KDError", "load_library", "workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd",
-    "kd_gather_rows", "kd_scatter_rows",
-    "forward_kl", "reverse_kl", "jsd", "topk_kd", "KD_TOPK_MAX",
+    "kd_tail_fwd", "kd_tail_bwd", "kd_gather_rows", "kd_scatter_rows",
+    "forward_kl", "reverse_kl", "jsd", "topk_kd", "tail_kd", "tail_default_support", "KD_TOPK_MAX",
+    "KD_SUPPORT_TEACHER", "KD_SUPPORT_STUDENT", "KD_SUPPORT_LABEL",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkd.so")
 KD_OK, KD_ERR_INVALID_ARG, KD_ERR_UNSUPPORTED, KD_ERR_WORKSPACE, KD_ERR_HIP = range(5)
 KD_F32, KD_BF16 = 0, 1
-KD_OP_FWD, KD_OP_BWD, KD_OP_TOPK, KD_OP_BWD_W, KD_OP_TOPK_BWD = 0, 1, 2, 3, 4
+KD_OP_FWD, KD_OP_BWD, KD_OP_TOPK, KD_OP_BWD_W, KD_OP_TOPK_BWD, KD_OP_TAIL, KD_OP_TAIL_BWD = range(7)
+KD_SUPPORT_TEACHER, KD_SUPPORT_STUDENT, KD_SUPPORT_LABEL = 1, 2, 4
 KD_TOPK_MAX = 64
 KD_TOPK_MAX_V = 524288
-EXPORTED = ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_gather_rows",
-            "kd_scatter_rows", "kd_status_string", "kd_last_error")
+EXPORTED = ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_tail_fwd", "kd_tail_bwd",
+            "kd_gather_rows", "kd_scatter_rows", "kd_status_string", "kd_last_error")
 
 
 class KDError(RuntimeError):
@@ -70,10 +72,14 @@ def load_library(path: str = LIB_PATH):
                                 vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_topk_bwd.argtypes = [vp, vp, i64, i64, i32, i32, f32, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                 vp, i32, vp, vp, sz, vp]
+    lib.kd_tail_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, i32, i32, f32, f32, ctypes.c_int, vp, vp, vp, vp,
+                                vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.kd_tail_bwd.argtypes = [vp, vp, i64, i64, i32, i32, i32, f32, f32, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32,
+                                vp, vp, sz, vp]
     lib.kd_gather_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
     lib.kd_scatter_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp]
-    for fn in ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_gather_rows",
-               "kd_scatter_rows"):
+    for fn in ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_tail_fwd", "kd_tail_bwd",
+               "kd_gather_rows", "kd_scatter_rows"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
     lib.kd_status_string.restype = ctypes.c_char_p
@@ -224,12 +230,80 @@ def kd_topk_bwd(h_s, W_s, fwd: dict, k: int, tau: float, labels=None, grad_binar
             raise ValueError(f"{name} must be a contiguous fp32 tensor of {N} elements")
     if dh is None:
         dh = torch.empty(N, d_s, dtype=torch.float32, device=dev)
-    nbytes = workspace_size(KD_OP_TOPK_BWD, N, V, d_s, d_s, dt, chunk_V=chunk_V)
+    nbytes = workspace_size(KD_OP_TOPK_BWD, N, V, d_s, d_s, dt, chunk_V=chunk_V, k=k)
     ws = _workspace(nbytes, dev, workspace)
     _check(lib.kd_topk_bwd(_ptr(h_s), _ptr(W_s), N, V, d_s, int(k), float(tau), dt, _ptr(labels),
                            _ptr(fwd["idx"]), _ptr(fwd["val"]), _ptr(fwd["val_s"]), _ptr(fwd["p_mass"]),
                            _ptr(fwd["q_mass"]), _ptr(fwd["lse_s"]), _ptr(fwd.get("lse_s1")), _ptr(grad_binary),
                            _ptr(grad_cond), _ptr(grad_ce), int(chunk_V), _ptr(dh), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream)))
+    return dh
+
+
+def tail_default_support(k: int, beta: float, with_labels: bool) -> int:
+    """Support of the tail-bucket divergence (ars-opd-rebuild "03 · 层 2：White-box
+    OPD 基线", section 2.4): one kept entry -> the label plus the teacher's top-1;
+    else the teacher's top-k (beta = 0, a teacher-weighted sum), the student's
+    (beta = 1) or their union (0 < beta < 1)."""
+    if k == 1:
+        return KD_SUPPORT_TEACHER | (KD_SUPPORT_LABEL if with_labels else 0)
+    if beta == 0.0:
+        return KD_SUPPORT_TEACHER
+    if beta == 1.0:
+        return KD_SUPPORT_STUDENT
+    return KD_SUPPORT_TEACHER | KD_SUPPORT_STUDENT
+
+
+def _support_slots(k: int, support: int) -> int:
+    return (k if support & KD_SUPPORT_TEACHER else 0) + (k if support & KD_SUPPORT_STUDENT else 0) + \
+        (1 if support & KD_SUPPORT_LABEL else 0)
+
+
+def kd_tail_fwd(h_s, W_s, h_t, W_t, k: int, beta: float, tau: float, support: int, labels=None, workspace=None,
+                stream=None):
+    """Tail-bucket divergence over a top-k support; returns a dict of
+    per-token tensors (``loss``, ``sup_idx`` / ``sup_t`` / ``sup_s`` [N, smax],
+    ``p_mass``, ``q_mass``, ``lse_s``, ``lse_t``)."""
+    lib = load_library()
+    N, V, d_s, d_t, dt = _inputs(h_s, W_s, h_t, W_t)
+    dev = h_s.device
+    if labels is not None and (labels.dtype != torch.int32 or labels.numel() != N or not labels.is_contiguous()):
+        raise ValueError("labels must be a contiguous int32 tensor of N elements")
+    smax = max(_support_slots(int(k), int(support)), 1)
+    f = lambda: torch.empty(N, dtype=torch.float32, device=dev)  # noqa: E731
+    out = dict(sup_idx=torch.empty(N, smax, dtype=torch.int32, device=dev),
+               sup_t=torch.empty(N, smax, dtype=torch.float32, device=dev),
+               sup_s=torch.empty(N, smax, dtype=torch.float32, device=dev),
+               loss=f(), p_mass=f(), q_mass=f(), lse_s=f(), lse_t=f())
+    nbytes = workspace_size(KD_OP_TAIL, N, V, d_s, d_t, dt, k=k)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.kd_tail_fwd(_ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t), N, V, d_s, d_t, int(k), int(support),
+                           float(beta), float(tau), dt, _ptr(labels), _ptr(out["sup_idx"]), _ptr(out["sup_t"]),
+                           _ptr(out["sup_s"]), _ptr(out["loss"]), _ptr(out["p_mass"]), _ptr(out["q_mass"]),
+                           _ptr(out["lse_s"]), _ptr(out["lse_t"]), _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream(stream)))
+    return out
+
+
+def kd_tail_bwd(h_s, W_s, fwd: dict, k: int, beta: float, tau: float, support: int, grad_loss=None,
+                chunk_V: int = 8192, workspace=None, stream=None, dh=None):
+    """dL/dh_s (fp32 [N, d_s]) of sum_n grad_loss[n] loss[n] for the dict
+    ``fwd`` that ``kd_tail_fwd`` returned for the same inputs."""
+    lib = load_library()
+    N, V, d_s, _, dt = _inputs(h_s, W_s, h_s, W_s)
+    dev = h_s.device
+    if grad_loss is not None and (grad_loss.dtype != torch.float32 or grad_loss.numel() != N
+                                  or not grad_loss.is_contiguous()):
+        raise ValueError(f"grad_loss must be a contiguous fp32 tensor of {N} elements")
+    if fwd["sup_idx"].shape != (N, _support_slots(int(k), int(support))):
+        raise ValueError("fwd's support arrays do not match k and support")
+    if dh is None:
+        dh = torch.empty(N, d_s, dtype=torch.float32, device=dev)
+    nbytes = workspace_size(KD_OP_TAIL_BWD, N, V, d_s, d_s, dt, chunk_V=chunk_V, k=k)
+    ws = _workspace(nbytes, dev, workspace)
+    _check(lib.kd_tail_bwd(_ptr(h_s), _ptr(W_s), N, V, d_s, int(k), int(support), float(beta), float(tau), dt,
+                           _ptr(fwd["sup_idx"]), _ptr(fwd["sup_t"]), _ptr(fwd["sup_s"]), _ptr(fwd["lse_s"]),
+                           _ptr(fwd["lse_t"]), _ptr(grad_loss), int(chunk_V), _ptr(dh), _ptr(ws),
                            ws.numel() * ws.element_size(), _stream(stream)))
     return dh
 
@@ -409,3 +483,59 @@ def topk_kd(xs, xt, ws, wt, k=64, labels=None, temperature=1.0, ignore_index=-10
                                    float(temperature), lab, int(chunk_V), holder)
     holder.update(binary=binary, cond=cond, ce=ce if lab is not None else None)
     return holder
+
+
+class _Tail(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, xs, ws, xt, wt, k, beta, tau, support, lab, chunk_V, holder):
+        out = kd_tail_fwd(xs, ws, xt, wt, k, beta, tau, support, labels=lab)
+        holder.update(out)
+        ctx.save_for_backward(xs, ws)
+        ctx.out, ctx.k, ctx.beta, ctx.tau, ctx.support, ctx.chunk_V = out, k, beta, tau, support, chunk_V
+        return out["loss"]
+
+    @staticmethod
+    def backward(ctx, g):
+        xs, ws = ctx.saved_tensors
+        if ctx.needs_input_grad[1] or ctx.needs_input_grad[2] or ctx.needs_input_grad[3]:
+            raise NotImplementedError("the tail-bucket divergence gives a gradient to the student hidden state only")
+        if not ctx.needs_input_grad[0]:
+            return (None,) * 11
+        dh = kd_tail_bwd(xs, ws, ctx.out, ctx.k, ctx.beta, ctx.tau, ctx.support, grad_loss=g.float().contiguous(),
+                         chunk_V=ctx.chunk_V)
+        return (dh.to(xs.dtype),) + (None,) * 10
+
+
+def tail_kd(xs, xt, ws, wt, k=1, beta=0.0, labels=None, temperature=1.0, support=None, reduction="mean",
+            ignore_index=-100, chunk_V=8192, return_dict=False):
+    """Beta-divergence over a top-k support plus a tail bucket (ars-opd-rebuild
+    "03 · 层 2：White-box OPD 基线", section 2.4), per-token mean over
+    non-ignored labels by default. ``support`` defaults to
+    ``tail_default_support(k, beta, labels is not None)``. With
+    ``return_dict`` also returns the forward's per-token dict."""
+    d_s, d_t = xs.shape[-1], xt.shape[-1]
+    lead = xs.shape[:-1]
+    lab = None
+    valid = None
+    if labels is not None:
+        lab = labels.reshape(-1).to(torch.int32).contiguous()
+        valid = lab != ignore_index
+        lab = torch.where(valid, lab, torch.full_like(lab, -100))
+    if support is None:
+        support = tail_default_support(int(k), float(beta), lab is not None)
+    holder = {}
+    per_tok = _Tail.apply(xs.reshape(-1, d_s).contiguous(), ws.contiguous(), xt.reshape(-1, d_t).contiguous(),
+                          wt.contiguous(), int(k), float(beta), float(temperature), int(support),
+                          lab if support & KD_SUPPORT_LABEL else None, int(chunk_V), holder)
+    if valid is not None:
+        per_tok = torch.where(valid, per_tok, torch.zeros_like(per_tok))
+    if reduction == "none":
+        res = per_tok.reshape(lead)
+    elif reduction == "sum":
+        res = per_tok.sum()
+    elif reduction == "mean":
+        count = valid.sum() if valid is not None else torch.tensor(per_tok.numel(), device=per_tok.device)
+        res = per_tok.sum() / count.float().clamp_min(1.0)
+    else:
+        raise ValueError(f"unknown reduction {reduction!r}")
+    return (res, holder) if return_dict else res

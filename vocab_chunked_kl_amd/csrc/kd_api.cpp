@@ -90,7 +90,17 @@ kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t
       return KD_OK;
     case KD_OP_TOPK_BWD:
       if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
-      *bytes = kd::bwd_workspace_bytes(p, chunk_V, false);
+      if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
+      *bytes = kd::topk_bwd_workspace_bytes(p, chunk_V, k);
+      return KD_OK;
+    case KD_OP_TAIL:
+      if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
+      *bytes = kd::tail_workspace_bytes(p, k);
+      return KD_OK;
+    case KD_OP_TAIL_BWD:
+      if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
+      if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
+      *bytes = kd::tail_bwd_workspace_bytes(p, chunk_V, k);
       return KD_OK;
   }
   return fail(KD_ERR_INVALID_ARG, "unknown op");
@@ -192,13 +202,68 @@ kd_status kd_topk_bwd(const void* h_s, const void* W_s, int64_t N, int64_t V, in
   if (grad_ce && labels && !lse_s1) return fail(KD_ERR_INVALID_ARG, "lse_s1 is needed for the CE gradient");
   if (!aligned16(dh_s)) return fail(KD_ERR_UNSUPPORTED, "dh_s must be 16-byte aligned");
   const kd::Plan p = kd::make_plan(N, V, d_s, d_s, true);
-  const size_t need = kd::bwd_workspace_bytes(p, chunk_V, false);
+  const size_t need = kd::topk_bwd_workspace_bytes(p, chunk_V, k);
   if (!workspace || ws_bytes < need) return fail(KD_ERR_WORKSPACE, "workspace smaller than kd_workspace_size(TOPK_BWD)");
   if (!aligned16(workspace)) return fail(KD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
   kd::TopkBwdIO io{h_s, W_s, k, tau, chunk_V, labels, topk_idx, topk_val, topk_val_s, p_mass, q_mass, lse_s,
                    grad_ce && labels ? lse_s1 : nullptr, grad_binary, grad_cond, grad_ce, dh_s, workspace};
   hipError_t e = kd::run_topk_bwd(p, io, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KD_OK : hip_fail(e, "kd_topk_bwd launch");
+}
+
+kd_status kd_tail_fwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
+                      int32_t d_s, int32_t d_t, int32_t k, int32_t support, float beta, float tau, kd_dtype dtype,
+                      const int32_t* labels, int32_t* sup_idx, float* sup_t, float* sup_s, float* loss, float* p_mass,
+                      float* q_mass, float* lse_s, float* lse_t, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  kd_status s = check_common(h_s, W_s, h_t, W_t, N, V, d_s, d_t, dtype);
+  if (s != KD_OK) return s;
+  if (dtype != KD_BF16) return fail(KD_ERR_UNSUPPORTED, "kd_tail_fwd takes bf16 inputs only");
+  if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
+  if (support < 1 || support > 7 || !(support & (KD_SUPPORT_TEACHER | KD_SUPPORT_STUDENT)))
+    return fail(KD_ERR_INVALID_ARG, "support must include KD_SUPPORT_TEACHER or KD_SUPPORT_STUDENT");
+  if ((support & KD_SUPPORT_LABEL) && !labels) return fail(KD_ERR_INVALID_ARG, "KD_SUPPORT_LABEL needs labels");
+  if (bad_beta(beta)) return fail(KD_ERR_INVALID_ARG, "beta outside [0, 1]");
+  if (bad_tau(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be positive and finite");
+  if (V > KD_TOPK_MAX_V) return fail(KD_ERR_UNSUPPORTED, "V above KD_TOPK_MAX_V for kd_tail_fwd");
+  if (!sup_idx || !sup_t || !sup_s || !loss || !lse_s || !lse_t) return fail(KD_ERR_INVALID_ARG, "null output pointer");
+  const kd::Plan p = kd::make_plan(N, V, d_s, d_t, true);
+  const size_t need = kd::tail_workspace_bytes(p, k);
+  if (!workspace || ws_bytes < need) return fail(KD_ERR_WORKSPACE, "workspace smaller than kd_workspace_size(TAIL)");
+  if (!aligned16(workspace)) return fail(KD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  kd::TailIO io{h_s,  W_s,     h_t,   W_t,  k,      support, beta,   tau,   (support & KD_SUPPORT_LABEL) ? labels : nullptr,
+                sup_idx, sup_t, sup_s, loss, p_mass, q_mass,  lse_s, lse_t, workspace};
+  hipError_t e = kd::run_tail(p, io, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KD_OK : hip_fail(e, "kd_tail_fwd launch");
+}
+
+kd_status kd_tail_bwd(const void* h_s, const void* W_s, int64_t N, int64_t V, int32_t d_s, int32_t k, int32_t support,
+                      float beta, float tau, kd_dtype dtype, const int32_t* sup_idx, const float* sup_t,
+                      const float* sup_s, const float* lse_s, const float* lse_t, const float* grad_loss,
+                      int32_t chunk_V, float* dh_s, void* workspace, size_t ws_bytes, void* stream) {
+  g_last_error[0] = 0;
+  // the teacher's arrays are not read: the student's stand in for the shape checks
+  kd_status s = check_common(h_s, W_s, h_s, W_s, N, V, d_s, d_s, dtype);
+  if (s != KD_OK) return s;
+  if (dtype != KD_BF16) return fail(KD_ERR_UNSUPPORTED, "kd_tail_bwd takes bf16 inputs only");
+  if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
+  if (support < 1 || support > 7 || !(support & (KD_SUPPORT_TEACHER | KD_SUPPORT_STUDENT)))
+    return fail(KD_ERR_INVALID_ARG, "support must include KD_SUPPORT_TEACHER or KD_SUPPORT_STUDENT");
+  if (bad_beta(beta)) return fail(KD_ERR_INVALID_ARG, "beta outside [0, 1]");
+  if (bad_tau(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be positive and finite");
+  if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
+  if (256 * (int64_t)chunk_V * 2 >= kMaxTileBytes) return fail(KD_ERR_UNSUPPORTED, "chunk_V too large");
+  if (!sup_idx || !sup_t || !sup_s || !lse_s || !lse_t || !dh_s)
+    return fail(KD_ERR_INVALID_ARG, "null input or output pointer");
+  if (!aligned16(dh_s)) return fail(KD_ERR_UNSUPPORTED, "dh_s must be 16-byte aligned");
+  const kd::Plan p = kd::make_plan(N, V, d_s, d_s, true);
+  const size_t need = kd::tail_bwd_workspace_bytes(p, chunk_V, k);
+  if (!workspace || ws_bytes < need) return fail(KD_ERR_WORKSPACE, "workspace smaller than kd_workspace_size(TAIL_BWD)");
+  if (!aligned16(workspace)) return fail(KD_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  kd::TailBwdIO io{h_s, W_s, kd::tail_support_slots(k, support), beta, tau, chunk_V, sup_idx, sup_t, sup_s, lse_s,
+                   lse_t, grad_loss, dh_s, workspace};
+  hipError_t e = kd::run_tail_bwd(p, io, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KD_OK : hip_fail(e, "kd_tail_bwd launch");
 }
 
 kd_status kd_gather_rows(const void* src, int64_t n_src, int64_t row_bytes, const int32_t* rows, int64_t n_rows,

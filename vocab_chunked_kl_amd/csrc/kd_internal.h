@@ -106,6 +106,7 @@ struct TopkBwdIO {
   float* dh;
   void* workspace;
 };
+size_t topk_bwd_workspace_bytes(const Plan& p, int32_t chunk_V, int32_t k);
 hipError_t run_topk_bwd(const Plan& p, const TopkBwdIO& io, hipStream_t stream);
 
 // dst[i] = src[rows[i]] (gather) or dst[rows[i]] = src[i] (scatter), rows of
@@ -113,5 +114,32 @@ hipError_t run_topk_bwd(const Plan& p, const TopkBwdIO& io, hipStream_t stream);
 hipError_t run_copy_rows(const void* src, void* dst, const int32_t* rows, int64_t n_rows, int64_t n_other,
                          int64_t row_bytes, bool scatter, hipStream_t stream);
 hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t stream);
+
+// Tail-bucket divergence over a top-k support (support bits KD_SUPPORT_*).
+struct TailIO {
+  const void *h_s, *W_s, *h_t, *W_t;
+  int32_t k, support;
+  float beta, tau;
+  const int32_t* labels;
+  int32_t* sup_idx;  // [N, smax]
+  float *sup_t, *sup_s, *loss, *p_mass, *q_mass, *lse_s, *lse_t;
+  void* workspace;
+};
+int32_t tail_support_slots(int32_t k, int32_t support);
+size_t tail_workspace_bytes(const Plan& p, int32_t k);
+hipError_t run_tail(const Plan& p, const TailIO& io, hipStream_t stream);
+
+struct TailBwdIO {
+  const void *h_s, *W_s;
+  int32_t smax;
+  float beta, tau;
+  int32_t chunk_V;
+  const int32_t* sup_idx;
+  const float *sup_t, *sup_s, *lse_s, *lse_t, *grad;
+  float* dh;
+  void* workspace;
+};
+size_t tail_bwd_workspace_bytes(const Plan& p, int32_t chunk_V, int32_t k);
+hipError_t run_tail_bwd(const Plan& p, const TailBwdIO& io, hipStream_t stream);
 
 }  // namespace kd

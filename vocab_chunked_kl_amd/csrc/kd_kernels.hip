@@ -480,45 +480,32 @@ __global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Top-k backward ([Top-K KD] 一.2 terms; gradient reading: selection and
-// teacher fixed, bf16 rounding of the student logits passed straight through).
-// dL/dz_s = dense + sparse, with q the tempered student softmax, r the
-// untempered one, Q / P the student / teacher mass on the set K:
-//   dense  (every v): -w_b B Q q_v / tau + w_ce r_v,   B = -P/Q + (1-P)/(1-Q)
-//   sparse (v in K):  (w_b B q_v + w_c (q_v / Q - p_v / P)) / tau
-//   sparse (v = y):   -w_ce
-// The sparse part is a k+1-row gather per token; the dense part is a
-// student-only recompute sweep writing G (bf16) for the dh GEMM.
+// Backward of the top-k style losses (the three top-k terms, [Top-K KD] 一.2;
+// the tail-bucket divergence, [White-box OPD] 2.4). Gradient reading: the
+// selection and the teacher fixed, the bf16 rounding of the student logits
+// passed straight through. Either gradient w.r.t. the student logits is
+//   dL/dz_v = A q_v + C r_v     for every v outside a short per-token list,
+// (q the tempered student softmax, r the untempered one, A and C per token)
+// and an arbitrary value on the list (the selected entries and the label).
+// A coefficient kernel (one wave per token) computes A, C and the list's
+// exact values; per vocabulary chunk a student-only recompute sweep writes
+// G = A q + C r in bf16, the list's entries in the chunk overwrite their G
+// elements, and the dh GEMM contracts G with the chunk of W_s. Writing the
+// listed values whole (rather than adding a correction to A q) keeps the bf16
+// rounding of G relative to each entry's own value.
 // ---------------------------------------------------------------------------
-struct TopkBwdArgs {
-  PairDesc ps;        // (W_s, h_s)
+struct DenseArgs {
+  PairDesc ps;  // (W_s, h_s)
   int64_t N, V;
-  int k;
-  float c2, inv_tau;  // log2(e) / tau, 1 / tau
-  const int32_t* labels;
-  const int32_t* idx;
-  const float *val_t, *val_s, *p_mass, *q_mass, *lse_s, *lse_s1, *gb, *gc, *ge;
+  float c2;     // log2(e) / tau
+  const float *lse_s, *lse_s1;  // lse_s1 only when dense_c is set
+  const float *dense_a, *dense_c;
   int n_tok_tiles, n_splits, tiles_per_split, n_vtiles, vt_offset;
   char* G;
   int64_t ldg, g_col0;
-  float* dh;
-  int32_t d_s;
 };
 
-// B of the binary term for token n (0 when the set is the whole vocabulary).
-__device__ __forceinline__ float topk_binary_slope(const TopkBwdArgs& a, int64_t n) {
-  if ((int64_t)a.k >= a.V) return 0.f;
-  const float P = a.p_mass[n], Q = a.q_mass[n];
-  return -P / Q + (1.f - P) / (1.f - Q);
-}
-
-__device__ __forceinline__ float topk_ce_weight(const TopkBwdArgs& a, int64_t n) {
-  if (!a.ge || !a.labels) return 0.f;
-  const int32_t y = a.labels[n];
-  return (y >= 0 && y < a.V) ? a.ge[n] : 0.f;
-}
-
-__global__ __launch_bounds__(kLogitThreads, 1) void topk_bwdg_kernel(TopkBwdArgs a) {
+__global__ __launch_bounds__(kLogitThreads, 1) void dense_g_kernel(DenseArgs a) {
   constexpr int TM = kTileV, TN = kTileT, WM = kLogitWM, WN = kLogitWN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
   KD_RING_LDS_N(TM, TN, kLogitRB, kLogitBuf);
@@ -536,10 +523,11 @@ __global__ __launch_bounds__(kLogitThreads, 1) void topk_bwdg_kernel(TopkBwdArgs
     Ls2[nb] = L12[nb] = A[nb] = C[nb] = 0.f;
     if (n < a.N) {
       Ls2[nb] = a.lse_s[n] * kLog2e;
-      L12[nb] = a.lse_s1 ? a.lse_s1[n] * kLog2e : 0.f;
-      const float wb = a.gb ? a.gb[n] : 0.f;
-      A[nb] = -wb * topk_binary_slope(a, n) * a.q_mass[n] * a.inv_tau;
-      C[nb] = a.lse_s1 ? topk_ce_weight(a, n) : 0.f;
+      A[nb] = a.dense_a[n];
+      if (a.dense_c) {
+        L12[nb] = a.lse_s1[n] * kLog2e;
+        C[nb] = a.dense_c[n];
+      }
     }
   }
   auto epi = [&](int vt, auto& zs, auto&) {
@@ -574,65 +562,199 @@ __global__ __launch_bounds__(kLogitThreads, 1) void topk_bwdg_kernel(TopkBwdArgs
   sweep<true, TM, TN, WM, WN, kLogitBuf, kLogitRB, false>(a.ps, a.ps, (int64_t)tt * TN, vt0, vt1, lds, epi);
 }
 
-// Sparse part, one wave per token: dh_s[n] = sum_j c_j W_s[idx_j] - w_ce W_s[y]
-// (overwrites dh_s; the dense chunks accumulate onto it).
-__global__ __launch_bounds__(256) void topk_sparse_kernel(TopkBwdArgs a) {
+// The listed entries of one vocabulary chunk overwrite their G elements: one
+// thread per (token, list slot); slots holding -1 or an index outside the
+// chunk are skipped.
+struct FixArgs {
+  const int32_t* idx;  // [N, slots]
+  const float* val;    // [N, slots], dL/dz at idx
+  int64_t N;
+  int slots;
+  int64_t c0, ccols;
+  char* G;
+  int64_t ldg;
+};
+
+__global__ __launch_bounds__(256) void g_fix_kernel(FixArgs f) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= f.N * f.slots) return;
+  const int64_t n = i / f.slots;
+  const int64_t v = f.idx[i];
+  if (v < f.c0 || v >= f.c0 + f.ccols) return;
+  *reinterpret_cast<uint16_t*>(f.G + n * f.ldg + (v - f.c0) * 2) = (uint16_t)f32_to_bf16_bits(f.val[i]);
+}
+
+__device__ __forceinline__ float wsum64(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wmax64(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// Student logit for vocabulary row v, fp32 dot product by the whole wave
+// (lane-strided partial sums, then a wave sum), rounded to bf16.
+__device__ __forceinline__ float wave_dot_bf16(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int64_t v,
+                                               int32_t d, int lane) {
+  const uint16_t* w = W + v * d;
+  float acc = 0.f;
+  for (int i = lane * 8; i < d; i += 64 * 8) {
+    const u32x4 hv = *reinterpret_cast<const u32x4*>(h + i);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(w + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t hx = hv[e], wx = wv[e];
+      acc = fmaf(__builtin_bit_cast(float, hx << 16), __builtin_bit_cast(float, wx << 16), acc);
+      acc = fmaf(__builtin_bit_cast(float, hx & 0xFFFF0000u), __builtin_bit_cast(float, wx & 0xFFFF0000u), acc);
+    }
+  }
+  return __builtin_bit_cast(float, f32_to_bf16_bits(wsum64(acc)) << 16);
+}
+
+// Three top-k terms. With Q / P the student / teacher mass on the set K, p^
+// the renormalised teacher on K, B = -P/Q + (1-P)/(1-Q) (0 when k == V):
+//   A = -w_b B Q / tau,  C = w_ce (when a label and its weight are given)
+//   v in K:  A q_v + C r_v + (w_b B q_v + w_c (q_v / Q - p^_v)) / tau - C 1[v = y]
+//   v = y outside K:  C (r_y - 1)
+// List: the k selected entries, then the label when it is outside K.
+struct TopkCoefArgs {
+  const uint16_t *h_s, *W_s;
+  int64_t N, V;
+  int32_t d_s;
+  int k;
+  float inv_tau;
+  const int32_t* labels;
+  const int32_t* idx;
+  const float *val_t, *val_s, *p_mass, *q_mass, *lse_s, *lse_s1, *gb, *gc, *ge;
+  float *dense_a, *dense_c;
+  int32_t* list_idx;  // [N, k + 1]
+  float* list_val;    // [N, k + 1]
+};
+
+__global__ __launch_bounds__(256) void topk_coef_kernel(TopkCoefArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n = (int64_t)blockIdx.x * 4 + wave;
   if (n >= a.N) return;  // whole waves only
-  const int K = a.k;
+  const int K = a.k, slots = K + 1;
   const bool act = lane < K;
   const int32_t v = act ? a.idx[n * K + lane] : -1;
   const bool ok = act && v >= 0 && v < a.V;
   // renormalised teacher on the set, from its bf16 values
   const float t = ok ? a.val_t[n * K + lane] * a.inv_tau : -INFINITY;
-  float mt = t;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mt = fmaxf(mt, __shfl_xor(mt, o));
-  float et = ok ? expf(t - mt) : 0.f, st = et;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) st += __shfl_xor(st, o);
-  const float ph = et / st;
-  const float Q = a.q_mass[n];
-  const float q = ok ? expf(a.val_s[n * K + lane] * a.inv_tau - a.lse_s[n]) : 0.f;
+  const float mt = wmax64(t);
+  const float et = ok ? expf(t - mt) : 0.f;
+  const float ph = et / wsum64(et);
+  const float P = a.p_mass[n], Q = a.q_mass[n];
+  const float B = (int64_t)K >= a.V ? 0.f : -P / Q + (1.f - P) / (1.f - Q);
   const float wb = a.gb ? a.gb[n] : 0.f, wc = a.gc ? a.gc[n] : 0.f;
-  const float cj = ok ? (wb * topk_binary_slope(a, n) * q + wc * (q / Q - ph)) * a.inv_tau : 0.f;
-  const float wce = topk_ce_weight(a, n);
-  const int32_t y = wce != 0.f ? a.labels[n] : -1;
-  const uint16_t* W = static_cast<const uint16_t*>(static_cast<const void*>(a.ps.A));
-  // every lane runs every iteration (the shuffles need the whole wave); only
-  // the memory accesses are guarded
-  for (int base = 0; base < a.d_s; base += 64 * 8) {
-    const int d0 = base + lane * 8;
-    const bool in = d0 < a.d_s;  // d_s is a multiple of 8: then all 8 columns exist
-    float acc[8];
+  const int32_t y = a.labels ? a.labels[n] : -1;
+  const bool has_ce = a.ge && a.lse_s1 && y >= 0 && y < a.V;
+  const float C = has_ce ? a.ge[n] : 0.f;
+  const float A = -wb * B * Q * a.inv_tau;
+  const float L1 = has_ce ? a.lse_s1[n] : 0.f;
+  const float zs = ok ? a.val_s[n * K + lane] : 0.f;
+  const float q = ok ? expf(zs * a.inv_tau - a.lse_s[n]) : 0.f;
+  const float r = (ok && has_ce) ? expf(zs - L1) : 0.f;
+  const float total = (wb * B * q * (1.f - Q) + wc * (q / Q - ph)) * a.inv_tau + C * (r - (v == y ? 1.f : 0.f));
+  if (act) {
+    a.list_idx[n * slots + lane] = ok ? v : -1;
+    a.list_val[n * slots + lane] = ok ? total : 0.f;
+  }
+  const bool y_in_k = __ballot(ok && v == y) != 0ull;
+  int32_t yi = -1;
+  float yv = 0.f;
+  if (has_ce && !y_in_k && C != 0.f) {  // wave-uniform
+    const float zy = wave_dot_bf16(a.h_s + n * a.d_s, a.W_s, y, a.d_s, lane);
+    yi = y;
+    yv = C * (expf(zy - L1) - 1.f);
+  }
+  if (lane == 0) {
+    a.list_idx[n * slots + K] = yi;
+    a.list_val[n * slots + K] = yv;
+    a.dense_a[n] = A;
+    if (a.dense_c) a.dense_c[n] = C;
+  }
+}
+
+// Tail-bucket divergence. With b(v) the bucket of entry v and a_b = dL/dq_b,
+// dL/ds_v = q_v (a_b(v) - c), c = sum_b q_b a_b; beta = 0: q_b a_b = -p_b;
+// beta = 1: a_b = log q_b - log p_b + 1; 0 < beta < 1:
+// a_b = (1 - beta)(log q_b - log m_b). Outside the support every entry is in
+// the tail bucket: A = (a_T - c) w (w = grad_loss / tau), C = 0; the support
+// entries get q_v (a_v - c) w. The list is the forward's support as it is.
+struct TailCoefArgs {
+  int64_t N, V;
+  int smax;
+  float beta, inv_tau;
+  const int32_t* sup_idx;
+  const float *sup_t, *sup_s, *lse_s, *lse_t, *grad;
+  float *dense_a, *list_val;  // [N], [N, smax]
+};
+
+__device__ __forceinline__ float log1mexp_f32(float x) {  // log(1 - e^x), x < 0
+  return x > -0.69314718f ? logf(-expm1f(x)) : log1pf(-expf(x));
+}
+
+__global__ __launch_bounds__(256) void tail_coef_kernel(TailCoefArgs a) {
+  constexpr int kSlots = 3;  // 2 * 64 + 1 support entries at most: three per lane
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * 4 + wave;
+  if (n >= a.N) return;  // whole waves only
+  const float Ls = a.lse_s[n], Lt = a.lse_t[n];
+  float lp[kSlots], lq[kSlots];
+  bool okj[kSlots];
+  int cnt_l = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int j = 0; j < K; ++j) {
-      const int32_t vj = __shfl(v, j);
-      const float c = __shfl(cj, j);
-      if (vj < 0 || vj >= a.V || c == 0.f || !in) continue;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(W + (int64_t)vj * a.d_s + d0);
+  for (int j = 0; j < kSlots; ++j) {
+    const int i = lane + 64 * j;
+    const int32_t v = i < a.smax ? a.sup_idx[n * a.smax + i] : -1;
+    okj[j] = v >= 0 && v < a.V;
+    lp[j] = okj[j] ? a.sup_t[n * a.smax + i] * a.inv_tau - Lt : -INFINITY;
+    lq[j] = okj[j] ? a.sup_s[n * a.smax + i] * a.inv_tau - Ls : -INFINITY;
+    cnt_l += okj[j];
+  }
+  const int cnt = (int)wsum64((float)cnt_l);
+  const float mp = wmax64(fmaxf(lp[0], fmaxf(lp[1], lp[2])));
+  const float mq = wmax64(fmaxf(lq[0], fmaxf(lq[1], lq[2])));
+  float ep = 0.f, eq = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t x = w[e];
-        acc[2 * e] = fmaf(c, __builtin_bit_cast(float, x << 16), acc[2 * e]);
-        acc[2 * e + 1] = fmaf(c, __builtin_bit_cast(float, x & 0xFFFF0000u), acc[2 * e + 1]);
-      }
-    }
-    if (!in) continue;
-    if (y >= 0) {
-      const u32x4 w = *reinterpret_cast<const u32x4*>(W + (int64_t)y * a.d_s + d0);
+  for (int j = 0; j < kSlots; ++j) {
+    ep += okj[j] ? expf(lp[j] - mp) : 0.f;
+    eq += okj[j] ? expf(lq[j] - mq) : 0.f;
+  }
+  const float logP = mp + logf(wsum64(ep)), logQ = mq + logf(wsum64(eq));
+  // the forward's tail convention: masses below fp32 resolution held at 2^-24
+  const bool tail = (int64_t)cnt < a.V;
+  const float lpT = log1mexp_f32(fminf(logP, -5.9604645e-8f));
+  const float lqT = log1mexp_f32(fminf(logQ, -5.9604645e-8f));
+  const float beta = a.beta, lb = logf(beta), l1b = log1pf(-beta);
+  // a_b for beta > 0 (log-domain mixture for 0 < beta < 1)
+  auto a_of = [&](float p_, float q_) {
+    if (beta == 1.f) return q_ - p_ + 1.f;
+    const float x = lb + p_, y = l1b + q_;
+    const float lm = fmaxf(x, y) + log1pf(expf(-fabsf(x - y)));
+    return (1.f - beta) * (q_ - lm);
+  };
+  const float qT = tail ? expf(lqT) : 0.f;
+  const float aT = !tail ? 0.f : beta == 0.f ? -expf(lpT - lqT) : a_of(lpT, lqT);
+  float qa[kSlots], q[kSlots], csum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t x = w[e];
-        acc[2 * e] = fmaf(-wce, __builtin_bit_cast(float, x << 16), acc[2 * e]);
-        acc[2 * e + 1] = fmaf(-wce, __builtin_bit_cast(float, x & 0xFFFF0000u), acc[2 * e + 1]);
-      }
-    }
-    float* o = a.dh + n * a.d_s + d0;
-    *reinterpret_cast<floatx4*>(o) = floatx4{acc[0], acc[1], acc[2], acc[3]};
-    *reinterpret_cast<floatx4*>(o + 4) = floatx4{acc[4], acc[5], acc[6], acc[7]};
+  for (int j = 0; j < kSlots; ++j) {
+    q[j] = okj[j] ? expf(lq[j]) : 0.f;
+    // q_b a_b; for beta = 0 taken as -p_b (no division by a small q_b)
+    qa[j] = !okj[j] ? 0.f : beta == 0.f ? -expf(lp[j]) : q[j] * a_of(lp[j], lq[j]);
+    csum += qa[j];
+  }
+  const float c = wsum64(csum) + qT * aT;
+  const float w = (a.grad ? a.grad[n] : 1.f) * a.inv_tau;
+  if (lane == 0) a.dense_a[n] = (aT - c) * w;
+#pragma unroll
+  for (int j = 0; j < kSlots; ++j) {
+    const int i = lane + 64 * j;
+    if (i < a.smax) a.list_val[n * a.smax + i] = okj[j] ? (qa[j] - c * q[j]) * w : 0.f;
   }
 }
 
@@ -866,65 +988,147 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   return hipSuccess;
 }
 
-hipError_t run_topk_bwd(const Plan& p, const TopkBwdIO& io, hipStream_t st) {
-  char* G = static_cast<char*>(io.workspace);
-  char* WsT = G + align_up((size_t)p.N * io.chunk_V * 2, 256);
-  TopkBwdArgs a{};
-  a.ps = PairDesc{static_cast<const char*>(io.W_s), static_cast<const char*>(io.h_s), (int64_t)p.d_s * 2,
-                  (int64_t)p.d_s * 2, p.V, p.N, (int32_t)(p.d_s * 2)};
-  a.N = p.N;
-  a.V = p.V;
-  a.k = io.k;
-  a.c2 = kLog2e / io.tau;
-  a.inv_tau = 1.f / io.tau;
-  a.labels = io.labels;
-  a.idx = io.idx;
-  a.val_t = io.val_t;
-  a.val_s = io.val_s;
-  a.p_mass = io.p_mass;
-  a.q_mass = io.q_mass;
-  a.lse_s = io.lse_s;
-  a.lse_s1 = io.lse_s1;
-  a.gb = io.grad_binary;
-  a.gc = io.grad_cond;
-  a.ge = io.grad_ce;
-  a.n_tok_tiles = p.n_tok_tiles;
-  a.tiles_per_split = 1;
-  a.G = G;
-  a.ldg = (int64_t)io.chunk_V * 2;
-  a.dh = io.dh;
-  a.d_s = p.d_s;
-  hipLaunchKernelGGL(topk_sparse_kernel, dim3((unsigned)((p.N + 3) / 4)), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+// Per vocabulary chunk: G = A q + C r (dense_g_kernel), the listed entries
+// overwrite their G elements (g_fix_kernel), W_s's chunk is transposed, and
+// the dh GEMM writes (first chunk) or accumulates onto dh_s.
+static hipError_t run_list_chunks(const Plan& p, DenseArgs a, const int32_t* list_idx, const float* list_val, int slots,
+                                  const void* W_s, char* G, char* WsT, int32_t chunk_V, float* dh, hipStream_t st) {
+  hipError_t e;
   const int n_d_tiles = (p.d_s + kTileDhD - 1) / kTileDhD;
   const int n_tok_tiles_dh = (int)((p.N + kTileDhT - 1) / kTileDhT);
-  for (int64_t c0 = 0; c0 < p.V; c0 += io.chunk_V) {
-    const int64_t ccols = (p.V - c0 < io.chunk_V) ? p.V - c0 : io.chunk_V;
+  FixArgs f{list_idx, list_val, p.N, slots, 0, 0, G, (int64_t)chunk_V * 2};
+  const unsigned fix_blocks = (unsigned)((p.N * slots + 255) / 256);
+  for (int64_t c0 = 0; c0 < p.V; c0 += chunk_V) {
+    const int64_t ccols = (p.V - c0 < chunk_V) ? p.V - c0 : chunk_V;
     const int ctiles = (int)((ccols + kTileV - 1) / kTileV);
     const int64_t kcols = (int64_t)ctiles * kTileV;
     a.vt_offset = (int)(c0 / kTileV);
     a.n_vtiles = ctiles;
     a.n_splits = ctiles;
     a.g_col0 = c0;
-    hipLaunchKernelGGL(topk_bwdg_kernel, dim3(p.n_tok_tiles * ctiles), dim3(kLogitThreads), 0, st, a);
+    hipLaunchKernelGGL(dense_g_kernel, dim3(p.n_tok_tiles * ctiles), dim3(kLogitThreads), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    f.c0 = c0;
+    f.ccols = ccols;
+    hipLaunchKernelGGL(g_fix_kernel, dim3(fix_blocks), dim3(256), 0, st, f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 tgrid((unsigned)(kcols / 64), (unsigned)((p.d_s + 63) / 64));
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, tgrid, dim3(256), 0, st, static_cast<const uint16_t*>(io.W_s),
-                       reinterpret_cast<uint16_t*>(WsT), p.V, p.d_s, c0, (int64_t)io.chunk_V);
+    hipLaunchKernelGGL(transpose_kernel<uint16_t>, tgrid, dim3(256), 0, st, static_cast<const uint16_t*>(W_s),
+                       reinterpret_cast<uint16_t*>(WsT), p.V, p.d_s, c0, (int64_t)chunk_V);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     DhArgs da{};
-    da.p = PairDesc{G, WsT, (int64_t)io.chunk_V * 2, (int64_t)io.chunk_V * 2, p.N, p.d_s, (int32_t)(kcols * 2)};
+    da.p = PairDesc{G, WsT, (int64_t)chunk_V * 2, (int64_t)chunk_V * 2, p.N, p.d_s, (int32_t)(kcols * 2)};
     da.N = p.N;
     da.d_s = p.d_s;
     da.n_tok_tiles = n_tok_tiles_dh;
     da.n_d_tiles = n_d_tiles;
-    da.dh = io.dh;
-    da.first = 0;  // onto the sparse part
+    da.dh = dh;
+    da.first = c0 == 0 ? 1 : 0;
     hipLaunchKernelGGL(dh_kernel<true>, dim3(n_tok_tiles_dh * n_d_tiles), dim3(kDhThreads), 0, st, da);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+static DenseArgs dense_args(const Plan& p, const void* h_s, const void* W_s, float tau, char* G, int32_t chunk_V) {
+  DenseArgs a{};
+  a.ps = PairDesc{static_cast<const char*>(W_s), static_cast<const char*>(h_s), (int64_t)p.d_s * 2,
+                  (int64_t)p.d_s * 2, p.V, p.N, (int32_t)(p.d_s * 2)};
+  a.N = p.N;
+  a.V = p.V;
+  a.c2 = kLog2e / tau;
+  a.n_tok_tiles = p.n_tok_tiles;
+  a.tiles_per_split = 1;
+  a.G = G;
+  a.ldg = (int64_t)chunk_V * 2;
+  return a;
+}
+
+// Workspace after the chunk buffers: dense_a [N], dense_c [N] (top-k only),
+// the list's indices [N, slots] (top-k only) and values [N, slots].
+size_t topk_bwd_workspace_bytes(const Plan& p, int32_t chunk_V, int32_t k) {
+  const size_t slots = (size_t)k + 1;
+  return bwd_workspace_bytes(p, chunk_V, false) + 2 * align_up((size_t)p.N * 4, 256) +
+         2 * align_up((size_t)p.N * slots * 4, 256);
+}
+
+size_t tail_bwd_workspace_bytes(const Plan& p, int32_t chunk_V, int32_t k) {
+  const size_t slots = 2 * (size_t)k + 1;  // the largest support
+  return bwd_workspace_bytes(p, chunk_V, false) + align_up((size_t)p.N * 4, 256) +
+         align_up((size_t)p.N * slots * 4, 256);
+}
+
+hipError_t run_topk_bwd(const Plan& p, const TopkBwdIO& io, hipStream_t st) {
+  char* G = static_cast<char*>(io.workspace);
+  char* WsT = G + align_up((size_t)p.N * io.chunk_V * 2, 256);
+  char* rest = static_cast<char*>(io.workspace) + bwd_workspace_bytes(p, io.chunk_V, false);
+  const int slots = io.k + 1;
+  float* dense_a = reinterpret_cast<float*>(rest);
+  float* dense_c = reinterpret_cast<float*>(rest + align_up((size_t)p.N * 4, 256));
+  int32_t* list_idx = reinterpret_cast<int32_t*>(rest + 2 * align_up((size_t)p.N * 4, 256));
+  float* list_val = reinterpret_cast<float*>(reinterpret_cast<char*>(list_idx) + align_up((size_t)p.N * slots * 4, 256));
+  TopkCoefArgs c{};
+  c.h_s = static_cast<const uint16_t*>(io.h_s);
+  c.W_s = static_cast<const uint16_t*>(io.W_s);
+  c.N = p.N;
+  c.V = p.V;
+  c.d_s = p.d_s;
+  c.k = io.k;
+  c.inv_tau = 1.f / io.tau;
+  c.labels = io.labels;
+  c.idx = io.idx;
+  c.val_t = io.val_t;
+  c.val_s = io.val_s;
+  c.p_mass = io.p_mass;
+  c.q_mass = io.q_mass;
+  c.lse_s = io.lse_s;
+  c.lse_s1 = io.lse_s1;
+  c.gb = io.grad_binary;
+  c.gc = io.grad_cond;
+  c.ge = io.grad_ce;
+  c.dense_a = dense_a;
+  const bool ce = io.grad_ce && io.labels && io.lse_s1;
+  c.dense_c = ce ? dense_c : nullptr;
+  c.list_idx = list_idx;
+  c.list_val = list_val;
+  hipLaunchKernelGGL(topk_coef_kernel, dim3((unsigned)((p.N + 3) / 4)), dim3(256), 0, st, c);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  DenseArgs a = dense_args(p, io.h_s, io.W_s, io.tau, G, io.chunk_V);
+  a.lse_s = io.lse_s;
+  a.lse_s1 = ce ? io.lse_s1 : nullptr;
+  a.dense_a = dense_a;
+  a.dense_c = ce ? dense_c : nullptr;
+  return run_list_chunks(p, a, list_idx, list_val, slots, io.W_s, G, WsT, io.chunk_V, io.dh, st);
+}
+
+hipError_t run_tail_bwd(const Plan& p, const TailBwdIO& io, hipStream_t st) {
+  char* G = static_cast<char*>(io.workspace);
+  char* WsT = G + align_up((size_t)p.N * io.chunk_V * 2, 256);
+  char* rest = static_cast<char*>(io.workspace) + bwd_workspace_bytes(p, io.chunk_V, false);
+  float* dense_a = reinterpret_cast<float*>(rest);
+  float* list_val = reinterpret_cast<float*>(rest + align_up((size_t)p.N * 4, 256));
+  TailCoefArgs c{};
+  c.N = p.N;
+  c.V = p.V;
+  c.smax = io.smax;
+  c.beta = io.beta;
+  c.inv_tau = 1.f / io.tau;
+  c.sup_idx = io.sup_idx;
+  c.sup_t = io.sup_t;
+  c.sup_s = io.sup_s;
+  c.lse_s = io.lse_s;
+  c.lse_t = io.lse_t;
+  c.grad = io.grad;
+  c.dense_a = dense_a;
+  c.list_val = list_val;
+  hipLaunchKernelGGL(tail_coef_kernel, dim3((unsigned)((p.N + 3) / 4)), dim3(256), 0, st, c);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  DenseArgs a = dense_args(p, io.h_s, io.W_s, io.tau, G, io.chunk_V);
+  a.lse_s = io.lse_s;
+  a.dense_a = dense_a;
+  return run_list_chunks(p, a, io.sup_idx, list_val, io.smax, io.W_s, G, WsT, io.chunk_V, io.dh, st);
 }
 
 hipError_t run_copy_rows(const void* src, void* dst, const int32_t* rows, int64_t n_rows, int64_t n_other,

@@ -41,6 +41,7 @@ struct TopkArgs {
   float c2;       // log2(e) / tau
   float inv_tau;
   int n_tok_tiles, n_splits, tiles_per_split, n_vtiles;
+  int swap;        // ps / pt hold the teacher / student pair: rank the student
   float* part;     // [kTopkFields][n_splits][N]
   uint32_t* lists; // [n_splits][N][k] packed words, descending
 };
@@ -83,6 +84,9 @@ constexpr int kTopkWM = 4, kTopkWN = 2, kTopkThreads = 64 * kTopkWM * kTopkWN;
 // ---------------------------------------------------------------------------
 // Sweep: per (token tile, vocabulary split) top-k lists and LSE partials.
 // kSep1: also accumulate the untempered student LSE (tau != 1, for the CE).
+// With swap set, the two operand pairs come in exchanged (the ranked model
+// is then the student) and the LSE partials are written back in the usual
+// field order.
 // ---------------------------------------------------------------------------
 template <bool kSep1>
 __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a) {
@@ -290,10 +294,11 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
       const int64_t n = (int64_t)tt * TN + col;
       if (n < a.N) {
         const int64_t S_ = a.n_splits;
-        a.part[(0 * S_ + sp) * a.N + n] = ms[nb];
-        a.part[(1 * S_ + sp) * a.N + n] = ls[nb];
-        a.part[(2 * S_ + sp) * a.N + n] = mt[nb];
-        a.part[(3 * S_ + sp) * a.N + n] = lt[nb];
+        const int fs = a.swap ? 2 : 0, ft = 2 - fs;  // fields of the student / teacher records
+        a.part[((fs + 0) * S_ + sp) * a.N + n] = ms[nb];
+        a.part[((fs + 1) * S_ + sp) * a.N + n] = ls[nb];
+        a.part[((ft + 0) * S_ + sp) * a.N + n] = mt[nb];
+        a.part[((ft + 1) * S_ + sp) * a.N + n] = lt[nb];
         a.part[(4 * S_ + sp) * a.N + n] = m1[nb];
         a.part[(5 * S_ + sp) * a.N + n] = l1[nb];
       }
@@ -363,6 +368,40 @@ __device__ __forceinline__ float log1mexp_f(float x) {  // log(1 - e^x), x <= 0
 
 constexpr int kMaxSplits = 8;  // vocabularies up to 8 * 65536 entries
 
+// Merge token n's per-split lists (S splits of K words) into its global top-K,
+// one wave: lane j < K receives the j-th entry's vocabulary index (-1 for an
+// empty slot) and its bf16 key value. cw holds S * K words, sel K words (LDS,
+// the wave's own).
+__device__ __forceinline__ void select_topk(const uint32_t* __restrict__ lists, int64_t N, int64_t V, int64_t n,
+                                            int S, int K, unsigned long long* cw, unsigned long long* sel, int lane,
+                                            int32_t& vj, float& val) {
+  // candidates as 64-bit words: key << 32 | (0xFFFFFFFF - vocabulary index); 0 = empty
+  const int C = S * K;
+  for (int i = lane; i < C; i += 64) {
+    const int s = i / K;
+    const uint32_t w = lists[((int64_t)s * N + n) * K + (i - s * K)];
+    const uint32_t vidx = (uint32_t)s * kTopkSplit + (0xFFFFu - (w & 0xFFFFu));
+    cw[i] = w == 0u ? 0ull : ((unsigned long long)(w >> 16) << 32) | (0xFFFFFFFFull - vidx);
+  }
+  if (lane < K) sel[lane] = 0ull;  // slots left empty stay 0 (never read as an index)
+  __builtin_amdgcn_wave_barrier();
+  // rank every candidate against all others (all words are distinct); rank < K is its slot
+  for (int i = lane; i < C; i += 64) {
+    const unsigned long long x = cw[i];
+    int r = 0;
+    for (int j = 0; j < C; ++j) r += cw[j] > x;
+    if (x != 0ull && r < K) sel[r] = x;
+  }
+  __builtin_amdgcn_wave_barrier();
+  const unsigned long long xj = lane < K ? sel[lane] : 0ull;
+  // an empty slot (only possible with fewer than k finite candidates) or a
+  // decoded index outside the vocabulary is never dereferenced
+  const uint32_t vdec = 0xFFFFFFFFu - (uint32_t)(xj & 0xFFFFFFFFull);
+  vj = (xj != 0ull && (int64_t)vdec < V) ? (int32_t)vdec : -1;
+  val = lane < K ? key_to_f32((uint32_t)(xj >> 32)) : 0.f;
+  __builtin_amdgcn_wave_barrier();  // cw and sel may be reused after this
+}
+
 __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
   __shared__ unsigned long long cand[4][kMaxSplits * KD_TOPK_MAX];
   __shared__ unsigned long long sel[4][KD_TOPK_MAX];
@@ -389,33 +428,10 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
   const float Lt = (mt + log2f(lt)) * kLn2;
   const float L1 = a.sep1 ? (m1 + log2f(l1)) * kLn2 : Ls;  // untempered student LSE (tau == 1: the same)
 
-  // candidates as 64-bit words: key << 32 | (0xFFFFFFFF - vocabulary index); 0 = empty
-  const int C = S * K;
-  unsigned long long* cw = cand[wave];
-  for (int i = lane; i < C; i += 64) {
-    const int s = i / K;
-    const uint32_t w = a.lists[((int64_t)s * a.N + n) * K + (i - s * K)];
-    const uint32_t vidx = (uint32_t)s * kTopkSplit + (0xFFFFu - (w & 0xFFFFu));
-    cw[i] = w == 0u ? 0ull : ((unsigned long long)(w >> 16) << 32) | (0xFFFFFFFFull - vidx);
-  }
-  if (lane < K) sel[wave][lane] = 0ull;  // slots left empty stay 0 (never read as an index)
-  __builtin_amdgcn_wave_barrier();
-  // rank every candidate against all others (all words are distinct); rank < K is its slot
-  for (int i = lane; i < C; i += 64) {
-    const unsigned long long x = cw[i];
-    int r = 0;
-    for (int j = 0; j < C; ++j) r += cw[j] > x;
-    if (x != 0ull && r < K) sel[wave][r] = x;
-  }
-  __builtin_amdgcn_wave_barrier();
-
   const bool act = lane < K;
-  const unsigned long long xj = act ? sel[wave][lane] : 0ull;
-  // an empty slot (only possible with fewer than k finite candidates) or a
-  // decoded index outside the vocabulary is never dereferenced
-  const uint32_t vdec = 0xFFFFFFFFu - (uint32_t)(xj & 0xFFFFFFFFull);
-  const int32_t vj = (xj != 0ull && (int64_t)vdec < a.V) ? (int32_t)vdec : -1;
-  const float tj = act ? key_to_f32((uint32_t)(xj >> 32)) : 0.f;
+  int32_t vj;
+  float tj;
+  select_topk(a.lists, a.N, a.V, n, S, K, cand[wave], sel[wave], lane, vj, tj);
   // student bf16 logits at the selected indices: one wave-wide dot product each
   const uint16_t* h = a.h_s + n * a.d_s;
   float sj = 0.f;
@@ -460,6 +476,182 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
     } else if (lane == 0) {
       a.ce[n] = NAN;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tail-bucket divergence (White-box OPD, section 2.4): the beta-divergence of
+// section 2.3 taken over the buckets {each support entry} + {the rest of the
+// vocabulary}. The support is the teacher's top-k, the student's top-k, their
+// union (duplicates removed) and/or the label, in that order. One wave per
+// token: merge the per-split log-sum-exps and lists (one list per ranked
+// model), assemble the support in LDS, fill in each entry's missing logit with
+// an fp32 dot product (rounded to bf16; the ranked model's value is its key),
+// then evaluate the buckets.
+// ---------------------------------------------------------------------------
+constexpr int kSupMax = 2 * KD_TOPK_MAX + 1;
+
+struct TailArgs {
+  const uint16_t *h_s, *W_s, *h_t, *W_t;
+  int64_t N, V;
+  int32_t d_s, d_t;
+  int k, n_splits, support, smax;
+  float beta, inv_tau;
+  const float* part;
+  const uint32_t *lists_t, *lists_s;
+  const int32_t* labels;
+  int32_t* sup_idx;
+  float *sup_t, *sup_s, *loss, *p_mass, *q_mass, *lse_s, *lse_t;
+};
+
+__device__ __forceinline__ float logaddexp_f(float x, float y) {
+  const float m = fmaxf(x, y);
+  return m == kNegInf ? kNegInf : m + log1pf(expf(-fabsf(x - y)));
+}
+
+// Wave-wide natural log-sum-exp of up to three values per lane (-inf = none).
+__device__ __forceinline__ float wave_lse3(float a, float b, float c) {
+  const float m = wave_max(fmaxf(a, fmaxf(b, c)));
+  if (m == kNegInf) return kNegInf;
+  return m + logf(wave_sum(expf(a - m) + expf(b - m) + expf(c - m)));
+}
+
+__global__ __launch_bounds__(256) void tail_merge_kernel(TailArgs a) {
+  __shared__ unsigned long long cand[4][kMaxSplits * KD_TOPK_MAX];
+  __shared__ unsigned long long sel[4][KD_TOPK_MAX];
+  __shared__ int32_t sidx[4][kSupMax];
+  __shared__ float sval_t[4][kSupMax], sval_s[4][kSupMax];
+  __shared__ int32_t sknown[4][kSupMax];  // bit 0: teacher value known, bit 1: student value known
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * 4 + wave;
+  if (n >= a.N) return;  // whole waves only: no block barrier below
+  const int K = a.k, S = a.n_splits;
+  const int64_t SN = (int64_t)S;
+  int32_t* si = sidx[wave];
+  float* st = sval_t[wave];
+  float* ss = sval_s[wave];
+  int32_t* sk = sknown[wave];
+
+  float ms = kNegInf, ls = 0.f, mt = kNegInf, lt = 0.f;
+  for (int s = lane; s < S; s += 64) {
+    merge2(ms, ls, a.part[(0 * SN + s) * a.N + n], a.part[(1 * SN + s) * a.N + n]);
+    merge2(mt, lt, a.part[(2 * SN + s) * a.N + n], a.part[(3 * SN + s) * a.N + n]);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    merge2(ms, ls, __shfl_xor(ms, o), __shfl_xor(ls, o));
+    merge2(mt, lt, __shfl_xor(mt, o), __shfl_xor(lt, o));
+  }
+  const float Ls = (ms + log2f(ls)) * kLn2;  // natural LSE of the tempered bf16 logits
+  const float Lt = (mt + log2f(lt)) * kLn2;
+
+  // 1) the support
+  const unsigned long long below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int cnt = 0;
+  if (a.support & KD_SUPPORT_TEACHER) {
+    int32_t v;
+    float key;
+    select_topk(a.lists_t, a.N, a.V, n, S, K, cand[wave], sel[wave], lane, v, key);
+    const bool ok = lane < K && v >= 0;  // filled slots form a prefix
+    if (ok) {
+      si[lane] = v;
+      st[lane] = key;
+      sk[lane] = 1;
+    }
+    cnt = __popcll(__ballot(ok));
+    __builtin_amdgcn_wave_barrier();
+  }
+  if (a.support & KD_SUPPORT_STUDENT) {
+    int32_t v;
+    float key;
+    select_topk(a.lists_s, a.N, a.V, n, S, K, cand[wave], sel[wave], lane, v, key);
+    bool keep = lane < K && v >= 0;
+    for (int j = 0; j < cnt; ++j) keep = keep && si[j] != v;
+    const unsigned long long m = __ballot(keep);
+    if (keep) {
+      const int pos = cnt + __popcll(m & below);
+      si[pos] = v;
+      ss[pos] = key;
+      sk[pos] = 2;
+    }
+    cnt += __popcll(m);
+    __builtin_amdgcn_wave_barrier();
+  }
+  if ((a.support & KD_SUPPORT_LABEL) && a.labels) {
+    const int32_t y = a.labels[n];
+    if (y >= 0 && y < a.V) {
+      bool found = false;
+      for (int j = lane; j < cnt; j += 64) found = found || si[j] == y;
+      if (__ballot(found) == 0ull) {
+        if (lane == 0) {
+          si[cnt] = y;
+          sk[cnt] = 0;
+        }
+        ++cnt;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // 2) the missing logits (wave-uniform loop: one wave-wide dot product each)
+  const uint16_t* hs = a.h_s + n * a.d_s;
+  const uint16_t* ht = a.h_t + n * a.d_t;
+  for (int i = 0; i < cnt; ++i) {
+    const int32_t v = si[i];
+    const int kn = sk[i];
+    if (!(kn & 1)) {
+      const float z = student_logit(ht, a.W_t, v, a.d_t, lane);
+      if (lane == 0) st[i] = z;
+    }
+    if (!(kn & 2)) {
+      const float z = student_logit(hs, a.W_s, v, a.d_s, lane);
+      if (lane == 0) ss[i] = z;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // 3) bucket log-probabilities: three slots per lane cover 2k + 1 <= 129 entries
+  float lp[3], lq[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int i = lane + 64 * j;
+    const bool ok = i < cnt;
+    lp[j] = ok ? st[i] * a.inv_tau - Lt : kNegInf;
+    lq[j] = ok ? ss[i] * a.inv_tau - Ls : kNegInf;
+  }
+  const float logP = wave_lse3(lp[0], lp[1], lp[2]);
+  const float logQ = wave_lse3(lq[0], lq[1], lq[2]);
+  // tail masses below fp32 resolution are held at 2^-24 (their logs stay finite);
+  // a support that covers the vocabulary leaves no tail bucket
+  const bool tail = (int64_t)cnt < a.V;
+  const float lpT = log1mexp_f(fminf(logP, -5.9604645e-8f));
+  const float lqT = log1mexp_f(fminf(logQ, -5.9604645e-8f));
+  const float beta = a.beta;
+  const float lb = logf(beta), l1b = log1pf(-beta);
+  auto term = [&](float p_, float q_) {  // one bucket's share of the divergence
+    if (beta == 0.f) return expf(p_) * (p_ - q_);
+    if (beta == 1.f) return expf(q_) * (q_ - p_);
+    const float lm = logaddexp_f(lb + p_, l1b + q_);
+    return beta * expf(p_) * (p_ - lm) + (1.f - beta) * expf(q_) * (q_ - lm);
+  };
+  float acc = 0.f;
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+    if (lane + 64 * j < cnt) acc += term(lp[j], lq[j]);
+  acc = wave_sum(acc);
+  if (lane == 0) {
+    a.loss[n] = acc + (tail ? term(lpT, lqT) : 0.f);
+    if (a.p_mass) a.p_mass[n] = tail ? expf(logP) : 1.f;
+    if (a.q_mass) a.q_mass[n] = tail ? expf(logQ) : 1.f;
+    a.lse_s[n] = Ls;
+    a.lse_t[n] = Lt;
+  }
+  // 4) the support rows, padded with index -1 and NaN values
+  for (int i = lane; i < a.smax; i += 64) {
+    const bool ok = i < cnt;
+    a.sup_idx[n * a.smax + i] = ok ? si[i] : -1;
+    a.sup_t[n * a.smax + i] = ok ? st[i] : NAN;
+    a.sup_s[n * a.smax + i] = ok ? ss[i] : NAN;
   }
 }
 
@@ -525,6 +717,88 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   m.lse_t = io.lse_t;
   m.sep1 = sep1;
   hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)((p.N + 3) / 4)), dim3(256), 0, st, m);
+  return hipGetLastError();
+}
+
+int32_t tail_support_slots(int32_t k, int32_t support) {
+  return ((support & KD_SUPPORT_TEACHER) ? k : 0) + ((support & KD_SUPPORT_STUDENT) ? k : 0) +
+         ((support & KD_SUPPORT_LABEL) ? 1 : 0);
+}
+
+size_t tail_workspace_bytes(const Plan& p, int32_t k) {
+  // the LSE partials and one list area per ranked model
+  return topk_workspace_bytes(p, k) + align_up((size_t)((p.V + kTopkSplit - 1) / kTopkSplit) * p.N * k * 4, 256);
+}
+
+hipError_t run_tail(const Plan& p, const TailIO& io, hipStream_t st) {
+  TopkArgs a{};
+  a.ps = PairDesc{static_cast<const char*>(io.W_s), static_cast<const char*>(io.h_s), (int64_t)p.d_s * 2,
+                  (int64_t)p.d_s * 2, p.V, p.N, p.d_s * 2};
+  a.pt = PairDesc{static_cast<const char*>(io.W_t), static_cast<const char*>(io.h_t), (int64_t)p.d_t * 2,
+                  (int64_t)p.d_t * 2, p.V, p.N, p.d_t * 2};
+  a.N = p.N;
+  a.V = p.V;
+  a.d_s = p.d_s;
+  a.k = io.k;
+  a.c2 = kLog2e / io.tau;
+  a.inv_tau = 1.f / io.tau;
+  a.n_tok_tiles = (int)((p.N + kTopkT - 1) / kTopkT);
+  a.n_vtiles = p.n_vtiles;
+  a.tiles_per_split = kTopkSplit / kTileV;
+  a.n_splits = (int)((p.V + kTopkSplit - 1) / kTopkSplit);
+  if (a.n_splits > kMaxSplits) return hipErrorInvalidValue;
+  char* ws = static_cast<char*>(io.workspace);
+  a.part = reinterpret_cast<float*>(ws);
+  const size_t part_bytes = align_up((size_t)kTopkFields * a.n_splits * p.N * sizeof(float), 256);
+  const size_t list_bytes = align_up((size_t)a.n_splits * p.N * io.k * sizeof(uint32_t), 256);
+  uint32_t* lists_t = reinterpret_cast<uint32_t*>(ws + part_bytes);
+  uint32_t* lists_s = reinterpret_cast<uint32_t*>(ws + part_bytes + list_bytes);
+  const dim3 grid(a.n_tok_tiles * a.n_splits);
+  // one sweep per ranked model; both write the same log-sum-exp partials
+  if (io.support & KD_SUPPORT_TEACHER) {
+    a.lists = lists_t;
+    hipLaunchKernelGGL(topk_sweep_kernel<false>, grid, dim3(kTopkThreads), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (io.support & KD_SUPPORT_STUDENT) {  // the same sweep with the models' roles exchanged
+    TopkArgs b = a;
+    b.ps = a.pt;
+    b.pt = a.ps;
+    b.swap = 1;
+    b.lists = lists_s;
+    hipLaunchKernelGGL(topk_sweep_kernel<false>, grid, dim3(kTopkThreads), 0, st, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  TailArgs m{};
+  m.h_s = static_cast<const uint16_t*>(io.h_s);
+  m.W_s = static_cast<const uint16_t*>(io.W_s);
+  m.h_t = static_cast<const uint16_t*>(io.h_t);
+  m.W_t = static_cast<const uint16_t*>(io.W_t);
+  m.N = p.N;
+  m.V = p.V;
+  m.d_s = p.d_s;
+  m.d_t = p.d_t;
+  m.k = io.k;
+  m.n_splits = a.n_splits;
+  m.support = io.support;
+  m.smax = tail_support_slots(io.k, io.support);
+  m.beta = io.beta;
+  m.inv_tau = 1.f / io.tau;
+  m.part = a.part;
+  m.lists_t = lists_t;
+  m.lists_s = lists_s;
+  m.labels = io.labels;
+  m.sup_idx = io.sup_idx;
+  m.sup_t = io.sup_t;
+  m.sup_s = io.sup_s;
+  m.loss = io.loss;
+  m.p_mass = io.p_mass;
+  m.q_mass = io.q_mass;
+  m.lse_s = io.lse_s;
+  m.lse_t = io.lse_t;
+  hipLaunchKernelGGL(tail_merge_kernel, dim3((unsigned)((p.N + 3) / 4)), dim3(256), 0, st, m);
   return hipGetLastError();
 }
 
