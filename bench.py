@@ -13,6 +13,13 @@ of the same workload.
 
 --with-dw adds dL/dW_s to the backward (one more GEMM sweep per chunk); the
 default step is the loss and dL/dh_s.
+
+  python bench.py --path topk|tail [--k K] [--beta B] [--support S] ...
+
+times the top-k paths instead, on the 248k-vocabulary 16k-token top-k
+workload: one step = kd_topk_fwd + kd_topk_bwd (three terms, all weights 1,
+labels given), or kd_tail_fwd + kd_tail_bwd (tail-bucket divergence; the
+support defaults to the beta rule). Their JSON line has no CPU baseline.
 """
 from __future__ import annotations
 
@@ -45,6 +52,10 @@ def parse():
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--path", choices=("kd", "topk", "tail"), default="kd",
+                    help="kd: the full-vocabulary divergence (default); topk / tail: the top-k paths")
+    ap.add_argument("--k", type=int, default=64, help="top-k size for --path topk / tail")
+    ap.add_argument("--support", type=int, default=None, help="KD_SUPPORT_* bits for --path tail")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a "
                          "'--calibrate-copy' run into the traffic record and exit")
@@ -120,6 +131,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU: "
               "no sharding or collectives are built)", file=sys.stderr)
         sys.exit(2)
+    if args.path != "kd":
+        bench_topk(args)
+        return
     import numpy as np
     import torch
 
@@ -255,6 +269,93 @@ def main():
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(w, beta, args.cpu_rows)
     print(json.dumps(out), flush=True)
+
+
+def bench_topk(args):
+    """Top-k three-term or tail-bucket step on the 248k-vocabulary workload."""
+    import numpy as np
+    import torch
+
+    import kdsynth
+    import vocab_chunked_kl_amd as kd
+
+    kd.load_library()
+    torch.cuda.set_device(0)
+    w = kdsynth.make(5)
+    N, V, ds, dt_, tau, k, beta = w.N, w.V, w.d_s, w.d_t, w.tau, args.k, args.beta
+    dev = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in (w.h_s, w.W_s, w.h_t, w.W_t)]
+    lab = torch.from_numpy(w.labels.astype(np.int32)).cuda()
+    stream = torch.cuda.Stream()
+    tail = args.path == "tail"
+    support = args.support if args.support is not None else kd.tail_default_support(k, beta, True)
+    with torch.cuda.stream(stream):
+        if tail:
+            ws_f = torch.empty(kd.workspace_size(kd.KD_OP_TAIL, N, V, ds, dt_, kd.KD_BF16, k=k), dtype=torch.uint8,
+                               device="cuda")
+            ws_b = torch.empty(kd.workspace_size(kd.KD_OP_TAIL_BWD, N, V, ds, ds, kd.KD_BF16, chunk_V=args.chunk_v,
+                                                 k=k), dtype=torch.uint8, device="cuda")
+        else:
+            ws_f = torch.empty(kd.workspace_size(kd.KD_OP_TOPK, N, V, ds, dt_, kd.KD_BF16, k=k), dtype=torch.uint8,
+                               device="cuda")
+            ws_b = torch.empty(kd.workspace_size(kd.KD_OP_TOPK_BWD, N, V, ds, ds, kd.KD_BF16, chunk_V=args.chunk_v,
+                                                 k=k), dtype=torch.uint8, device="cuda")
+        dh = torch.empty(N, ds, dtype=torch.float32, device="cuda")
+        one = torch.ones(N, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        if tail:
+            out = kd.kd_tail_fwd(*dev, k, beta, tau, support, labels=lab, workspace=ws_f, stream=stream)
+        else:
+            out = kd.kd_topk_fwd(*dev, k, tau, labels=lab, workspace=ws_f, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if tail:
+            kd.kd_tail_bwd(dev[0], dev[1], out, k, beta, tau, support, chunk_V=args.chunk_v, workspace=ws_b,
+                           stream=stream, dh=dh)
+        else:
+            kd.kd_topk_bwd(dev[0], dev[1], out, k, tau, labels=lab, grad_binary=one, grad_cond=one, grad_ce=one,
+                           chunk_V=args.chunk_v, workspace=ws_b, stream=stream, dh=dh)
+        return out
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        t0.record(stream)
+        for i in range(args.steps):
+            out = step(evs[i])
+        t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    fwd_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    assert np.isfinite(out["loss" if tail else "binary"].cpu().numpy()).all()
+    sweeps = ((1 if support & kd.KD_SUPPORT_TEACHER else 0) + (1 if support & kd.KD_SUPPORT_STUDENT else 0)) \
+        if tail else 1
+    fwd_flops = sweeps * 2.0 * N * V * (ds + dt_)
+    bwd_flops = 2.0 * N * V * ds * 2  # student recompute + dh GEMM
+    achieved = fwd_flops / (fwd_ms / 1e3) / 1e12
+    what = (f"tail-bucket divergence, k={k}, beta={beta}, support bits {support}" if tail
+            else f"top-k three terms, k={k}, labels, all weights 1")
+    print(json.dumps({
+        "metric": f"tokens/s for {args.path} fwd+bwd, V={V}, N={N}",
+        "value": round(N / (ms_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: N={N}, V={V}, d_s={ds}, d_t={dt_}, tau={tau}, {what}, "
+                               f"chunk_V={args.chunk_v}"},
+        "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(ms_step - fwd_ms, 3),
+        "step_tflops": round((fwd_flops + bwd_flops) / (ms_step / 1e3) / 1e12, 1),
+        "roofline": {"kernel": f"{'tail' if tail else 'topk'} forward (top-k sweep{'s' if sweeps > 1 else ''} "
+                               "+ merge, HIP events around the call)",
+                     "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }), flush=True)
 
 
 def kernel_hash() -> str:
