@@ -29,7 +29,10 @@ namespace kd {
 namespace {
 
 constexpr float kNegInf = -INFINITY;
-constexpr int kTopkSplit = 65536;  // vocabulary entries per split: the in-split index fits 16 bits
+// At most 65536 vocabulary entries per split (the in-split index fits 16
+// bits); the vocabulary is cut into ceil(V / 65536) splits of equal tile
+// counts, so that no split's blocks run much longer than the others.
+constexpr int kTopkSplit = 65536;
 constexpr int kCandCap = 16;       // candidate buffer entries per token per round
 constexpr int kTopkFields = 6;     // m_s, l_s, m_t, l_t, m_1, l_1 (untempered student)
 
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
   block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_splits, tt, sp);
   const int vt0 = sp * a.tiles_per_split;
   const int vt1 = min(vt0 + a.tiles_per_split, a.n_vtiles);
-  const int64_t vbase = (int64_t)sp * kTopkSplit;
+  const int64_t vbase = (int64_t)vt0 * TM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave % WM, wn = wave / WM;
   const int K = a.k;
   const float c2 = a.c2;
@@ -320,7 +323,7 @@ struct MergeArgs {
   const uint16_t *h_s, *W_s;
   int64_t N, V;
   int32_t d_s;
-  int k, n_splits;
+  int k, n_splits, split;  // split: vocabulary entries per split
   float tau, inv_tau;
   const float* part;
   const uint32_t* lists;
@@ -373,14 +376,14 @@ constexpr int kMaxSplits = 8;  // vocabularies up to 8 * 65536 entries
 // empty slot) and its bf16 key value. cw holds S * K words, sel K words (LDS,
 // the wave's own).
 __device__ __forceinline__ void select_topk(const uint32_t* __restrict__ lists, int64_t N, int64_t V, int64_t n,
-                                            int S, int K, unsigned long long* cw, unsigned long long* sel, int lane,
-                                            int32_t& vj, float& val) {
+                                            int S, int K, int split, unsigned long long* cw, unsigned long long* sel,
+                                            int lane, int32_t& vj, float& val) {
   // candidates as 64-bit words: key << 32 | (0xFFFFFFFF - vocabulary index); 0 = empty
   const int C = S * K;
   for (int i = lane; i < C; i += 64) {
     const int s = i / K;
     const uint32_t w = lists[((int64_t)s * N + n) * K + (i - s * K)];
-    const uint32_t vidx = (uint32_t)s * kTopkSplit + (0xFFFFu - (w & 0xFFFFu));
+    const uint32_t vidx = (uint32_t)s * (uint32_t)split + (0xFFFFu - (w & 0xFFFFu));
     cw[i] = w == 0u ? 0ull : ((unsigned long long)(w >> 16) << 32) | (0xFFFFFFFFull - vidx);
   }
   if (lane < K) sel[lane] = 0ull;  // slots left empty stay 0 (never read as an index)
@@ -431,7 +434,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
   const bool act = lane < K;
   int32_t vj;
   float tj;
-  select_topk(a.lists, a.N, a.V, n, S, K, cand[wave], sel[wave], lane, vj, tj);
+  select_topk(a.lists, a.N, a.V, n, S, K, a.split, cand[wave], sel[wave], lane, vj, tj);
   // student bf16 logits at the selected indices: one wave-wide dot product each
   const uint16_t* h = a.h_s + n * a.d_s;
   float sj = 0.f;
@@ -495,7 +498,7 @@ struct TailArgs {
   const uint16_t *h_s, *W_s, *h_t, *W_t;
   int64_t N, V;
   int32_t d_s, d_t;
-  int k, n_splits, support, smax;
+  int k, n_splits, split, support, smax;  // split: vocabulary entries per split
   float beta, inv_tau;
   const float* part;
   const uint32_t *lists_t, *lists_s;
@@ -551,7 +554,7 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(TailArgs a) {
   if (a.support & KD_SUPPORT_TEACHER) {
     int32_t v;
     float key;
-    select_topk(a.lists_t, a.N, a.V, n, S, K, cand[wave], sel[wave], lane, v, key);
+    select_topk(a.lists_t, a.N, a.V, n, S, K, a.split, cand[wave], sel[wave], lane, v, key);
     const bool ok = lane < K && v >= 0;  // filled slots form a prefix
     if (ok) {
       si[lane] = v;
@@ -564,7 +567,7 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(TailArgs a) {
   if (a.support & KD_SUPPORT_STUDENT) {
     int32_t v;
     float key;
-    select_topk(a.lists_s, a.N, a.V, n, S, K, cand[wave], sel[wave], lane, v, key);
+    select_topk(a.lists_s, a.N, a.V, n, S, K, a.split, cand[wave], sel[wave], lane, v, key);
     bool keep = lane < K && v >= 0;
     for (int j = 0; j < cnt; ++j) keep = keep && si[j] != v;
     const unsigned long long m = __ballot(keep);
@@ -677,8 +680,8 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   a.inv_tau = 1.f / io.tau;
   a.n_tok_tiles = (int)((p.N + kTopkT - 1) / kTopkT);
   a.n_vtiles = p.n_vtiles;
-  a.tiles_per_split = kTopkSplit / kTileV;
   a.n_splits = (int)((p.V + kTopkSplit - 1) / kTopkSplit);
+  a.tiles_per_split = (p.n_vtiles + a.n_splits - 1) / a.n_splits;  // <= kTopkSplit / kTileV
   if (a.n_splits > kMaxSplits) return hipErrorInvalidValue;
   a.part = static_cast<float*>(io.workspace);
   a.lists = reinterpret_cast<uint32_t*>(static_cast<char*>(io.workspace) +
@@ -699,6 +702,7 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   m.d_s = p.d_s;
   m.k = io.k;
   m.n_splits = a.n_splits;
+  m.split = a.tiles_per_split * kTileV;
   m.tau = io.tau;
   m.inv_tau = 1.f / io.tau;
   m.part = a.part;
@@ -744,8 +748,8 @@ hipError_t run_tail(const Plan& p, const TailIO& io, hipStream_t st) {
   a.inv_tau = 1.f / io.tau;
   a.n_tok_tiles = (int)((p.N + kTopkT - 1) / kTopkT);
   a.n_vtiles = p.n_vtiles;
-  a.tiles_per_split = kTopkSplit / kTileV;
   a.n_splits = (int)((p.V + kTopkSplit - 1) / kTopkSplit);
+  a.tiles_per_split = (p.n_vtiles + a.n_splits - 1) / a.n_splits;  // <= kTopkSplit / kTileV
   if (a.n_splits > kMaxSplits) return hipErrorInvalidValue;
   char* ws = static_cast<char*>(io.workspace);
   a.part = reinterpret_cast<float*>(ws);
@@ -782,6 +786,7 @@ hipError_t run_tail(const Plan& p, const TailIO& io, hipStream_t st) {
   m.d_t = p.d_t;
   m.k = io.k;
   m.n_splits = a.n_splits;
+  m.split = a.tiles_per_split * kTileV;
   m.support = io.support;
   m.smax = tail_support_slots(io.k, io.support);
   m.beta = io.beta;
