@@ -1,11 +1,9 @@
 // kd_device.hpp - device building blocks shared by the gfx950 kernels.
 //
-// One workgroup = 256 threads = 4 wave64s arranged 2 x 2 over a TM x TN output
-// tile of C = A * B^T, where A [rows, K] and B [rows, K] are both row-major
-// with K contiguous (an "NT" contraction: logits z = W h^T, or dh = G W_s^T
-// with W_s transposed per chunk). K is staged through LDS 128 bytes at a time
-// (64 bf16 or 32 fp32 per row), double buffered: the global loads of stage
-// i+1 are in flight while the MFMAs consume stage i.
+// The MFMA kernels compute tiles of C = A * B^T where A [rows, K] and B
+// [rows, K] are both row-major with K contiguous (an "NT" contraction: logits
+// z = W h^T, or dh = G W_s^T with the chunk of W_s transposed); the
+// pipelined tile loop itself lives in kd_sweep.hpp.
 //
 // MFMA lane layouts (v_mfma_f32_32x32x16_bf16 / v_mfma_f32_32x32x2_f32), as
 // checked on the device:  A operand: lane l holds row (l & 31), k-slice
@@ -36,6 +34,44 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// Wave64 reductions (every lane receives the result).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// log(1 - e^x) for x < 0, in the two-branch form that stays accurate near 0
+// (expm1) and far from it (log1p).
+__device__ __forceinline__ float log1mexp_f32(float x) {
+  return x > -0.69314718f ? logf(-expm1f(x)) : log1pf(-expf(x));
+}
+
+// h . W[v] for bf16 rows of d elements (d a multiple of 8, rows 16-byte
+// aligned), computed by the whole wave: lane-strided fp32 partial sums, then a
+// wave sum; the result is rounded to bf16 and returned as fp32.
+__device__ __forceinline__ float wave_dot_bf16(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                                               int64_t v, int32_t d, int lane) {
+  const uint16_t* w = W + v * d;
+  float acc = 0.f;
+  for (int i = lane * 8; i < d; i += 64 * 8) {
+    const u32x4 hv = *reinterpret_cast<const u32x4*>(h + i);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(w + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t hx = hv[e], wx = wv[e];
+      acc = fmaf(__builtin_bit_cast(float, hx << 16), __builtin_bit_cast(float, wx << 16), acc);
+      acc = fmaf(__builtin_bit_cast(float, hx & 0xFFFF0000u), __builtin_bit_cast(float, wx & 0xFFFF0000u), acc);
+    }
+  }
+  return __builtin_bit_cast(float, f32_to_bf16_bits(wave_sum(acc)) << 16);
 }
 
 // --------------------------------------------------------------------------

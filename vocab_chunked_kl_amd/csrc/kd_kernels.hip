@@ -584,36 +584,6 @@ __global__ __launch_bounds__(256) void g_fix_kernel(FixArgs f) {
   *reinterpret_cast<uint16_t*>(f.G + n * f.ldg + (v - f.c0) * 2) = (uint16_t)f32_to_bf16_bits(f.val[i]);
 }
 
-__device__ __forceinline__ float wsum64(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ float wmax64(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-// Student logit for vocabulary row v, fp32 dot product by the whole wave
-// (lane-strided partial sums, then a wave sum), rounded to bf16.
-__device__ __forceinline__ float wave_dot_bf16(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int64_t v,
-                                               int32_t d, int lane) {
-  const uint16_t* w = W + v * d;
-  float acc = 0.f;
-  for (int i = lane * 8; i < d; i += 64 * 8) {
-    const u32x4 hv = *reinterpret_cast<const u32x4*>(h + i);
-    const u32x4 wv = *reinterpret_cast<const u32x4*>(w + i);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t hx = hv[e], wx = wv[e];
-      acc = fmaf(__builtin_bit_cast(float, hx << 16), __builtin_bit_cast(float, wx << 16), acc);
-      acc = fmaf(__builtin_bit_cast(float, hx & 0xFFFF0000u), __builtin_bit_cast(float, wx & 0xFFFF0000u), acc);
-    }
-  }
-  return __builtin_bit_cast(float, f32_to_bf16_bits(wsum64(acc)) << 16);
-}
-
 // Three top-k terms. With Q / P the student / teacher mass on the set K, p^
 // the renormalised teacher on K, B = -P/Q + (1-P)/(1-Q) (0 when k == V):
 //   A = -w_b B Q / tau,  C = w_ce (when a label and its weight are given)
@@ -644,9 +614,9 @@ __global__ __launch_bounds__(256) void topk_coef_kernel(TopkCoefArgs a) {
   const bool ok = act && v >= 0 && v < a.V;
   // renormalised teacher on the set, from its bf16 values
   const float t = ok ? a.val_t[n * K + lane] * a.inv_tau : -INFINITY;
-  const float mt = wmax64(t);
+  const float mt = wave_max(t);
   const float et = ok ? expf(t - mt) : 0.f;
-  const float ph = et / wsum64(et);
+  const float ph = et / wave_sum(et);
   const float P = a.p_mass[n], Q = a.q_mass[n];
   const float B = (int64_t)K >= a.V ? 0.f : -P / Q + (1.f - P) / (1.f - Q);
   const float wb = a.gb ? a.gb[n] : 0.f, wc = a.gc ? a.gc[n] : 0.f;
@@ -694,10 +664,6 @@ struct TailCoefArgs {
   float *dense_a, *list_val;  // [N], [N, smax]
 };
 
-__device__ __forceinline__ float log1mexp_f32(float x) {  // log(1 - e^x), x < 0
-  return x > -0.69314718f ? logf(-expm1f(x)) : log1pf(-expf(x));
-}
-
 __global__ __launch_bounds__(256) void tail_coef_kernel(TailCoefArgs a) {
   constexpr int kSlots = 3;  // 2 * 64 + 1 support entries at most: three per lane
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -716,16 +682,16 @@ __global__ __launch_bounds__(256) void tail_coef_kernel(TailCoefArgs a) {
     lq[j] = okj[j] ? a.sup_s[n * a.smax + i] * a.inv_tau - Ls : -INFINITY;
     cnt_l += okj[j];
   }
-  const int cnt = (int)wsum64((float)cnt_l);
-  const float mp = wmax64(fmaxf(lp[0], fmaxf(lp[1], lp[2])));
-  const float mq = wmax64(fmaxf(lq[0], fmaxf(lq[1], lq[2])));
+  const int cnt = (int)wave_sum((float)cnt_l);
+  const float mp = wave_max(fmaxf(lp[0], fmaxf(lp[1], lp[2])));
+  const float mq = wave_max(fmaxf(lq[0], fmaxf(lq[1], lq[2])));
   float ep = 0.f, eq = 0.f;
 #pragma unroll
   for (int j = 0; j < kSlots; ++j) {
     ep += okj[j] ? expf(lp[j] - mp) : 0.f;
     eq += okj[j] ? expf(lq[j] - mq) : 0.f;
   }
-  const float logP = mp + logf(wsum64(ep)), logQ = mq + logf(wsum64(eq));
+  const float logP = mp + logf(wave_sum(ep)), logQ = mq + logf(wave_sum(eq));
   // the forward's tail convention: masses below fp32 resolution held at 2^-24
   const bool tail = (int64_t)cnt < a.V;
   const float lpT = log1mexp_f32(fminf(logP, -5.9604645e-8f));
@@ -748,7 +714,7 @@ __global__ __launch_bounds__(256) void tail_coef_kernel(TailCoefArgs a) {
     qa[j] = !okj[j] ? 0.f : beta == 0.f ? -expf(lp[j]) : q[j] * a_of(lp[j], lq[j]);
     csum += qa[j];
   }
-  const float c = wsum64(csum) + qT * aT;
+  const float c = wave_sum(csum) + qT * aT;
   const float w = (a.grad ? a.grad[n] : 1.f) * a.inv_tau;
   if (lane == 0) a.dense_a[n] = (aT - c) * w;
 #pragma unroll

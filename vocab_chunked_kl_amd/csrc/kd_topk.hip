@@ -14,7 +14,8 @@
 // ordered by one 32-bit word: (order-preserving bf16 key << 16) | (0xFFFF -
 // index within the split), i.e. key descending, then index ascending. Only
 // values above the token's current k-th word enter a small candidate buffer;
-// buffers are merged into the state by ranking (count of larger entries).
+// after each tile the buffers are merged into the running lists by a bitonic
+// sort in registers.
 //
 // Merge kernel (one wave per token): merge the per-split log-sum-exps and
 // top-k lists, recompute the student logits at the selected indices and at
@@ -333,42 +334,6 @@ struct MergeArgs {
   int sep1;
 };
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __builtin_bit_cast(float, (uint32_t)b << 16); }
-
-// Student logit for vocabulary row v (fp32 accumulation, rounded to bf16),
-// computed by the whole wave: lane-strided partial dot, then a wave sum.
-__device__ __forceinline__ float student_logit(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W, int64_t v,
-                                               int32_t d, int lane) {
-  const uint16_t* w = W + v * d;
-  float acc = 0.f;
-  for (int i = lane * 8; i < d; i += 64 * 8) {
-    const u32x4 hv = *reinterpret_cast<const u32x4*>(h + i);
-    const u32x4 wv = *reinterpret_cast<const u32x4*>(w + i);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t hx = hv[e], wx = wv[e];
-      acc = fmaf(__builtin_bit_cast(float, hx << 16), __builtin_bit_cast(float, wx << 16), acc);
-      acc = fmaf(__builtin_bit_cast(float, hx & 0xFFFF0000u), __builtin_bit_cast(float, wx & 0xFFFF0000u), acc);
-    }
-  }
-  return round_bf16(wave_sum(acc));
-}
-
-__device__ __forceinline__ float log1mexp_f(float x) {  // log(1 - e^x), x <= 0
-  return x > -0.69314718f ? logf(-expm1f(x)) : log1pf(-expf(x));
-}
-
 constexpr int kMaxSplits = 8;  // vocabularies up to 8 * 65536 entries
 
 // Merge token n's per-split lists (S splits of K words) into its global top-K,
@@ -440,7 +405,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
   float sj = 0.f;
   for (int j = 0; j < K; ++j) {
     const int32_t v = __shfl(vj, j);  // wave-uniform
-    const float zsv = v >= 0 ? student_logit(h, a.W_s, v, a.d_s, lane) : kNegInf;
+    const float zsv = v >= 0 ? wave_dot_bf16(h, a.W_s, v, a.d_s, lane) : kNegInf;
     if (lane == j) sj = zsv;
   }
   if (act) {
@@ -461,7 +426,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
   const float condv = wave_sum(cterm);
   if (lane == 0) {
     const float P = expf(logP), Q = expf(logQ);
-    const float l1P = log1mexp_f(logP), l1Q = log1mexp_f(logQ);
+    const float l1P = log1mexp_f32(logP), l1Q = log1mexp_f32(logQ);
     const float tail = (1.f - P) * (l1P - l1Q);
     a.binary[n] = all ? 0.f : P * (logP - logQ) + tail;
     a.cond[n] = condv;
@@ -474,7 +439,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
   if (a.labels) {
     const int32_t y = a.labels[n];
     if (y >= 0 && y < a.V) {
-      const float zy = student_logit(h, a.W_s, y, a.d_s, lane);
+      const float zy = wave_dot_bf16(h, a.W_s, y, a.d_s, lane);
       if (lane == 0) a.ce[n] = L1 - zy;
     } else if (lane == 0) {
       a.ce[n] = NAN;
@@ -603,11 +568,11 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(TailArgs a) {
     const int32_t v = si[i];
     const int kn = sk[i];
     if (!(kn & 1)) {
-      const float z = student_logit(ht, a.W_t, v, a.d_t, lane);
+      const float z = wave_dot_bf16(ht, a.W_t, v, a.d_t, lane);
       if (lane == 0) st[i] = z;
     }
     if (!(kn & 2)) {
-      const float z = student_logit(hs, a.W_s, v, a.d_s, lane);
+      const float z = wave_dot_bf16(hs, a.W_s, v, a.d_s, lane);
       if (lane == 0) ss[i] = z;
     }
   }
@@ -627,8 +592,8 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(TailArgs a) {
   // tail masses below fp32 resolution are held at 2^-24 (their logs stay finite);
   // a support that covers the vocabulary leaves no tail bucket
   const bool tail = (int64_t)cnt < a.V;
-  const float lpT = log1mexp_f(fminf(logP, -5.9604645e-8f));
-  const float lqT = log1mexp_f(fminf(logQ, -5.9604645e-8f));
+  const float lpT = log1mexp_f32(fminf(logP, -5.9604645e-8f));
+  const float lqT = log1mexp_f32(fminf(logQ, -5.9604645e-8f));
   const float beta = a.beta;
   const float lb = logf(beta), l1b = log1pf(-beta);
   auto term = [&](float p_, float q_) {  // one bucket's share of the divergence
