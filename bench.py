@@ -19,7 +19,7 @@ default step is the loss and dL/dh_s.
 times the top-k paths instead, on the 248k-vocabulary 16k-token top-k
 workload: one step = kd_topk_fwd + kd_topk_bwd (three terms, all weights 1,
 labels given), or kd_tail_fwd + kd_tail_bwd (tail-bucket divergence; the
-support defaults to the beta rule). Their JSON line has no CPU baseline.
+support defaults to the beta rule); their CPU baseline is the oracle on 48 tokens.
 """
 from __future__ import annotations
 
@@ -48,7 +48,8 @@ def parse():
     ap.add_argument("--with-dw", action="store_true",
                     help="also compute dL/dW_s in the backward (the step then runs three GEMM sweeps)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="tokens in the CPU oracle sample (default 1024; 48 for the top-k paths)")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -100,17 +101,35 @@ def summarize_traffic(fetch_csv, write_csv, out_path):
     print(json.dumps(rec))
 
 
-def cpu_baseline(w, beta, rows_n):
+def cpu_baseline(w, beta, rows_n, path="kd", with_dw=False, k=64, support=None):
     """The fp64 oracle (as it stands) on a bounded row sample of the same
-    workload: forward loss plus dL/dh_s for ``rows_n`` tokens."""
+    workload and the same step: for the full-vocabulary path the forward loss
+    plus dL/dh_s (and dL/dW_s's share of the sampled rows with ``with_dw``);
+    for the top-k paths their forward and backward."""
     import numpy as np
 
     import kdsynth
     from oracle import kd_oracle as O
     rows = kdsynth.sample_rows(w.N, rows_n, seed=99)
+    hs, ht = w.h_s[rows], w.h_t[rows]
     t0 = time.perf_counter()
-    O.kd_fwd(w.h_s[rows], w.W_s, w.h_t[rows], w.W_t, beta, w.tau)
-    O.kd_bwd(w.h_s[rows], w.W_s, w.h_t[rows], w.W_t, beta, w.tau)
+    if path == "kd":
+        O.kd_fwd(hs, w.W_s, ht, w.W_t, beta, w.tau)
+        O.kd_bwd(hs, w.W_s, ht, w.W_t, beta, w.tau)
+        if with_dw:
+            O.kd_bwd_w(hs, w.W_s, ht, w.W_t, beta, w.tau)
+        what = "fwd loss + dL/dh_s" + (" + dL/dW_s" if with_dw else "")
+    elif path == "topk":
+        lab = w.labels[rows]
+        one = np.ones(len(rows))
+        out = O.kd_topk_fwd(hs, w.W_s, ht, w.W_t, k, w.tau, labels=lab)
+        O.kd_topk_bwd(hs, w.W_s, ht, w.W_t, k, w.tau, lab, one, one, one, sel=out["idx"])
+        what = f"top-{k} three terms + their dL/dh_s"
+    else:
+        lab = w.labels[rows]
+        out = O.kd_tail_fwd(hs, w.W_s, ht, w.W_t, k, beta, w.tau, support=support, labels=lab)
+        O.kd_tail_bwd(hs, w.W_s, ht, w.W_t, k, beta, w.tau, sup=out["sup"])
+        what = f"tail-bucket divergence (k={k}, beta={beta}) + its dL/dh_s"
     dt = time.perf_counter() - t0
     try:
         from threadpoolctl import threadpool_info
@@ -118,8 +137,7 @@ def cpu_baseline(w, beta, rows_n):
     except Exception:  # pragma: no cover
         threads = len(os.sched_getaffinity(0))
     return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} of {w.N} tokens of the same workload (fwd loss + dL/dh_s, fp64 numpy/BLAS), "
-                      f"{dt:.1f} s"}
+            "sample": f"{len(rows)} of {w.N} tokens of the same workload ({what}, fp64 numpy/BLAS), {dt:.1f} s"}
 
 
 def main():
@@ -131,6 +149,8 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path is single-GPU: "
               "no sharding or collectives are built)", file=sys.stderr)
         sys.exit(2)
+    if args.cpu_rows is None:
+        args.cpu_rows = 1024 if args.path == "kd" else 48
     if args.path != "kd":
         bench_topk(args)
         return
@@ -267,7 +287,7 @@ def main():
     if not args.no_cpu:
         del dev
         torch.cuda.empty_cache()
-        out["cpu_baseline"] = cpu_baseline(w, beta, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(w, beta, args.cpu_rows, with_dw=args.with_dw)
     print(json.dumps(out), flush=True)
 
 
@@ -342,7 +362,7 @@ def bench_topk(args):
     achieved = fwd_flops / (fwd_ms / 1e3) / 1e12
     what = (f"tail-bucket divergence, k={k}, beta={beta}, support bits {support}" if tail
             else f"top-k three terms, k={k}, labels, all weights 1")
-    print(json.dumps({
+    res = {
         "metric": f"tokens/s for {args.path} fwd+bwd, V={V}, N={N}",
         "value": round(N / (ms_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
@@ -355,7 +375,12 @@ def bench_topk(args):
                                "+ merge, HIP events around the call)",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
-    }), flush=True)
+    }
+    if not args.no_cpu:
+        del dev
+        torch.cuda.empty_cache()
+        res["cpu_baseline"] = cpu_baseline(w, beta, args.cpu_rows, path=args.path, k=k, support=support)
+    print(json.dumps(res), flush=True)
 
 
 def kernel_hash() -> str:
