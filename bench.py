@@ -355,9 +355,7 @@ def bench_topk(args):
     ms_step = t0.elapsed_time(t1) / args.steps
     fwd_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     assert np.isfinite(out["loss" if tail else "binary"].cpu().numpy()).all()
-    sweeps = ((1 if support & kd.KD_SUPPORT_TEACHER else 0) + (1 if support & kd.KD_SUPPORT_STUDENT else 0)) \
-        if tail else 1
-    fwd_flops = sweeps * 2.0 * N * V * (ds + dt_)
+    fwd_flops = 2.0 * N * V * (ds + dt_)  # one top-k sweep (it ranks one model or both)
     bwd_flops = 2.0 * N * V * ds * 2  # student recompute + dh GEMM
     achieved = fwd_flops / (fwd_ms / 1e3) / 1e12
     what = (f"tail-bucket divergence, k={k}, beta={beta}, support bits {support}" if tail
@@ -371,8 +369,8 @@ def bench_topk(args):
                                f"chunk_V={args.chunk_v}"},
         "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(ms_step - fwd_ms, 3),
         "step_tflops": round((fwd_flops + bwd_flops) / (ms_step / 1e3) / 1e12, 1),
-        "roofline": {"kernel": f"{'tail' if tail else 'topk'} forward (top-k sweep{'s' if sweeps > 1 else ''} "
-                               "+ merge, HIP events around the call)",
+        "roofline": {"kernel": f"{'tail' if tail else 'topk'} forward (top-k sweep + merge, HIP events around "
+                               "the call)",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None},
     }

@@ -259,8 +259,8 @@ kd_status kd_topk_bwd(const void* h_s, const void* W_s, int64_t N, int64_t V, in
  *   loss, lse_s, lse_t (device, [N] fp32, written); lse_* over the tempered
  *            bf16 logits. p_mass, q_mass (device, [N] fp32, written; may be
  *            NULL): sum_S p and sum_S q.
- *   workspace (device, >= kd_workspace_size(KD_OP_TAIL, ...) bytes). Each
- *            ranked model costs one sweep over the vocabulary.
+ *   workspace (device, >= kd_workspace_size(KD_OP_TAIL, ...) bytes). One
+ *            sweep over the vocabulary ranks one model or both.
  */
 kd_status kd_tail_fwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
                       int32_t d_s, int32_t d_t, int32_t k, int32_t support, float beta, float tau, kd_dtype dtype,

@@ -34,7 +34,8 @@ constexpr float kNegInf = -INFINITY;
 // bits); the vocabulary is cut into ceil(V / 65536) splits of equal tile
 // counts, so that no split's blocks run much longer than the others.
 constexpr int kTopkSplit = 65536;
-constexpr int kCandCap = 16;       // candidate buffer entries per token per round
+constexpr int kCandCap = 16;       // candidate buffer entries per token per round (one list)
+constexpr int kCandCap2 = 12;      // the same with two lists (both models ranked at once)
 constexpr int kTopkFields = 6;     // m_s, l_s, m_t, l_t, m_1, l_1 (untempered student)
 
 struct TopkArgs {
@@ -48,6 +49,7 @@ struct TopkArgs {
   int swap;        // ps / pt hold the teacher / student pair: rank the student
   float* part;     // [kTopkFields][n_splits][N]
   uint32_t* lists; // [n_splits][N][k] packed words, descending
+  uint32_t* lists2;  // with two lists: the student-ranked one, same layout
 };
 
 // Round to bf16 (nearest, ties to even) and return the rounded value as fp32.
@@ -84,26 +86,30 @@ __device__ __forceinline__ void merge2(float& m, float& l, float m2, float l2) {
 
 // Wave grid of the top-k sweep: 4 vocabulary slices x 2 token halves.
 constexpr int kTopkWM = 4, kTopkWN = 2, kTopkThreads = 64 * kTopkWM * kTopkWN;
+typedef uint32_t u32x16 __attribute__((__vector_size__(16 * sizeof(uint32_t))));
 
 // ---------------------------------------------------------------------------
 // Sweep: per (token tile, vocabulary split) top-k lists and LSE partials.
 // kSep1: also accumulate the untempered student LSE (tau != 1, for the CE).
 // With swap set, the two operand pairs come in exchanged (the ranked model
 // is then the student) and the LSE partials are written back in the usual
-// field order.
+// field order. kTwo: rank both models at once, the teacher into lists and
+// the student into lists2 (smaller candidate buffers, more merge rounds).
 // ---------------------------------------------------------------------------
-template <bool kSep1>
+template <bool kSep1, bool kTwo>
 __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a) {
   constexpr int TM = kTileV, TN = kTopkT, WM = kTopkWM, WN = kTopkWN, NW = WM * WN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
+  constexpr int NL = kTwo ? 2 : 1;                // lists: 0 teacher-ranked, 1 student-ranked
+  constexpr int CAP = kTwo ? kCandCap2 : kCandCap;
   // LDS: a three-stage ring, the candidate buffers and per-token counters.
   // The running top-k lists live in the per-split output rows of the
   // workspace (each token's row is read and written only by the wave that
   // merges it), which leaves LDS room for the third ring stage.
   KD_RING3_LDS(TM, TN);
-  __shared__ uint32_t B[TN][kCandCap];     // candidate buffer
-  __shared__ int cntS[TN], cntB[TN];
-  __shared__ uint32_t theta[TN];           // k-th word once full, else 0
+  __shared__ uint32_t B[NL][TN][CAP];      // candidate buffers
+  __shared__ int cntS[NL][TN], cntB[NL][TN];
+  __shared__ uint32_t theta[NL][TN];       // k-th word once full, else 0
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
@@ -115,10 +121,10 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
   const int K = a.k;
   const float c2 = a.c2;
 
-  for (int t = tid; t < TN; t += kTopkThreads) {
-    cntS[t] = 0;
-    cntB[t] = 0;
-    theta[t] = 0u;
+  for (int i = tid; i < NL * TN; i += kTopkThreads) {
+    cntS[i / TN][i % TN] = 0;
+    cntB[i / TN][i % TN] = 0;
+    theta[i / TN][i % TN] = 0u;
   }
   __syncthreads();
 
@@ -134,14 +140,14 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
   // are sorted descending by a bitonic network in registers (words are
   // distinct and nonzero, so the zeros sink), and the first min(total, k)
   // become the new state
-  auto merge_token = [&](int t) {
-    const int cs = cntS[t];
-    const int cb = min(cntB[t], kCandCap);
+  auto merge_token = [&](int li, int t) {
+    const int cs = cntS[li][t];
+    const int cb = min(cntB[li][t], CAP);
     const int total = cs + cb;
-    uint32_t* Sg = a.lists + ((int64_t)sp * a.N + (int64_t)tt * TN + t) * K;  // token < N (see below)
-    uint32_t e0 = lane < cs ? Sg[lane] : (lane - cs < cb ? B[t][lane - cs] : 0u);
+    uint32_t* Sg = (li ? a.lists2 : a.lists) + ((int64_t)sp * a.N + (int64_t)tt * TN + t) * K;  // token < N
+    uint32_t e0 = lane < cs ? Sg[lane] : (lane - cs < cb ? B[li][t][lane - cs] : 0u);
     const int j1 = lane + 64;
-    uint32_t e1 = j1 - cs < cb ? B[t][j1 - cs] : 0u;  // cs <= 64 <= j1
+    uint32_t e1 = j1 - cs < cb ? B[li][t][j1 - cs] : 0u;  // cs <= 64 <= j1
 #pragma unroll
     for (int k = 2; k <= 128; k <<= 1) {
 #pragma unroll
@@ -164,9 +170,9 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
     if (lane < K) Sg[lane] = lane < ns ? e0 : 0u;  // the row stays fully defined
     const uint32_t th = __shfl(e0, K - 1);
     if (lane == 0) {
-      cntS[t] = ns;
-      cntB[t] = 0;
-      theta[t] = ns == K ? th : 0u;
+      cntS[li][t] = ns;
+      cntB[li][t] = 0;
+      theta[li][t] = ns == K ? th : 0u;
     }
   };
 
@@ -217,43 +223,71 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
         m1[nb] = m1_new;
       }
     }
+    // with two lists, both 16-bit keys are packed into the teacher's registers
+    // (teacher key high, student key low; whole-vector bit casts), so that the
+    // student's accumulators are free during the candidate rounds
+    if constexpr (kTwo) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          u32x16 kv;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) kv[r] = (bf16_key(zt[mb][nb][r]) << 16) | bf16_key(zs[mb][nb][r]);
+          zt[mb][nb] = __builtin_bit_cast(floatx16, kv);
+        }
+    }
     // 3) top-k candidates: rounds until no token's buffer overflowed
     constexpr int kDoneWords = (MB * 16 + 31) / 32;
-    uint32_t done[NB][kDoneWords];
+    uint32_t done[NL][NB][kDoneWords];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
+    for (int li = 0; li < NL; ++li)
 #pragma unroll
-      for (int i = 0; i < kDoneWords; ++i) done[nb][i] = 0u;
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int i = 0; i < kDoneWords; ++i) done[li][nb][i] = 0u;
     const int rel0 = (int)(vrow0 - vbase);
     while (true) {
       int ov = 0;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int col = wn * (TN / WN) + nb * 32 + (lane & 31);
-        const uint32_t th = theta[col];
         const bool tok_ok = (int64_t)tt * TN + col < a.N;  // tokens past N have no list row
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int li = 0; li < NL; ++li) {
+          const uint32_t th = theta[li][col];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int bit = mb * 16 + r;
-            const int rel = rel0 + mb * 32 + acc_row(r, lane);
-            const bool ok = full || (vbase + rel < a.V);
-            const uint32_t w = (bf16_key(zt[mb][nb][r]) << 16) | (0xFFFFu - (uint32_t)rel);
-            if (ok && tok_ok && w > th && !((done[nb][bit >> 5] >> (bit & 31)) & 1u)) {
-              const int slot = atomicAdd(&cntB[col], 1);
-              if (slot < kCandCap) {
-                B[col][slot] = w;
-                done[nb][bit >> 5] |= 1u << (bit & 31);
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int bit = mb * 16 + r;
+              const int rel = rel0 + mb * 32 + acc_row(r, lane);
+              const bool ok = full || (vbase + rel < a.V);
+              uint32_t key;
+              if constexpr (kTwo) {
+                const uint32_t both = __builtin_bit_cast(u32x16, zt[mb][nb])[r];
+                key = li ? (both & 0xFFFFu) : (both >> 16);
               } else {
-                ov = 1;
+                key = bf16_key(zt[mb][nb][r]);
+              }
+              const uint32_t w = (key << 16) | (0xFFFFu - (uint32_t)rel);
+              if (ok && tok_ok && w > th && !((done[li][nb][bit >> 5] >> (bit & 31)) & 1u)) {
+                const int slot = atomicAdd(&cntB[li][col], 1);
+                if (slot < CAP) {
+                  B[li][col][slot] = w;
+                  done[li][nb][bit >> 5] |= 1u << (bit & 31);
+                } else {
+                  ov = 1;
+                }
               }
             }
-          }
+        }
       }
       const int any = __syncthreads_or(ov);
       for (int t = wave; t < TN; t += NW)
-        if (cntB[t] > 0) merge_token(t);
+#pragma unroll
+        for (int li = 0; li < NL; ++li)
+          if (cntB[li][t] > 0) merge_token(li, t);
       __syncthreads();
       if (!any) break;
     }
@@ -310,11 +344,13 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
   }
   // the lists are in place; a token that never received a candidate (only
   // possible for a split with no valid entry) gets a row of empty words
-  for (int i = tid; i < TN * K; i += kTopkThreads) {
-    const int t = i / K, j = i - t * K;
-    const int64_t n = (int64_t)tt * TN + t;
-    if (n < a.N && cntS[t] == 0) a.lists[((int64_t)sp * a.N + n) * K + j] = 0u;
-  }
+#pragma unroll
+  for (int li = 0; li < NL; ++li)
+    for (int i = tid; i < TN * K; i += kTopkThreads) {
+      const int t = i / K, j = i - t * K;
+      const int64_t n = (int64_t)tt * TN + t;
+      if (n < a.N && cntS[li][t] == 0) (li ? a.lists2 : a.lists)[((int64_t)sp * a.N + n) * K + j] = 0u;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -654,9 +690,9 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   const bool sep1 = (io.labels != nullptr || io.lse_s1 != nullptr) && io.tau != 1.f;
   const dim3 grid(a.n_tok_tiles * a.n_splits);
   if (sep1)
-    hipLaunchKernelGGL(topk_sweep_kernel<true>, grid, dim3(kTopkThreads), 0, st, a);
+    hipLaunchKernelGGL((topk_sweep_kernel<true, false>), grid, dim3(kTopkThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(topk_sweep_kernel<false>, grid, dim3(kTopkThreads), 0, st, a);
+    hipLaunchKernelGGL((topk_sweep_kernel<false, false>), grid, dim3(kTopkThreads), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MergeArgs m{};
@@ -723,23 +759,26 @@ hipError_t run_tail(const Plan& p, const TailIO& io, hipStream_t st) {
   uint32_t* lists_t = reinterpret_cast<uint32_t*>(ws + part_bytes);
   uint32_t* lists_s = reinterpret_cast<uint32_t*>(ws + part_bytes + list_bytes);
   const dim3 grid(a.n_tok_tiles * a.n_splits);
-  // one sweep per ranked model; both write the same log-sum-exp partials
-  if (io.support & KD_SUPPORT_TEACHER) {
+  // one sweep: the teacher's list, the student's (the same sweep with the
+  // two operand pairs exchanged) or both at once
+  const bool rank_t = io.support & KD_SUPPORT_TEACHER, rank_s = io.support & KD_SUPPORT_STUDENT;
+  if (rank_t && rank_s) {
     a.lists = lists_t;
-    hipLaunchKernelGGL(topk_sweep_kernel<false>, grid, dim3(kTopkThreads), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (io.support & KD_SUPPORT_STUDENT) {  // the same sweep with the models' roles exchanged
+    a.lists2 = lists_s;
+    hipLaunchKernelGGL((topk_sweep_kernel<false, true>), grid, dim3(kTopkThreads), 0, st, a);
+  } else if (rank_t) {
+    a.lists = lists_t;
+    hipLaunchKernelGGL((topk_sweep_kernel<false, false>), grid, dim3(kTopkThreads), 0, st, a);
+  } else {
     TopkArgs b = a;
     b.ps = a.pt;
     b.pt = a.ps;
     b.swap = 1;
     b.lists = lists_s;
-    hipLaunchKernelGGL(topk_sweep_kernel<false>, grid, dim3(kTopkThreads), 0, st, b);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((topk_sweep_kernel<false, false>), grid, dim3(kTopkThreads), 0, st, b);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   TailArgs m{};
   m.h_s = static_cast<const uint16_t*>(io.h_s);
   m.W_s = static_cast<const uint16_t*>(io.W_s);
