@@ -397,22 +397,35 @@ class _Unrows(torch.autograd.Function):
         return kd_gather_rows(g.contiguous(), rows), None, None
 
 
+def _no_tokens(xs, xt, ws, wt, lead, reduction):
+    """The value of a loss over zero tokens (or zero kept tokens): 0, still
+    attached to the inputs; per-token zeros for reduction="none"."""
+    for name, t in (("xs", xs), ("xt", xt), ("ws", ws), ("wt", wt)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    zero = (xs.sum() + xt.sum() + ws.sum() + wt.sum()).float() * 0.0
+    if reduction == "none":
+        return (torch.zeros(lead, device=xs.device) + zero)
+    if reduction not in ("sum", "mean"):
+        raise ValueError(f"unknown reduction {reduction!r}")
+    return zero
+
+
 def _divergence(xs, xt, ws, wt, beta, temperature, reduction, chunk_V, labels, ignore_index):
     d_s, d_t = xs.shape[-1], xt.shape[-1]
     lead = xs.shape[:-1]
     xs2 = xs.reshape(-1, d_s).contiguous()
     xt2 = xt.reshape(-1, d_t).contiguous()
+    if xs2.shape[0] == 0:
+        return _no_tokens(xs, xt, ws, wt, lead, reduction)
     rows = None
     if labels is not None:
         valid = labels.reshape(-1) != ignore_index
         if not bool(valid.all()):
             # only the tokens that carry a loss are computed ([Top-K KD] 二.4)
             rows = torch.nonzero(valid).reshape(-1).to(torch.int32)
-            if rows.numel() == 0:  # nothing carries a loss: zero, still attached to the inputs
-                zero = (xs2.sum() + xt2.sum() + ws.sum() + wt.sum()).float() * 0.0
-                if reduction == "none":
-                    return (torch.zeros(xs2.shape[0], device=xs.device) + zero).reshape(lead)
-                return zero
+            if rows.numel() == 0:  # nothing carries a loss
+                return _no_tokens(xs, xt, ws, wt, lead, reduction)
             xs2, xt2 = _Rows.apply(xs2, rows), _Rows.apply(xt2, rows)
     per_tok = _KD.apply(xs2, ws.contiguous(), xt2, wt.contiguous(), float(beta), float(temperature), int(chunk_V))
     count = torch.tensor(float(per_tok.numel()), device=per_tok.device)
@@ -515,6 +528,9 @@ def tail_kd(xs, xt, ws, wt, k=1, beta=0.0, labels=None, temperature=1.0, support
     ``return_dict`` also returns the forward's per-token dict."""
     d_s, d_t = xs.shape[-1], xt.shape[-1]
     lead = xs.shape[:-1]
+    if xs.reshape(-1, d_s).shape[0] == 0:
+        res = _no_tokens(xs, xt, ws, wt, lead, reduction)
+        return (res, {}) if return_dict else res
     lab = None
     valid = None
     if labels is not None:
