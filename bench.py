@@ -12,7 +12,8 @@ of the same workload.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--chunk-v C] [--beta B] [--with-dw] [--no-cpu]
 
 --with-dw adds dL/dW_s to the backward (one more GEMM sweep per chunk); the
-default step is the loss and dL/dh_s.
+default step is the loss and dL/dh_s. --workload 2 or 4 runs the same step on
+the 152k-vocabulary 4k-token or the 248k-vocabulary heavy-head workload.
 
   python bench.py --path topk|tail [--k K] [--beta B] [--support S] ...
 
@@ -53,6 +54,8 @@ def parse():
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic.json"))
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    ap.add_argument("--workload", type=int, choices=(2, 3, 4), default=WORKLOAD,
+                    help="the full-vocabulary workload (3: the headline; 2 and 4: the other bf16 shapes)")
     ap.add_argument("--path", choices=("kd", "topk", "tail"), default="kd",
                     help="kd: the full-vocabulary divergence (default); topk / tail: the top-k paths")
     ap.add_argument("--k", type=int, default=64, help="top-k size for --path topk / tail")
@@ -150,7 +153,7 @@ def main():
               "no sharding or collectives are built)", file=sys.stderr)
         sys.exit(2)
     if args.cpu_rows is None:
-        args.cpu_rows = 1024 if args.path == "kd" else 48
+        args.cpu_rows = (256 if args.workload == 4 else 1024) if args.path == "kd" else 48
     if args.path != "kd":
         bench_topk(args)
         return
@@ -165,7 +168,7 @@ def main():
 
     kd.load_library()
     torch.cuda.set_device(0)
-    w = kdsynth.make(WORKLOAD)
+    w = kdsynth.make(args.workload)
     N, V, ds, dt_, tau, beta = w.N, w.V, w.d_s, w.d_t, w.tau, args.beta
     dev = [to_dev(x) for x in (w.h_s, w.W_s, w.h_t, w.W_t)]
     stream = torch.cuda.Stream()
@@ -221,7 +224,7 @@ def main():
     # the other points of the beta sweep of this workload, one warm step then two timed steps each
     # (reported beside the headline step, which is the configured beta)
     sweep_ms = {}
-    for b in (0.0, 0.5, 1.0):
+    for b in w.betas:
         bws_b = kd.workspace_size(bop, N, V, ds, dt_, kd.KD_BF16, beta=b, chunk_V=args.chunk_v)
         fws_b = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt_, kd.KD_BF16, beta=b)
         if bws_b > ws_b.numel() or fws_b > ws_f.numel():
@@ -257,7 +260,8 @@ def main():
         except Exception:
             traffic = None
     out = {
-        "metric": "tokens/s + MFMA % of peak for fused chunked KL fwd+bwd, V=151936, N=32k",
+        "metric": ("tokens/s + MFMA % of peak for fused chunked KL fwd+bwd, V=151936, N=32k" if args.workload == 3
+                   else f"tokens/s + MFMA % of peak for fused chunked KL fwd+bwd, V={V}, N={N}"),
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -269,10 +273,10 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: N={N} tokens (B=4 x T=8192), V={V}, d_s={ds}, d_t={dt_}, "
+        "config": {"workload": f"{w.name}: N={N} tokens, V={V}, d_s={ds}, d_t={dt_}, "
                                f"beta={beta}, tau={tau}, fwd+bwd (dL/dh_s{', dL/dW_s' if args.with_dw else ''}), "
                                f"chunk_V={args.chunk_v}",
-                   "global_batch": N, "seq_len": 8192, "parallelism": "single GPU"},
+                   "global_batch": N, "parallelism": "single GPU"},
         "mfma_frac_step": round(step_flops / (ms_step / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "step_tflops": round(step_flops / (ms_step / 1e3) / 1e12, 1),
         "fwd_ms": round(fwd_ms, 3),
