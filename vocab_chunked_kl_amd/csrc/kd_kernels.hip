@@ -19,7 +19,12 @@
 // Backward (Nitrobrew notes, "仓库实现": recompute per vocabulary block
 // instead of storing logits): per vocabulary chunk, recompute the tile logits,
 // form g = dloss/ds scaled by grad/tau and store it as bf16 [N, chunk]; then
-// dh_s += G . W_s[chunk] with W_s[chunk] transposed once per chunk.
+// dh_s += G . W_s[chunk] with W_s[chunk] transposed once per chunk, and, when
+// asked, dW_s[chunk] = G^T . h_s from a transposed copy of the same tile.
+//
+// Also here: the backward of the top-k style losses (a per-token coefficient
+// kernel, a student-only recompute sweep and a fix-up of the listed entries
+// before the same dh GEMM) and the row gather / scatter of token masking.
 //
 // All exponentials and logarithms are base 2 (v_exp_f32 / v_log_f32) on
 // logits prescaled by log2(e)/tau; the per-token results are converted back
