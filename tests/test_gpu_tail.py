@@ -99,23 +99,35 @@ def test_tail_workload_v248k_sampled(beta, support):
 
 
 def test_tail_kd_autograd_matches_direct_call():
+    """tail_kd (kept rows gathered, per-token mean, autograd) against direct
+    calls on every row with the mean's weights; ignored rows get a zero
+    gradient and their own values do not enter the loss."""
     kd, torch = _kd()
     N, V, ds, dt = 96, 3000, 64, 64
     arrays = kdsynth.small_case(44, N, V, ds, dt)
     labels = kdsynth.uniform_labels(9, N, V, ignore_frac=0.1)
     dev = [to_dev(x) for x in arrays]
     lab = torch.from_numpy(labels.astype(np.int64)).cuda()
+    lab32 = lab.to(torch.int32)
+    valid = (lab != -100).float()
+    assert 0 < int(valid.sum()) < N
     for k, beta in ((1, 0.5), (16, 0.5), (16, 1.0)):
         xs = dev[0].clone().requires_grad_(True)
         loss, fwd = kd.tail_kd(xs, dev[2], dev[1], dev[3], k=k, beta=beta, labels=lab, temperature=1.3,
                                chunk_V=1024, return_dict=True)
         loss.backward()
+        assert fwd["loss"].numel() == int(valid.sum())  # only the kept rows were computed
         support = kd.tail_default_support(k, beta, True)
-        valid = (lab != -100).float()
-        direct = kd.kd_tail_bwd(dev[0], dev[1], fwd, k, beta, 1.3, support,
+        full = kd.kd_tail_fwd(*dev, k, beta, 1.3, support, labels=lab32)
+        direct = kd.kd_tail_bwd(dev[0], dev[1], full, k, beta, 1.3, support,
                                 grad_loss=(valid / valid.sum()).contiguous(), chunk_V=1024)
         torch.cuda.synchronize()
-        per_tok = fwd["loss"] * valid
+        kept = valid.bool()
+        assert torch.equal(fwd["loss"], full["loss"][kept])  # the same arithmetic per kept row
         lv = float(loss.detach())
-        assert abs(lv - float(per_tok.sum() / valid.sum())) <= 1e-5 * max(1.0, abs(lv))
+        assert abs(lv - float((full["loss"] * valid).sum() / valid.sum())) <= 1e-5 * max(1.0, abs(lv))
+        assert torch.all(xs.grad[~kept] == 0)
         assert torch.allclose(xs.grad.float(), direct.to(torch.bfloat16).float(), rtol=1e-2, atol=1e-4)
+        none = kd.tail_kd(dev[0], dev[2], dev[1], dev[3], k=k, beta=beta, labels=lab, temperature=1.3,
+                          reduction="none")
+        assert torch.equal(none[kept], full["loss"][kept]) and torch.all(none[~kept] == 0)

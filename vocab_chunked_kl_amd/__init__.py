@@ -524,34 +524,43 @@ def tail_kd(xs, xt, ws, wt, k=1, beta=0.0, labels=None, temperature=1.0, support
     """Beta-divergence over a top-k support plus a tail bucket (ars-opd-rebuild
     "03 · 层 2：White-box OPD 基线", section 2.4), per-token mean over
     non-ignored labels by default. ``support`` defaults to
-    ``tail_default_support(k, beta, labels is not None)``. With
-    ``return_dict`` also returns the forward's per-token dict."""
+    ``tail_default_support(k, beta, labels is not None)``. Tokens whose label
+    is ignored are gathered out before the sweep ([Top-K KD] 二.4) and count
+    as 0. With ``return_dict`` also returns the forward's per-token dict (over
+    the computed rows: all tokens, or the kept ones when some are ignored)."""
     d_s, d_t = xs.shape[-1], xt.shape[-1]
     lead = xs.shape[:-1]
-    if xs.reshape(-1, d_s).shape[0] == 0:
+    xs2 = xs.reshape(-1, d_s).contiguous()
+    xt2 = xt.reshape(-1, d_t).contiguous()
+    if xs2.shape[0] == 0:
         res = _no_tokens(xs, xt, ws, wt, lead, reduction)
         return (res, {}) if return_dict else res
     lab = None
-    valid = None
+    rows = None
     if labels is not None:
         lab = labels.reshape(-1).to(torch.int32).contiguous()
         valid = lab != ignore_index
-        lab = torch.where(valid, lab, torch.full_like(lab, -100))
+        if not bool(valid.all()):
+            rows = torch.nonzero(valid).reshape(-1).to(torch.int32)
+            if rows.numel() == 0:
+                res = _no_tokens(xs, xt, ws, wt, lead, reduction)
+                return (res, {}) if return_dict else res
+            xs2, xt2 = _Rows.apply(xs2, rows), _Rows.apply(xt2, rows)
+            lab = lab.index_select(0, rows.long()).contiguous()
     if support is None:
         support = tail_default_support(int(k), float(beta), lab is not None)
     holder = {}
-    per_tok = _Tail.apply(xs.reshape(-1, d_s).contiguous(), ws.contiguous(), xt.reshape(-1, d_t).contiguous(),
-                          wt.contiguous(), int(k), float(beta), float(temperature), int(support),
-                          lab if support & KD_SUPPORT_LABEL else None, int(chunk_V), holder)
-    if valid is not None:
-        per_tok = torch.where(valid, per_tok, torch.zeros_like(per_tok))
+    per_tok = _Tail.apply(xs2, ws.contiguous(), xt2, wt.contiguous(), int(k), float(beta), float(temperature),
+                          int(support), lab if support & KD_SUPPORT_LABEL else None, int(chunk_V), holder)
+    count = torch.tensor(float(per_tok.numel()), device=per_tok.device)
     if reduction == "none":
+        if rows is not None:  # back to one value per position, 0 where ignored
+            per_tok = _Unrows.apply(per_tok.reshape(-1, 1).contiguous(), rows, xs.reshape(-1, d_s).shape[0])
         res = per_tok.reshape(lead)
     elif reduction == "sum":
         res = per_tok.sum()
     elif reduction == "mean":
-        count = valid.sum() if valid is not None else torch.tensor(per_tok.numel(), device=per_tok.device)
-        res = per_tok.sum() / count.float().clamp_min(1.0)
+        res = per_tok.sum() / count.clamp_min(1.0)
     else:
         raise ValueError(f"unknown reduction {reduction!r}")
     return (res, holder) if return_dict else res
