@@ -131,3 +131,29 @@ def test_tail_kd_autograd_matches_direct_call():
         none = kd.tail_kd(dev[0], dev[2], dev[1], dev[3], k=k, beta=beta, labels=lab, temperature=1.3,
                           reduction="none")
         assert torch.equal(none[kept], full["loss"][kept]) and torch.all(none[~kept] == 0)
+
+
+@pytest.mark.parametrize("k,beta,support", [(1, 0.5, T | L), (8, 0.5, T | S | L), (8, 1.0, S | L)])
+def test_tail_label_already_in_the_support(k, beta, support):
+    """Labels set to the teacher's or the student's top-1 on some rows: the
+    support lists them once (no extra label slot used)."""
+    kd, torch = _kd()
+    N, V, ds, dt = 64, 2000, 64, 64
+    arrays = kdsynth.small_case(45, N, V, ds, dt)
+    zs = O.bf16_round(O.logits(arrays[0], arrays[1]))
+    zt = O.bf16_round(O.logits(arrays[2], arrays[3]))
+    labels = kdsynth.uniform_labels(10, N, V, ignore_frac=0.1)
+    labels[::2] = O.topk_order(zt, 1)[::2, 0]
+    labels[1::4] = O.topk_order(zs, 1)[1::4, 0]
+    print(f"tail label in support k={k} beta={beta} support={support}", flush=True)
+    out, exact = _case(kd, torch, arrays, k, beta, 1.0, support, labels, np.arange(N), grad_seed=55)
+    assert exact >= 0.9 * N
+    sup = out["sup_idx"].cpu().numpy()
+    ranked = (k if support & T else 0) + (k if support & S else 0)
+    inside = list(range(0, N, 2)) if support & T else list(range(1, N, 4))  # label = a ranked top-1
+    for r in inside:  # listed once, by its model's list; the label slot stays free
+        assert np.sum(sup[r] == labels[r]) == 1
+        assert sup[r, ranked] == -1 or sup[r, ranked] != labels[r]
+    for r in range(N):
+        if labels[r] >= 0:
+            assert np.sum(sup[r] == labels[r]) == 1
