@@ -56,6 +56,9 @@ def parse():
                     help="also run a plain 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--workload", type=int, choices=(2, 3, 4), default=WORKLOAD,
                     help="the full-vocabulary workload (3: the headline; 2 and 4: the other bf16 shapes)")
+    ap.add_argument("--small-n", action="store_true",
+                    help="time kd_fwd alone on the 4k-token workload's shapes at N = 64 .. 1024 tokens, where the "
+                         "sweep streams W from HBM, against the HBM roofline")
     ap.add_argument("--path", choices=("kd", "topk", "tail"), default="kd",
                     help="kd: the full-vocabulary divergence (default); topk / tail: the top-k paths")
     ap.add_argument("--k", type=int, default=64, help="top-k size for --path topk / tail")
@@ -154,6 +157,9 @@ def main():
         sys.exit(2)
     if args.cpu_rows is None:
         args.cpu_rows = (256 if args.workload == 4 else 1024) if args.path == "kd" else 48
+    if args.small_n:
+        bench_small_n(args)
+        return
     if args.path != "kd":
         bench_topk(args)
         return
@@ -293,6 +299,57 @@ def main():
         torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(w, beta, args.cpu_rows, with_dw=args.with_dw)
     print(json.dumps(out), flush=True)
+
+
+def bench_small_n(args):
+    """kd_fwd (reverse KL) on the 4k-token workload's shapes (V = 151936, d_s = 1024,
+    d_t = 2560) at N = 64 .. 1024 tokens: the sweep reads both unembeddings once
+    (1.09 GB) and does 2 N V (d_s + d_t) flops, so below ~315 tokens it is
+    bound by HBM. Median of ``steps`` timed calls per N (HIP events on the
+    call's stream)."""
+    import numpy as np
+    import torch
+
+    import kdsynth
+    import vocab_chunked_kl_amd as kd
+
+    kd.load_library()
+    torch.cuda.set_device(0)
+    w = kdsynth.make(2)
+    dev = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in (w.h_s, w.W_s, w.h_t, w.W_t)]
+    stream = torch.cuda.Stream()
+    w_bytes = 2.0 * w.V * (w.d_s + w.d_t)
+    points = []
+    for n in (64, 128, 256, 512, 1024):
+        hs, ht = dev[0][:n].contiguous(), dev[2][:n].contiguous()
+        ws = torch.empty(kd.workspace_size(kd.KD_OP_FWD, n, w.V, w.d_s, w.d_t, kd.KD_BF16, beta=1.0),
+                         dtype=torch.uint8, device="cuda")
+        with torch.cuda.stream(stream):
+            for _ in range(args.warmup):
+                kd.kd_fwd(hs, dev[1], ht, dev[3], 1.0, w.tau, workspace=ws, stream=stream)
+            times = []
+            for _ in range(args.steps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                kd.kd_fwd(hs, dev[1], ht, dev[3], 1.0, w.tau, workspace=ws, stream=stream)
+                e1.record(stream)
+                times.append((e0, e1))
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in times]))
+        gbs = (w_bytes + 2.0 * n * (w.d_s + w.d_t)) / (ms / 1e3) / 1e9
+        points.append({"N": n, "ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                       "TFLOP/s": round(2.0 * n * w.V * (w.d_s + w.d_t) / (ms / 1e3) / 1e12, 1)})
+    first = points[0]
+    print(json.dumps({
+        "metric": f"kd_fwd time at small N, V={w.V}, d_s={w.d_s}, d_t={w.d_t}", "value": first["ms"], "unit": "ms",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False, "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name} shapes, N in {[p['N'] for p in points]}, reverse KL, tau={w.tau}"},
+        "points": points,
+        "roofline": {"kernel": "fwd_kernel + merge at N = 64 (HIP events around kd_fwd)", "bound": "hbm",
+                     "achieved": first["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": first["hbm_frac"],
+                     "traffic": None},
+    }), flush=True)
 
 
 def bench_topk(args):

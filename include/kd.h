@@ -91,7 +91,7 @@ typedef enum {
  *   The backward's workspace is O(N * chunk_V) (the gradient tile G of one
  *   vocabulary chunk, in the input dtype) plus O(chunk_V * d_s) for one
  *   transposed chunk of W_s; KD_OP_BWD_W adds a transposed copy of G and of
- *   h_s (O(N * chunk_V + N * d_s)). The forward's is O(N * V / 2048) floats
+ *   h_s (O(N * chunk_V + N * d_s)). The forward's is O(N * V / 1024) floats
  *   of partial statistics. Writes the size to *bytes (host pointer). Pure
  *   host function.
  */

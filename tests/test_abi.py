@@ -51,8 +51,8 @@ def test_workspace_sizes():
     f1 = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt, kd.KD_BF16, beta=1.0)
     f5 = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt, kd.KD_BF16, beta=0.5)
     # forward: one partial record (5 floats; +2 for the JSD sums) per token per
-    # 2048-entry vocabulary slice
-    S = -(-(-(-V // 256)) // 8)
+    # 1024-entry vocabulary slice
+    S = -(-(-(-V // 256)) // 4)
     al = lambda x: -(-x // 256) * 256  # noqa: E731
     assert f1 == al(5 * S * N * 4) and f5 == f1 + al(2 * S * N * 4)
     with pytest.raises(kd.KDError):
