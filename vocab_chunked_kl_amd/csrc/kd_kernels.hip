@@ -272,7 +272,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Cross-split merge: one thread per token.
+// Cross-split merge: one thread per token, slices in a fixed order.
 // ---------------------------------------------------------------------------
 template <int MODE>
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part, int n_splits, int64_t N,
@@ -283,6 +283,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   const int64_t S = n_splits;
   if constexpr (MODE == kModeJSD) {
     float sl = 0.f, sx = 0.f;
+#pragma unroll 8
     for (int s = 0; s < n_splits; ++s) {
       sl += part[(0 * S + s) * N + n];
       sx += part[(1 * S + s) * N + n];
@@ -291,6 +292,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     if (aux) aux[n] = sx * kLn2;
   } else {
     float ms = kNegInf, ls = 0.f, mt = kNegInf, lt = 0.f, ac = 0.f;
+    // unrolled so that the loads of several slices are in flight at once (the
+    // merges themselves form a chain)
+#pragma unroll 8
     for (int s = 0; s < n_splits; ++s)
       merge_record<MODE>(ms, ls, mt, lt, ac, part[(0 * S + s) * N + n], part[(1 * S + s) * N + n],
                          part[(2 * S + s) * N + n], part[(3 * S + s) * N + n], part[(4 * S + s) * N + n]);
