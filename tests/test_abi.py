@@ -55,6 +55,16 @@ def test_workspace_sizes():
     S = -(-(-(-V // 256)) // 4)
     al = lambda x: -(-x // 256) * 256  # noqa: E731
     assert f1 == al(5 * S * N * 4) and f5 == f1 + al(2 * S * N * 4)
+    # up to 4 token tiles: the slice width minimising (waves of workgroups on 256 CUs) x (tiles + 1.5);
+    # from 5 token tiles on, 4 tiles
+    tiles = -(-V // 256)
+    for n, want_tps in ((64, 3), (256, 5), (512, 5), (640, 4), (1024, 4)):
+        T = -(-n // 128)
+        if T <= 4:
+            cost = {t: (-(-(T * -(-tiles // t)) // 256)) * (t + 1.5) for t in range(1, 9)}
+            assert min(cost, key=lambda t: (cost[t], t)) == want_tps
+        S_n = -(-tiles // want_tps)
+        assert kd.workspace_size(kd.KD_OP_FWD, n, V, ds, dt, kd.KD_BF16, beta=1.0) == al(5 * S_n * n * 4), n
     with pytest.raises(kd.KDError):
         kd.workspace_size(kd.KD_OP_BWD, N, V, ds, dt, kd.KD_BF16, chunk_V=1000)
     with pytest.raises(kd.KDError):

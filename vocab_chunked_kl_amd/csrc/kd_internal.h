@@ -38,11 +38,11 @@ constexpr int kDhBuf = 2;
 #define KD_TOK_GROUP 8
 #endif
 constexpr int kTokGroup = KD_TOK_GROUP;
-// Vocabulary tiles per forward workgroup (1024 vocabulary entries): blocks
-// that run together finish together, which keeps their shared operand rows
-// in L2; each writes one partial record per token. Measured against 1, 2 and
-// 8: equal at 32k tokens, best or near best from 64 to 4096 tokens, where
-// the sweep has few token tiles and streams W from HBM.
+// Vocabulary tiles per forward workgroup (1024 vocabulary entries; chosen per
+// shape for up to 4 token tiles, see make_plan): blocks that run together
+// finish together, which keeps their shared operand rows in L2; each writes
+// one partial record per token. Measured against 1 to 8: equal to 8 at 32k
+// tokens, at or near the best at 1024 to 4096 tokens.
 #ifndef KD_FWD_TILES_PER_BLOCK
 #define KD_FWD_TILES_PER_BLOCK 4
 #endif

@@ -818,7 +818,23 @@ Plan make_plan(int64_t N, int64_t V, int32_t d_s, int32_t d_t, bool bf16) {
   p.esz = bf16 ? 2 : 4;
   p.n_tok_tiles = (int)((N + kTileT - 1) / kTileT);
   p.n_vtiles = (int)((V + kTileV - 1) / kTileV);
-  p.tiles_per_split = kFwdTilesPerBlock < p.n_vtiles ? kFwdTilesPerBlock : p.n_vtiles;
+  int tps = kFwdTilesPerBlock;
+  if (p.n_tok_tiles <= 4) {
+    // few token tiles: the forward streams W from HBM and its time is about
+    // (waves of workgroups over the 256 CUs) x (tiles per workgroup + the
+    // fixed cost of one, ~1.5 tiles); pick the tiles per workgroup that
+    // minimise it (the measured best at 64..512 tokens)
+    double best = 1e30;
+    for (int t = 1; t <= 8; ++t) {
+      const int64_t blocks = (int64_t)p.n_tok_tiles * ((p.n_vtiles + t - 1) / t);
+      const double cost = (double)((blocks + 255) / 256) * (t + 1.5);
+      if (cost < best) {
+        best = cost;
+        tps = t;
+      }
+    }
+  }
+  p.tiles_per_split = tps < p.n_vtiles ? tps : p.n_vtiles;
   p.n_splits = (p.n_vtiles + p.tiles_per_split - 1) / p.tiles_per_split;
   return p;
 }
