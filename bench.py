@@ -337,8 +337,20 @@ def bench_small_n(args):
         torch.cuda.synchronize()
         ms = float(np.median([a.elapsed_time(b) for a, b in times]))
         gbs = (w_bytes + 2.0 * n * (w.d_s + w.d_t)) / (ms / 1e3) / 1e9
+        # the backward at the same N (beside the forward line; chunk_V as given)
+        loss, lse_s, lse_t, aux = kd.kd_fwd(hs, dev[1], ht, dev[3], 1.0, w.tau)
+        dh = torch.empty(n, w.d_s, dtype=torch.float32, device="cuda")
+        kd.kd_bwd(hs, dev[1], ht, dev[3], 1.0, w.tau, lse_s, lse_t, aux, chunk_V=args.chunk_v, dh=dh)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            kd.kd_bwd(hs, dev[1], ht, dev[3], 1.0, w.tau, lse_s, lse_t, aux, chunk_V=args.chunk_v, dh=dh)
+        e1.record()
+        torch.cuda.synchronize()
         points.append({"N": n, "ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
-                       "TFLOP/s": round(2.0 * n * w.V * (w.d_s + w.d_t) / (ms / 1e3) / 1e12, 1)})
+                       "TFLOP/s": round(2.0 * n * w.V * (w.d_s + w.d_t) / (ms / 1e3) / 1e12, 1),
+                       "bwd_ms": round(e0.elapsed_time(e1) / 5, 4)})
     first = points[0]
     print(json.dumps({
         "metric": f"kd_fwd time at small N, V={w.V}, d_s={w.d_s}, d_t={w.d_t}", "value": first["ms"], "unit": "ms",

@@ -65,6 +65,13 @@ def test_workspace_sizes():
             assert min(cost, key=lambda t: (cost[t], t)) == want_tps
         S_n = -(-tiles // want_tps)
         assert kd.workspace_size(kd.KD_OP_FWD, n, V, ds, dt, kd.KD_BF16, beta=1.0) == al(5 * S_n * n * 4), n
+    # few tokens: the dh GEMM splits its contraction into s = min(ceil(256 / output tiles), chunk_V / 512)
+    # partial tiles of N x d_s fp32 (output tiles of 256 x 256; none from 128 tiles on)
+    for n, d, cv, s in ((64, 1024, 16384, 32), (4096, 1024, 16384, 4), (300, 64, 2048, 4), (64, 1024, 256, 1),
+                        (32768, 2560, 16384, 1)):
+        base = al(n * cv * 2) + al(d * cv * 2)
+        want = base + (al(s * n * d * 4) if s > 1 else 0)
+        assert kd.workspace_size(kd.KD_OP_BWD, n, V, d, dt, kd.KD_BF16, chunk_V=cv) == want, (n, d, cv)
     with pytest.raises(kd.KDError):
         kd.workspace_size(kd.KD_OP_BWD, N, V, ds, dt, kd.KD_BF16, chunk_V=1000)
     with pytest.raises(kd.KDError):

@@ -305,3 +305,35 @@ def test_all_tokens_masked():
     assert float(m) == 0.0 and float(xs.grad.float().abs().sum()) == 0.0
     n = kd.reverse_kl(dev[0], dev[2], dev[1], dev[3], labels=lab, reduction="none")
     assert n.shape == (64,) and float(n.abs().sum()) == 0.0
+
+
+@pytest.mark.parametrize("beta", [1.0, 0.5])
+def test_split_contraction_backward(beta):
+    """Few tokens: the dh GEMM splits its contraction over the chunk into up to
+    32 partial tiles summed in a fixed order (chunk_V = 16384 -> 32 splits of
+    512 entries; 4096 -> 8; 256 -> none). Every split count matches the oracle."""
+    kd, torch = _kd()
+    N, V, ds, dt = 200, 20000, 96, 64
+    arrays = kdsynth.small_case(71, N, V, ds, dt)
+    grad = np.random.default_rng(8).uniform(-1, 2, size=N)
+    for chunk in (16384, 4096, 256):
+        _say(f"split dh N={N} V={V} chunk={chunk} beta={beta}")
+        run_case(kd, torch, arrays, beta, 1.3, grad=grad, chunk_V=chunk)
+
+
+def test_split_contraction_topk_backward():
+    kd, torch = _kd()
+    N, V, ds, dt = 150, 30000, 64, 64
+    arrays = kdsynth.small_case(72, N, V, ds, dt)
+    labels = kdsynth.uniform_labels(13, N, V, ignore_frac=0.2)
+    dev = [to_dev(x) for x in arrays]
+    lab = torch.from_numpy(labels.astype(np.int32)).cuda()
+    rng = np.random.default_rng(14)
+    wb, wc, we = (rng.uniform(0, 1.5, N) for _ in range(3))
+    f32 = lambda a: torch.from_numpy(a.astype(np.float32)).cuda()  # noqa: E731
+    out = kd.kd_topk_fwd(*dev, 16, 1.2, labels=lab)
+    dh = kd.kd_topk_bwd(dev[0], dev[1], out, 16, 1.2, labels=lab, grad_binary=f32(wb), grad_cond=f32(wc),
+                        grad_ce=f32(we), chunk_V=16384)
+    torch.cuda.synchronize()
+    ref = O.kd_topk_bwd(*arrays, 16, 1.2, labels, wb, wc, we, sel=out["idx"].cpu().numpy())
+    assert_grad_rows(dh.cpu().numpy(), ref, name="topk dh_s (split)")

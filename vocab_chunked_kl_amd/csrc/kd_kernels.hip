@@ -443,6 +443,12 @@ struct DhArgs {
   int n_tok_tiles, n_d_tiles;
   float* dh;         // output
   int first;         // 1: overwrite, 0: accumulate
+  // split contraction (few output tiles): split ks of n_ksplit covers
+  // bytes [ks * kspan, (ks + 1) * kspan) of K and writes its own partial
+  // tile to part + ks * N * d_s; dh_reduce_kernel then sums the partials
+  int n_ksplit;      // 1: no split
+  int32_t kspan;
+  float* part;
 };
 
 template <bool kBf16>
@@ -450,10 +456,23 @@ __global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
   constexpr int TM = kTileDhT, TN = kTileDhD, WM = kDhWM, WN = kDhWN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
   KD_RING_LDS_N(TM, TN, kDhRB, kDhBuf);
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int L0 = xcd_remap(blockIdx.x, gridDim.x);
+  const int per_split = a.n_tok_tiles * a.n_d_tiles;
+  const int ks = L0 / per_split;  // 0 unless the contraction is split
   int tt, dt;
-  block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_d_tiles, tt, dt);
+  block_coords<kTokGroup>(L0 - ks * per_split, a.n_tok_tiles, a.n_d_tiles, tt, dt);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave % WM, wn = wave / WM;
+  PairDesc pd = a.p;
+  float* out = a.dh;
+  int first = a.first;
+  if (a.n_ksplit > 1) {
+    const int32_t k0 = ks * a.kspan;  // < kbytes: the host sizes the splits
+    pd.A += k0;
+    pd.B += k0;
+    pd.kbytes = min(a.kspan, a.p.kbytes - k0);
+    out = a.part + (int64_t)ks * a.N * a.d_s;
+    first = 1;
+  }
   // Read-modify-write of dh, one 32-row slice at a time: all loads of the
   // slice are issued before its stores, so they overlap instead of forming a
   // chain of dependent round trips.
@@ -467,13 +486,13 @@ __global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
       for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) old[nb][r] = 0.f;
-      if (!a.first) {
+      if (!first) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int64_t n = n0 + acc_row(r, lane), d = d0 + nb * 32;
-            if (n < a.N && d < a.d_s) old[nb][r] = a.dh[n * a.d_s + d];
+            if (n < a.N && d < a.d_s) old[nb][r] = out[n * a.d_s + d];
           }
       }
 #pragma unroll
@@ -481,11 +500,21 @@ __global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t n = n0 + acc_row(r, lane), d = d0 + nb * 32;
-          if (n < a.N && d < a.d_s) a.dh[n * a.d_s + d] = old[nb][r] + acc[mb][nb][r];
+          if (n < a.N && d < a.d_s) out[n * a.d_s + d] = old[nb][r] + acc[mb][nb][r];
         }
     }
   };
-  sweep<kBf16, TM, TN, WM, WN, kDhBuf, kDhRB, false>(a.p, a.p, (int64_t)dt * TN, tt, tt + 1, lds, epi);
+  sweep<kBf16, TM, TN, WM, WN, kDhBuf, kDhRB, false>(pd, pd, (int64_t)dt * TN, tt, tt + 1, lds, epi);
+}
+
+// dh (=|+=) the sum of the split contraction's partial tiles, in split order.
+__global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict__ part, int n_split, int64_t count,
+                                                        float* __restrict__ dh, int first) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
+    float v = 0.f;
+    for (int s = 0; s < n_split; ++s) v += part[s * count + i];
+    dh[i] = first ? v : dh[i] + v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -848,13 +877,64 @@ size_t fwd_workspace_bytes(const Plan& p, bool jsd) {
 // weight-gradient GEMM, zero-padded.
 int64_t padded_tokens(const Plan& p) { return (p.N + kTileT - 1) / kTileT * kTileT; }
 
-size_t bwd_workspace_bytes(const Plan& p, int32_t chunk_V, bool with_dW) {
+// Splits of the dh GEMM's contraction (over one chunk) when its output has
+// few 256 x 256 tiles (few tokens): enough workgroups for the 256 CUs, each
+// split at least 512 vocabulary entries long.
+int dh_ksplit(const Plan& p, int32_t chunk_V) {
+  const int64_t tiles = ((p.N + kTileDhT - 1) / kTileDhT) * ((p.d_s + kTileDhD - 1) / kTileDhD);
+  if (tiles >= 128) return 1;
+  int64_t s = (256 + tiles - 1) / tiles;
+  const int64_t by_k = chunk_V / 512;
+  s = s < by_k ? s : by_k;
+  return s > 1 ? (int)s : 1;
+}
+
+// The chunk buffers (G, W_s's chunk transposed, and for dW_s their token-major
+// counterparts); the dh GEMM's split partial tiles follow them.
+static size_t bwd_base_bytes(const Plan& p, int32_t chunk_V, bool with_dW) {
   size_t b = align_up((size_t)p.N * chunk_V * p.esz, 256) + align_up((size_t)p.d_s * chunk_V * p.esz, 256);
   if (with_dW) {
     const size_t np = (size_t)padded_tokens(p);
     b += align_up((size_t)chunk_V * np * p.esz, 256) + align_up((size_t)p.d_s * np * p.esz, 256);
   }
   return b;
+}
+
+size_t bwd_workspace_bytes(const Plan& p, int32_t chunk_V, bool with_dW) {
+  const int s = dh_ksplit(p, chunk_V);
+  return bwd_base_bytes(p, chunk_V, with_dW) +
+         (s > 1 ? align_up((size_t)s * p.N * p.d_s * sizeof(float), 256) : 0);
+}
+
+// dh (+)= G . W_s[chunk] for one chunk (kcols contracted entries), split over
+// the contraction when the output has few tiles.
+static hipError_t launch_dh(const Plan& p, bool bf16, DhArgs da, int32_t chunk_V, int64_t kcols, float* part,
+                            hipStream_t st) {
+  const int n_d_tiles = (p.d_s + kTileDhD - 1) / kTileDhD;
+  const int n_tok_tiles = (int)((p.N + kTileDhT - 1) / kTileDhT);
+  da.n_tok_tiles = n_tok_tiles;
+  da.n_d_tiles = n_d_tiles;
+  da.n_ksplit = 1;
+  const int s_max = dh_ksplit(p, chunk_V);
+  if (s_max > 1) {
+    // splits of whole 256-entry vocabulary tiles: every split is non-empty
+    const int64_t ktiles = kcols / kTileV;
+    const int64_t per = (ktiles + s_max - 1) / s_max;
+    da.n_ksplit = (int)((ktiles + per - 1) / per);
+    da.kspan = (int32_t)(per * kTileV * p.esz);
+    da.part = part;
+  }
+  const dim3 grid((unsigned)(n_tok_tiles * n_d_tiles * da.n_ksplit));
+  if (bf16)
+    hipLaunchKernelGGL(dh_kernel<true>, grid, dim3(kDhThreads), 0, st, da);
+  else
+    hipLaunchKernelGGL(dh_kernel<false>, grid, dim3(kDhThreads), 0, st, da);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || da.n_ksplit == 1) return e;
+  const int64_t count = p.N * (int64_t)p.d_s;
+  const unsigned rblocks = (unsigned)((count + 255) / 256 < 4096 ? (count + 255) / 256 : 4096);
+  hipLaunchKernelGGL(dh_reduce_kernel, dim3(rblocks), dim3(256), 0, st, part, da.n_ksplit, count, da.dh, da.first);
+  return hipGetLastError();
 }
 
 hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
@@ -904,6 +984,8 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   char* WsT = G + align_up((size_t)p.N * io.chunk_V * p.esz, 256);
   char* GT = WsT + align_up((size_t)p.d_s * io.chunk_V * p.esz, 256);
   char* hsT = GT + align_up((size_t)io.chunk_V * np * p.esz, 256);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(io.workspace) +
+                                         bwd_base_bytes(p, io.chunk_V, io.dW != nullptr));
   LogitArgs la = logit_args(p, io.h_s, io.W_s, io.h_t, io.W_t, io.tau, io.beta);
   la.lse_s = io.lse_s;
   la.lse_t = io.lse_t;
@@ -957,11 +1039,9 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
                       (int32_t)(kcols * p.esz)};
       da.N = p.N;
       da.d_s = p.d_s;
-      da.n_tok_tiles = n_tok_tiles_dh;
-      da.n_d_tiles = n_d_tiles;
       da.dh = io.dh;
       da.first = c0 == 0;
-      if ((e = gemm(da, n_tok_tiles_dh)) != hipSuccess) return e;
+      if ((e = launch_dh(p, p.bf16, da, io.chunk_V, kcols, part, st)) != hipSuccess) return e;
     }
     if (io.dW) {
       // dW_s[chunk] = G^T . h_s: rows of the chunk, contracted over the tokens
@@ -973,6 +1053,7 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
       dw.n_d_tiles = n_d_tiles;
       dw.dh = io.dW + c0 * p.d_s;
       dw.first = 1;
+      dw.n_ksplit = 1;
       if ((e = gemm(dw, dw.n_tok_tiles)) != hipSuccess) return e;
     }
   }
@@ -983,7 +1064,8 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
 // overwrite their G elements (g_fix_kernel), W_s's chunk is transposed, and
 // the dh GEMM writes (first chunk) or accumulates onto dh_s.
 static hipError_t run_list_chunks(const Plan& p, DenseArgs a, const int32_t* list_idx, const float* list_val, int slots,
-                                  const void* W_s, char* G, char* WsT, int32_t chunk_V, float* dh, hipStream_t st) {
+                                  const void* W_s, char* G, char* WsT, float* part, int32_t chunk_V, float* dh,
+                                  hipStream_t st) {
   hipError_t e;
   const int n_d_tiles = (p.d_s + kTileDhD - 1) / kTileDhD;
   const int n_tok_tiles_dh = (int)((p.N + kTileDhT - 1) / kTileDhT);
@@ -1011,12 +1093,9 @@ static hipError_t run_list_chunks(const Plan& p, DenseArgs a, const int32_t* lis
     da.p = PairDesc{G, WsT, (int64_t)chunk_V * 2, (int64_t)chunk_V * 2, p.N, p.d_s, (int32_t)(kcols * 2)};
     da.N = p.N;
     da.d_s = p.d_s;
-    da.n_tok_tiles = n_tok_tiles_dh;
-    da.n_d_tiles = n_d_tiles;
     da.dh = dh;
     da.first = c0 == 0 ? 1 : 0;
-    hipLaunchKernelGGL(dh_kernel<true>, dim3(n_tok_tiles_dh * n_d_tiles), dim3(kDhThreads), 0, st, da);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = launch_dh(p, true, da, chunk_V, kcols, part, st)) != hipSuccess) return e;
   }
   return hipSuccess;
 }
@@ -1090,7 +1169,8 @@ hipError_t run_topk_bwd(const Plan& p, const TopkBwdIO& io, hipStream_t st) {
   a.lse_s1 = ce ? io.lse_s1 : nullptr;
   a.dense_a = dense_a;
   a.dense_c = ce ? dense_c : nullptr;
-  return run_list_chunks(p, a, list_idx, list_val, slots, io.W_s, G, WsT, io.chunk_V, io.dh, st);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(io.workspace) + bwd_base_bytes(p, io.chunk_V, false));
+  return run_list_chunks(p, a, list_idx, list_val, slots, io.W_s, G, WsT, part, io.chunk_V, io.dh, st);
 }
 
 hipError_t run_tail_bwd(const Plan& p, const TailBwdIO& io, hipStream_t st) {
@@ -1119,7 +1199,8 @@ hipError_t run_tail_bwd(const Plan& p, const TailBwdIO& io, hipStream_t st) {
   DenseArgs a = dense_args(p, io.h_s, io.W_s, io.tau, G, io.chunk_V);
   a.lse_s = io.lse_s;
   a.dense_a = dense_a;
-  return run_list_chunks(p, a, io.sup_idx, list_val, io.smax, io.W_s, G, WsT, io.chunk_V, io.dh, st);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(io.workspace) + bwd_base_bytes(p, io.chunk_V, false));
+  return run_list_chunks(p, a, io.sup_idx, list_val, io.smax, io.W_s, G, WsT, part, io.chunk_V, io.dh, st);
 }
 
 hipError_t run_copy_rows(const void* src, void* dst, const int32_t* rows, int64_t n_rows, int64_t n_other,
