@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--chunk-v", type=int, default=16384)
+    ap.add_argument("--chunk-v", type=int, default=0,
+                    help="backward recompute chunk (0: the library's default for the shape, kd_default_chunk)")
     ap.add_argument("--beta", type=float, default=1.0)
     ap.add_argument("--with-dw", action="store_true",
                     help="also compute dL/dW_s in the backward (the step then runs three GEMM sweeps)")
@@ -176,6 +177,7 @@ def main():
     torch.cuda.set_device(0)
     w = kdsynth.make(args.workload)
     N, V, ds, dt_, tau, beta = w.N, w.V, w.d_s, w.d_t, w.tau, args.beta
+    args.chunk_v = args.chunk_v or kd.default_chunk(N, V)
     dev = [to_dev(x) for x in (w.h_s, w.W_s, w.h_t, w.W_t)]
     stream = torch.cuda.Stream()
     fws = kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt_, kd.KD_BF16, beta=0.5)  # covers every beta
@@ -337,20 +339,21 @@ def bench_small_n(args):
         torch.cuda.synchronize()
         ms = float(np.median([a.elapsed_time(b) for a, b in times]))
         gbs = (w_bytes + 2.0 * n * (w.d_s + w.d_t)) / (ms / 1e3) / 1e9
-        # the backward at the same N (beside the forward line; chunk_V as given)
+        # the backward at the same N (beside the forward line; chunk_V as given, else the default for n)
+        cv = args.chunk_v or kd.default_chunk(n, w.V)
         loss, lse_s, lse_t, aux = kd.kd_fwd(hs, dev[1], ht, dev[3], 1.0, w.tau)
         dh = torch.empty(n, w.d_s, dtype=torch.float32, device="cuda")
-        kd.kd_bwd(hs, dev[1], ht, dev[3], 1.0, w.tau, lse_s, lse_t, aux, chunk_V=args.chunk_v, dh=dh)
+        kd.kd_bwd(hs, dev[1], ht, dev[3], 1.0, w.tau, lse_s, lse_t, aux, chunk_V=cv, dh=dh)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(5):
-            kd.kd_bwd(hs, dev[1], ht, dev[3], 1.0, w.tau, lse_s, lse_t, aux, chunk_V=args.chunk_v, dh=dh)
+            kd.kd_bwd(hs, dev[1], ht, dev[3], 1.0, w.tau, lse_s, lse_t, aux, chunk_V=cv, dh=dh)
         e1.record()
         torch.cuda.synchronize()
         points.append({"N": n, "ms": round(ms, 4), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                        "TFLOP/s": round(2.0 * n * w.V * (w.d_s + w.d_t) / (ms / 1e3) / 1e12, 1),
-                       "bwd_ms": round(e0.elapsed_time(e1) / 5, 4)})
+                       "bwd_ms": round(e0.elapsed_time(e1) / 5, 4), "bwd_chunk_V": cv})
     first = points[0]
     print(json.dumps({
         "metric": f"kd_fwd time at small N, V={w.V}, d_s={w.d_s}, d_t={w.d_t}", "value": first["ms"], "unit": "ms",
@@ -376,6 +379,7 @@ def bench_topk(args):
     torch.cuda.set_device(0)
     w = kdsynth.make(5)
     N, V, ds, dt_, tau, k, beta = w.N, w.V, w.d_s, w.d_t, w.tau, args.k, args.beta
+    args.chunk_v = args.chunk_v or kd.default_chunk(N, V)
     dev = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in (w.h_s, w.W_s, w.h_t, w.W_t)]
     lab = torch.from_numpy(w.labels.astype(np.int32)).cuda()
     stream = torch.cuda.Stream()

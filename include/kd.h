@@ -85,9 +85,9 @@ typedef enum {
  *   (kd_topk_bwd: KD_OP_BWD's chunk buffers plus O(N k) floats), KD_OP_TAIL
  *   (kd_tail_fwd, any support) or KD_OP_TAIL_BWD (kd_tail_bwd, any support:
  *   KD_OP_BWD's buffers plus O(N k) floats).
- *   beta is read for KD_OP_FWD, chunk_V for the backward ops, k for the
- *   top-k and tail ops; d_s/d_t/dtype size the backward's per-chunk
- *   buffers.
+ *   beta is read for KD_OP_FWD, chunk_V for the backward ops (0 selects
+ *   kd_default_chunk, as in the backward calls), k for the top-k and tail
+ *   ops; d_s/d_t/dtype size the backward's per-chunk buffers.
  *   The backward's workspace is O(N * chunk_V) (the gradient tile G of one
  *   vocabulary chunk, in the input dtype) plus O(chunk_V * d_s) for one
  *   transposed chunk of W_s; KD_OP_BWD_W adds a transposed copy of G and of
@@ -97,6 +97,20 @@ typedef enum {
  */
 kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t d_t, kd_dtype dtype,
                             float beta, int32_t chunk_V, int32_t k, size_t* bytes);
+
+/*
+ * kd_default_chunk - the recompute chunk that the backward calls use when
+ *   passed chunk_V = 0. The recompute structure (one vocabulary chunk of the
+ *   gradient at a time) is the Nitrobrew notes' "仓库实现"; the chunk size is
+ *   the caller's memory/speed trade-off. The default keeps the [N, chunk]
+ *   gradient tile within 1 GiB (input dtype) and splits the vocabulary, V
+ *   rounded up to 256, into the fewest equal chunks (multiples of 256) under
+ *   that bound, never below 2048 entries unless the vocabulary is smaller.
+ *   Few tokens thus get the whole vocabulary as one chunk; 32768 bf16 tokens
+ *   over 151936 entries get ten chunks of 15360.
+ *   Returns 0 for N < 0, V < 1 or an unknown dtype. Pure host function.
+ */
+int32_t kd_default_chunk(int64_t N, int64_t V, kd_dtype dtype);
 
 /*
  * kd_fwd - per-token beta-divergence between student and teacher.
@@ -139,7 +153,8 @@ kd_status kd_fwd(const void* h_s, const void* W_s, const void* h_t, const void* 
  *         same inputs, beta and tau (aux unused when beta == 0, may be NULL).
  *   grad_loss (device, [N] fp32, read; NULL means all ones).
  *   chunk_V: vocabulary entries per recompute chunk (a positive multiple of
- *         256); the workspace holds one [N, chunk_V] gradient chunk.
+ *         256, or 0 for kd_default_chunk(N, V, dtype)); the workspace holds
+ *         one [N, chunk_V] gradient chunk.
  *   dh_s  (device, [N, d_s] fp32, overwritten; may be NULL if dW_s is not).
  *   dW_s  (device, [V, d_s] fp32, overwritten; may be NULL). When given, the
  *         workspace must hold kd_workspace_size(KD_OP_BWD_W, ...) bytes and

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libkd.so not bu
 
 def header_symbols():
     text = open(os.path.join(ROOT, "include", "kd.h")).read()
-    return sorted(set(re.findall(r"^(?:kd_status|const char\*)\s+(kd_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^(?:kd_status|const char\*|int32_t)\s+(kd_\w+)\s*\(", text, flags=re.M)))
 
 
 def test_header_symbols_exported():
@@ -78,6 +78,34 @@ def test_workspace_sizes():
         kd.workspace_size(kd.KD_OP_FWD, N, V, ds, dt, kd.KD_BF16, beta=1.5)
     with pytest.raises(kd.KDError):
         kd.workspace_size(kd.KD_OP_TOPK, N, V, ds, dt, kd.KD_BF16, k=0)
+
+
+def test_default_chunk():
+    import vocab_chunked_kl_amd as kd
+    # the [N, chunk] gradient tile stays within 1 GiB; the vocabulary (rounded up to 256) is cut into the
+    # fewest equal chunks under that bound, each rounded up to 256, never below 2048 unless V is smaller
+    cases = [
+        (32768, 151936, kd.KD_BF16, 15360),  # 16384 allowed: 10 chunks of 15207 -> 15360
+        (4096, 151936, kd.KD_BF16, 76032),   # 131072 allowed: 2 chunks
+        (64, 151936, kd.KD_BF16, 152064),    # the whole (padded) vocabulary
+        (8192, 248320, kd.KD_BF16, 62208),   # 65536 allowed: 4 chunks of 62080 -> 62208
+        (1 << 22, 151936, kd.KD_BF16, 2048),  # the bound would give 128: the 2048 floor
+        (10, 1000, kd.KD_F32, 1024),         # a small vocabulary is one chunk
+        (32768, 151936, kd.KD_F32, 8192),    # fp32: 8192 allowed, 19 chunks of 8004 -> 8192
+        (0, 151936, kd.KD_BF16, 152064),
+    ]
+    for n, v, dt, want in cases:
+        assert kd.default_chunk(n, v, dt) == want, (n, v, dt)
+        assert (n or 1) * want * (2 if dt == kd.KD_BF16 else 4) <= (1 << 30) or want == 2048 or want >= v
+    assert kd.default_chunk(-1, 100) == 0 and kd.default_chunk(8, 0) == 0 and kd.default_chunk(8, 100, 7) == 0
+    # chunk_V = 0 sizes every backward op's workspace for the default chunk
+    for n, v in ((64, 151936), (4096, 151936), (3000, 50000)):
+        c = kd.default_chunk(n, v)
+        for op in (kd.KD_OP_BWD, kd.KD_OP_BWD_W, kd.KD_OP_TOPK_BWD, kd.KD_OP_TAIL_BWD):
+            assert kd.workspace_size(op, n, v, 1024, 2048, kd.KD_BF16, chunk_V=0, k=16) == \
+                kd.workspace_size(op, n, v, 1024, 2048, kd.KD_BF16, chunk_V=c, k=16), (n, v, op)
+    with pytest.raises(kd.KDError):
+        kd.workspace_size(kd.KD_OP_BWD, 64, 1000, 64, 64, kd.KD_BF16, chunk_V=-256)
 
 
 FAKE = 0x10000  # aligned non-null address: never dereferenced, every call below fails validation first

@@ -337,3 +337,32 @@ def test_split_contraction_topk_backward():
     torch.cuda.synchronize()
     ref = O.kd_topk_bwd(*arrays, 16, 1.2, labels, wb, wc, we, sel=out["idx"].cpu().numpy())
     assert_grad_rows(dh.cpu().numpy(), ref, name="topk dh_s (split)")
+
+
+def test_default_chunk_backward():
+    """chunk_V = 0 runs the library's default chunk (here the whole vocabulary,
+    one chunk, with the dh contraction split): the same bits as passing that
+    chunk explicitly, and the oracle's gradient, for all three backward calls."""
+    kd, torch = _kd()
+    N, V, ds, dt = 200, 20000, 96, 64
+    c = kd.default_chunk(N, V)
+    assert c == 20224
+    arrays = kdsynth.small_case(73, N, V, ds, dt)
+    grad = np.random.default_rng(9).uniform(-1, 2, size=N)
+    _say(f"default chunk kd_bwd N={N} V={V} chunk={c}")
+    _, dh0 = run_case(kd, torch, arrays, 0.5, 1.1, grad=grad, chunk_V=0)
+    _, dhc = run_case(kd, torch, arrays, 0.5, 1.1, grad=grad, chunk_V=c)
+    assert torch.equal(dh0, dhc)
+    dev = [to_dev(x) for x in arrays]
+    _say(f"default chunk kd_topk_bwd / kd_tail_bwd N={N} V={V} chunk={c}")
+    one = torch.ones(N, dtype=torch.float32, device="cuda")
+    out = kd.kd_topk_fwd(*dev, 8, 1.1)
+    t0, tc = (kd.kd_topk_bwd(dev[0], dev[1], out, 8, 1.1, grad_binary=one, grad_cond=one, chunk_V=cv)
+              for cv in (0, c))
+    tl = kd.kd_tail_fwd(*dev, 8, 0.5, 1.1, kd.KD_SUPPORT_TEACHER | kd.KD_SUPPORT_STUDENT)
+    l0, lc = (kd.kd_tail_bwd(dev[0], dev[1], tl, 8, 0.5, 1.1, kd.KD_SUPPORT_TEACHER | kd.KD_SUPPORT_STUDENT,
+                             chunk_V=cv) for cv in (0, c))
+    torch.cuda.synchronize()
+    assert torch.equal(t0, tc) and torch.equal(l0, lc)
+    ref = O.kd_topk_bwd(*arrays, 8, 1.1, None, np.ones(N), np.ones(N), None, sel=out["idx"].cpu().numpy())
+    assert_grad_rows(t0.cpu().numpy(), ref, name="topk dh_s (default chunk)")

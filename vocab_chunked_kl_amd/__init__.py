@@ -40,7 +40,7 @@ KD_OP_FWD, KD_OP_BWD, KD_OP_TOPK, KD_OP_BWD_W, KD_OP_TOPK_BWD, KD_OP_TAIL, KD_OP
 KD_SUPPORT_TEACHER, KD_SUPPORT_STUDENT, KD_SUPPORT_LABEL = 1, 2, 4
 KD_TOPK_MAX = 64
 KD_TOPK_MAX_V = 524288
-EXPORTED = ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_tail_fwd", "kd_tail_bwd",
+EXPORTED = ("kd_workspace_size", "kd_default_chunk", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_tail_fwd", "kd_tail_bwd",
             "kd_gather_rows", "kd_scatter_rows", "kd_status_string", "kd_last_error")
 
 
@@ -76,6 +76,8 @@ def load_library(path: str = LIB_PATH):
                                 vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_tail_bwd.argtypes = [vp, vp, i64, i64, i32, i32, i32, f32, f32, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32,
                                 vp, vp, sz, vp]
+    lib.kd_default_chunk.argtypes = [i64, i64, ctypes.c_int]
+    lib.kd_default_chunk.restype = i32
     lib.kd_gather_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
     lib.kd_scatter_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp]
     for fn in ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_tail_fwd", "kd_tail_bwd",
@@ -128,9 +130,17 @@ def _inputs(h_s, W_s, h_t, W_t):
     return N, V, d_s, d_t, _dtype_code(h_s)
 
 
+def default_chunk(N: int, V: int, dtype: int = KD_BF16) -> int:
+    """The recompute chunk the backward calls use for ``chunk_V=0``
+    (kd_default_chunk): the fewest equal chunks whose [N, chunk] gradient
+    tile fits in 1 GiB."""
+    return int(load_library().kd_default_chunk(N, V, dtype))
+
+
 def workspace_size(op: int, N: int, V: int, d_s: int, d_t: int, dtype: int = KD_BF16, beta: float = 1.0,
-                   chunk_V: int = 2048, k: int = 64) -> int:
-    """Bytes of device workspace ``op`` needs (kd_workspace_size)."""
+                   chunk_V: int = 0, k: int = 64) -> int:
+    """Bytes of device workspace ``op`` needs (kd_workspace_size); ``chunk_V=0``
+    is the library's default chunk."""
     lib = load_library()
     out = ctypes.c_size_t(0)
     _check(lib.kd_workspace_size(op, N, V, d_s, d_t, dtype, float(beta), chunk_V, k, ctypes.byref(out)))
@@ -159,7 +169,7 @@ def kd_fwd(h_s, W_s, h_t, W_t, beta: float, tau: float, workspace=None, stream=N
     return loss, lse_s, lse_t, aux
 
 
-def kd_bwd(h_s, W_s, h_t, W_t, beta: float, tau: float, lse_s, lse_t, aux, grad_loss=None, chunk_V: int = 8192,
+def kd_bwd(h_s, W_s, h_t, W_t, beta: float, tau: float, lse_s, lse_t, aux, grad_loss=None, chunk_V: int = 0,
            workspace=None, stream=None, dh=None, dW=None, want_dh: bool = True, want_dW: bool = False):
     """dL/dh_s (fp32 [N, d_s]) and, with ``want_dW``, dL/dW_s (fp32 [V, d_s])
     for L = sum_n grad_loss[n] * loss[n]. Returns dh, or (dh, dW) when
@@ -216,7 +226,7 @@ def kd_topk_fwd(h_s, W_s, h_t, W_t, k: int, tau: float, labels=None, workspace=N
 
 
 def kd_topk_bwd(h_s, W_s, fwd: dict, k: int, tau: float, labels=None, grad_binary=None, grad_cond=None,
-                grad_ce=None, chunk_V: int = 8192, workspace=None, stream=None, dh=None):
+                grad_ce=None, chunk_V: int = 0, workspace=None, stream=None, dh=None):
     """dL/dh_s (fp32 [N, d_s]) of sum_n grad_binary[n] binary[n] + grad_cond[n] cond[n]
     + grad_ce[n] ce[n]; ``fwd`` is the dict returned by ``kd_topk_fwd`` for the
     same inputs (called with ``with_values=True``)."""
@@ -286,7 +296,7 @@ def kd_tail_fwd(h_s, W_s, h_t, W_t, k: int, beta: float, tau: float, support: in
 
 
 def kd_tail_bwd(h_s, W_s, fwd: dict, k: int, beta: float, tau: float, support: int, grad_loss=None,
-                chunk_V: int = 8192, workspace=None, stream=None, dh=None):
+                chunk_V: int = 0, workspace=None, stream=None, dh=None):
     """dL/dh_s (fp32 [N, d_s]) of sum_n grad_loss[n] loss[n] for the dict
     ``fwd`` that ``kd_tail_fwd`` returned for the same inputs."""
     lib = load_library()
@@ -440,18 +450,19 @@ def _divergence(xs, xt, ws, wt, beta, temperature, reduction, chunk_V, labels, i
     raise ValueError(f"unknown reduction {reduction!r}")
 
 
-def forward_kl(xs, xt, ws, wt, temperature=1.0, reduction="mean", chunk_V=2048, labels=None, ignore_index=-100):
+def forward_kl(xs, xt, ws, wt, temperature=1.0, reduction="mean", chunk_V=0, labels=None, ignore_index=-100):
     """KL(teacher || student) from hidden states xs [.., D_s], xt [.., D_t] and
-    unembeddings ws [V, D_s], wt [V, D_t]."""
+    unembeddings ws [V, D_s], wt [V, D_t]. ``chunk_V`` is the backward's
+    recompute chunk (0: ``default_chunk``), here and in the other losses."""
     return _divergence(xs, xt, ws, wt, 0.0, temperature, reduction, chunk_V, labels, ignore_index)
 
 
-def reverse_kl(xs, xt, ws, wt, temperature=1.0, reduction="mean", chunk_V=2048, labels=None, ignore_index=-100):
+def reverse_kl(xs, xt, ws, wt, temperature=1.0, reduction="mean", chunk_V=0, labels=None, ignore_index=-100):
     """KL(student || teacher) from hidden states and unembeddings."""
     return _divergence(xs, xt, ws, wt, 1.0, temperature, reduction, chunk_V, labels, ignore_index)
 
 
-def jsd(xs, xt, ws, wt, beta=0.5, temperature=1.0, reduction="mean", chunk_V=2048, labels=None, ignore_index=-100):
+def jsd(xs, xt, ws, wt, beta=0.5, temperature=1.0, reduction="mean", chunk_V=0, labels=None, ignore_index=-100):
     """beta KL(teacher || m) + (1 - beta) KL(student || m), m = beta teacher + (1 - beta) student;
     beta = 0 / 1 give forward / reverse KL."""
     return _divergence(xs, xt, ws, wt, beta, temperature, reduction, chunk_V, labels, ignore_index)
@@ -481,7 +492,7 @@ class _TopK(torch.autograd.Function):
         return (dh.to(xs.dtype),) + (None,) * 8
 
 
-def topk_kd(xs, xt, ws, wt, k=64, labels=None, temperature=1.0, ignore_index=-100, chunk_V=8192):
+def topk_kd(xs, xt, ws, wt, k=64, labels=None, temperature=1.0, ignore_index=-100, chunk_V=0):
     """Top-k three-term KD terms per token: dict with ``binary``, ``cond``,
     ``ce`` (when labels are given; these three carry the gradient to ``xs``),
     masses, LSEs and the selection."""
@@ -520,7 +531,7 @@ class _Tail(torch.autograd.Function):
 
 
 def tail_kd(xs, xt, ws, wt, k=1, beta=0.0, labels=None, temperature=1.0, support=None, reduction="mean",
-            ignore_index=-100, chunk_V=8192, return_dict=False):
+            ignore_index=-100, chunk_V=0, return_dict=False):
     """Beta-divergence over a top-k support plus a tail bucket (ars-opd-rebuild
     "03 · 层 2：White-box OPD 基线", section 2.4), per-token mean over
     non-ignored labels by default. ``support`` defaults to

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <algorithm>
 #include <stdio.h>
 #include <string.h>
 
@@ -48,6 +50,28 @@ kd_status check_common(const void* h_s, const void* W_s, const void* h_t, const 
   return KD_OK;
 }
 
+// Default recompute chunk: the [N, chunk] gradient tile stays within 1 GiB,
+// and the vocabulary is cut into equal chunks (multiples of 256, at least
+// 2048 entries unless V is smaller) so that the last one is not a sliver.
+constexpr int64_t kChunkBudget = (int64_t)1 << 30;
+
+int32_t default_chunk(int64_t N, int64_t V, int64_t esz) {
+  const int64_t vr = (V + 255) / 256 * 256;
+  const int64_t cap = (kMaxTileBytes - 1) / (256 * esz) / 256 * 256;  // 256 * chunk * esz < kMaxTileBytes
+  int64_t cmax = N > 0 ? kChunkBudget / (N * esz) / 256 * 256 : vr;
+  cmax = std::min(std::max<int64_t>(cmax, 2048), std::min(vr, cap));
+  const int64_t n = (vr + cmax - 1) / cmax;
+  return (int32_t)(((vr + n - 1) / n + 255) / 256 * 256);
+}
+
+// chunk_V == 0 selects the default; anything else must be a positive multiple of 256.
+kd_status resolve_chunk(int32_t& chunk_V, int64_t N, int64_t V, int64_t esz) {
+  if (chunk_V == 0) chunk_V = default_chunk(N, V, esz);
+  if (chunk_V < 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be 0 or a positive multiple of 256");
+  if (256 * (int64_t)chunk_V * esz >= kMaxTileBytes) return fail(KD_ERR_UNSUPPORTED, "chunk_V too large");
+  return KD_OK;
+}
+
 bool bad_beta(float beta) { return !(beta >= 0.f && beta <= 1.f); }
 bool bad_tau(float tau) { return !(tau > 0.f) || !isfinite(tau); }
 
@@ -68,12 +92,21 @@ const char* kd_status_string(kd_status s) {
 
 const char* kd_last_error(void) { return g_last_error; }
 
+int32_t kd_default_chunk(int64_t N, int64_t V, kd_dtype dtype) {
+  if (N < 0 || V < 1 || (dtype != KD_F32 && dtype != KD_BF16)) return 0;
+  return default_chunk(N, V, dtype == KD_BF16 ? 2 : 4);
+}
+
 kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t d_t, kd_dtype dtype, float beta,
                             int32_t chunk_V, int32_t k, size_t* bytes) {
   if (!bytes) return fail(KD_ERR_INVALID_ARG, "bytes is null");
   if (N <= 0 || V < 2 || d_s <= 0 || d_t <= 0) return fail(KD_ERR_INVALID_ARG, "bad shape");
   if (dtype != KD_F32 && dtype != KD_BF16) return fail(KD_ERR_UNSUPPORTED, "unknown dtype");
   const kd::Plan p = kd::make_plan(N, V, d_s, d_t, dtype == KD_BF16);
+  if (op == KD_OP_BWD || op == KD_OP_BWD_W || op == KD_OP_TOPK_BWD || op == KD_OP_TAIL_BWD) {
+    const kd_status s = resolve_chunk(chunk_V, N, V, dtype == KD_BF16 ? 2 : 4);
+    if (s != KD_OK) return s;
+  }
   switch (op) {
     case KD_OP_FWD:
       if (bad_beta(beta)) return fail(KD_ERR_INVALID_ARG, "beta outside [0, 1]");
@@ -81,7 +114,6 @@ kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t
       return KD_OK;
     case KD_OP_BWD:
     case KD_OP_BWD_W:
-      if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
       *bytes = kd::bwd_workspace_bytes(p, chunk_V, op == KD_OP_BWD_W);
       return KD_OK;
     case KD_OP_TOPK:
@@ -89,7 +121,6 @@ kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t
       *bytes = kd::topk_workspace_bytes(p, k);
       return KD_OK;
     case KD_OP_TOPK_BWD:
-      if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
       if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
       *bytes = kd::topk_bwd_workspace_bytes(p, chunk_V, k);
       return KD_OK;
@@ -98,7 +129,6 @@ kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t
       *bytes = kd::tail_workspace_bytes(p, k);
       return KD_OK;
     case KD_OP_TAIL_BWD:
-      if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
       if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
       *bytes = kd::tail_bwd_workspace_bytes(p, chunk_V, k);
       return KD_OK;
@@ -136,9 +166,8 @@ kd_status kd_bwd(const void* h_s, const void* W_s, const void* h_t, const void* 
   if (s != KD_OK) return s;
   if (bad_beta(beta)) return fail(KD_ERR_INVALID_ARG, "beta outside [0, 1]");
   if (bad_tau(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be positive and finite");
-  if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
   const int64_t esz = dtype == KD_BF16 ? 2 : 4;
-  if (256 * (int64_t)chunk_V * esz >= kMaxTileBytes) return fail(KD_ERR_UNSUPPORTED, "chunk_V too large");
+  if ((s = resolve_chunk(chunk_V, N, V, esz)) != KD_OK) return s;
   if (!lse_s || !lse_t) return fail(KD_ERR_INVALID_ARG, "null pointer (lse_s, lse_t)");
   if (!dh_s && !dW_s) return fail(KD_ERR_INVALID_ARG, "dh_s and dW_s are both null");
   if (!aux && beta > 0.f) return fail(KD_ERR_INVALID_ARG, "aux may be null only for beta == 0");
@@ -195,8 +224,7 @@ kd_status kd_topk_bwd(const void* h_s, const void* W_s, int64_t N, int64_t V, in
   if (dtype != KD_BF16) return fail(KD_ERR_UNSUPPORTED, "kd_topk_bwd takes bf16 inputs only");
   if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
   if (bad_tau(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be positive and finite");
-  if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
-  if (256 * (int64_t)chunk_V * 2 >= kMaxTileBytes) return fail(KD_ERR_UNSUPPORTED, "chunk_V too large");
+  if ((s = resolve_chunk(chunk_V, N, V, 2)) != KD_OK) return s;
   if (!topk_idx || !topk_val || !topk_val_s || !p_mass || !q_mass || !lse_s || !dh_s)
     return fail(KD_ERR_INVALID_ARG, "null input or output pointer");
   if (grad_ce && labels && !lse_s1) return fail(KD_ERR_INVALID_ARG, "lse_s1 is needed for the CE gradient");
@@ -251,8 +279,7 @@ kd_status kd_tail_bwd(const void* h_s, const void* W_s, int64_t N, int64_t V, in
     return fail(KD_ERR_INVALID_ARG, "support must include KD_SUPPORT_TEACHER or KD_SUPPORT_STUDENT");
   if (bad_beta(beta)) return fail(KD_ERR_INVALID_ARG, "beta outside [0, 1]");
   if (bad_tau(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be positive and finite");
-  if (chunk_V <= 0 || chunk_V % 256) return fail(KD_ERR_INVALID_ARG, "chunk_V must be a positive multiple of 256");
-  if (256 * (int64_t)chunk_V * 2 >= kMaxTileBytes) return fail(KD_ERR_UNSUPPORTED, "chunk_V too large");
+  if ((s = resolve_chunk(chunk_V, N, V, 2)) != KD_OK) return s;
   if (!sup_idx || !sup_t || !sup_s || !lse_s || !lse_t || !dh_s)
     return fail(KD_ERR_INVALID_ARG, "null input or output pointer");
   if (!aligned16(dh_s)) return fail(KD_ERR_UNSUPPORTED, "dh_s must be 16-byte aligned");
