@@ -998,7 +998,6 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   la.Np = np;
   la.tiles_per_split = 1;
   const int n_d_tiles = (p.d_s + kTileDhD - 1) / kTileDhD;
-  const int n_tok_tiles_dh = (int)((p.N + kTileDhT - 1) / kTileDhT);
   hipError_t e;
   auto transpose = [&](const void* src, char* dst, int64_t rows, int64_t c0, int64_t cols, int64_t pitch) {
     const dim3 tgrid((unsigned)(cols / 64), (unsigned)((p.d_s + 63) / 64));
@@ -1067,8 +1066,6 @@ static hipError_t run_list_chunks(const Plan& p, DenseArgs a, const int32_t* lis
                                   const void* W_s, char* G, char* WsT, float* part, int32_t chunk_V, float* dh,
                                   hipStream_t st) {
   hipError_t e;
-  const int n_d_tiles = (p.d_s + kTileDhD - 1) / kTileDhD;
-  const int n_tok_tiles_dh = (int)((p.N + kTileDhT - 1) / kTileDhT);
   FixArgs f{list_idx, list_val, p.N, slots, 0, 0, G, (int64_t)chunk_V * 2};
   const unsigned fix_blocks = (unsigned)((p.N * slots + 255) / 256);
   for (int64_t c0 = 0; c0 < p.V; c0 += chunk_V) {

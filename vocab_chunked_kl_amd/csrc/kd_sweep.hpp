@@ -77,38 +77,40 @@ struct Ring {
   static constexpr int kBytes = (TM + TN) * RB;
 };
 
+// Fetch-side state of the stage ring besides its two buffer resources (a
+// sizeless type, so they are kept apart): this lane's byte offsets (row *
+// pitch + its chunk, at K offset 0) of the stage issued next and the pair's K
+// extent. It changes only when the fetch cursor moves to the other operand
+// pair or to the next A tile, so it is rebuilt then (once per K extent) and a
+// stage's loads cost an add, a compare and a select per lane. Past the last A
+// tile both resources are empty and every load writes zeros without reading.
+template <int QA, int QB>
+struct FetchState {
+  int32_t offa[QA], offb[QB];
+  int32_t kbytes;
+};
+
 // Issue the direct-to-LDS loads of one stage (this wave's share of NW waves:
-// (TM + TN) / (rows per load * NW) instructions). `ra` / `rb`: resources
-// starting at the tile's first row; `a_lane_row` / `b_lane_row`: this lane's
-// row-in-group times the row pitch. A lane whose chunk lies at or past the
-// row length, or every lane when `valid` is false, reads past the resource
-// end and writes zeros.
-template <int TM, int TN, int NW, int RB>
+// QA + QB instructions, one 1024-byte row group each; `qa0` / `qb0`: this
+// wave's first row group). `ca` / `cb`: this lane's chunk byte offset per
+// load; a lane whose chunk lies at or past the row length reads past the
+// resource end and writes zeros.
+template <int TM, int RB, int QA, int QB>
 __device__ __forceinline__ void dma_stage(char* dst, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                          int32_t a_lane_row, int32_t b_lane_row, int64_t lda, int64_t ldb,
-                                          int32_t kbyte0, int32_t kbytes, bool valid, int wave, int lane) {
-  using F = RowFmt<RB>;
-  constexpr int RPL = F::kRowsPerLoad;
-  constexpr int QA = TM / (RPL * NW), QB = TN / (RPL * NW);  // instructions per wave
-  static_assert(QA * RPL * NW == TM && QB * RPL * NW == TN, "tile rows must split evenly over the waves");
-  const int slot = lane % F::kChunks, rig = lane / F::kChunks;  // LDS slot, row in the load's group
+                                          const FetchState<QA, QB>& st, const int32_t (&ca)[QA],
+                                          const int32_t (&cb)[QB], int qa0, int qb0, int32_t kbyte0) {
+  const int32_t rem = st.kbytes - kbyte0;
 #pragma unroll
   for (int i = 0; i < QA; ++i) {
-    const int q = wave * QA + i;                   // row group index within the tile
-    const int c = slot ^ F::swz(q * RPL + rig);    // global chunk this lane moves
-    const bool in = valid && (kbyte0 + c * 16 < kbytes);
-    const int32_t off = in ? a_lane_row + (int32_t)(RPL * q * lda) + c * 16 + kbyte0 : 0x7FFFFFF0;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(dst + q * 1024), 16, off,
-                                             0, 0, 0);
+    const int32_t off = ca[i] < rem ? st.offa[i] + kbyte0 : 0x7FFFFFF0;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(dst + (qa0 + i) * 1024),
+                                             16, off, 0, 0, 0);
   }
 #pragma unroll
   for (int i = 0; i < QB; ++i) {
-    const int q = wave * QB + i;
-    const int c = slot ^ F::swz(q * RPL + rig);
-    const bool in = valid && (kbyte0 + c * 16 < kbytes);
-    const int32_t off = in ? b_lane_row + (int32_t)(RPL * q * ldb) + c * 16 + kbyte0 : 0x7FFFFFF0;
+    const int32_t off = cb[i] < rem ? st.offb[i] + kbyte0 : 0x7FFFFFF0;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (__attribute__((address_space(3))) void*)(dst + TM * RB + q * 1024), 16, off, 0, 0, 0);
+        rb, (__attribute__((address_space(3))) void*)(dst + TM * RB + (qb0 + i) * 1024), 16, off, 0, 0, 0);
   }
 }
 
@@ -209,7 +211,8 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
   static_assert((NBUF - 2) * kDma < 64, "vmcnt counts up to 63");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // the wave index is uniform: keep it (and the load addresses built from it) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31;
   const int a_off = ((wave % WM) * (TM / WM) + r32) * RB;
   const int b_off = (TM + (wave / WM) * (TN / WN) + r32) * RB;
@@ -222,34 +225,53 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
   const int ks2 = kDual ? (p2.kbytes + RB - 1) / RB : 0;
   if (a_tile_end <= a_tile_begin || ks1 == 0) return;
 
-  const int rig = lane / F::kChunks;
-  const int32_t la1 = (int32_t)(rig * p1.lda), la2 = (int32_t)(rig * p2.lda);
-  const int32_t lb1 = (int32_t)(rig * p1.ldb), lb2 = (int32_t)(rig * p2.ldb);
+  // Load geometry: row group q (8 rows of 128 bytes) of the A tile is load
+  // qa0 + i of this wave; the lane moves row q * 8 + rig, swizzled chunk c.
+  constexpr int RPL = F::kRowsPerLoad;
+  constexpr int QA = TM / (RPL * NW), QB = TN / (RPL * NW);
+  static_assert(QA * RPL * NW == TM && QB * RPL * NW == TN, "tile rows must split evenly over the waves");
+  const int slot = lane % F::kChunks, rig = lane / F::kChunks;
+  const int qa0 = wave * QA, qb0 = wave * QB;
+  int32_t ca[QA], cb[QB];
+#pragma unroll
+  for (int i = 0; i < QA; ++i) ca[i] = (slot ^ F::swz((qa0 + i) * RPL + rig)) * 16;
+#pragma unroll
+  for (int i = 0; i < QB; ++i) cb[i] = (slot ^ F::swz((qb0 + i) * RPL + rig)) * 16;
   const __amdgpu_buffer_rsrc_t rb1 = make_rsrc(p1.B + b_row0 * p1.ldb, (p1.b_rows - b_row0) * p1.ldb);
   const __amdgpu_buffer_rsrc_t rb2 = make_rsrc(p2.B + b_row0 * p2.ldb, (p2.b_rows - b_row0) * p2.ldb);
 
-  // Fetch cursor: the stage issued next (tile ft, pair fp, stage fs). The
-  // loads pick their operand pair with selects, not branches, so that they
-  // stay in the MFMA block and can be interleaved with it; the cursor
-  // advances after it.
+  // Fetch cursor: the stage issued next (tile ft, pair fp, stage fs), and the
+  // state its loads use, rebuilt whenever the cursor leaves a pair's K extent.
   int ft = a_tile_begin, fp = 0, fs = 0;
-  auto issue = [&](char* dst) __attribute__((always_inline)) {
-    const bool valid = ft < a_tile_end;
+  FetchState<QA, QB> st;
+  __amdgpu_buffer_rsrc_t fra = rb1, frb = rb1;
+  auto refresh = [&]() __attribute__((always_inline)) {
     const bool second = kDual && fp != 0;
-    const int64_t a_row0 = (int64_t)(valid ? ft : a_tile_begin) * TM;
     const char* A = second ? p2.A : p1.A;
     const int64_t lda = second ? p2.lda : p1.lda, ldb = second ? p2.ldb : p1.ldb;
-    const int64_t a_rows = second ? p2.a_rows : p1.a_rows;
-    dma_stage<TM, TN, NW, RB>(dst, make_rsrc(A + a_row0 * lda, (a_rows - a_row0) * lda), second ? rb2 : rb1,
-                              second ? la2 : la1, second ? lb2 : lb1, lda, ldb, fs * RB,
-                              second ? p2.kbytes : p1.kbytes, valid, wave, lane);
+    const int64_t a_row0 = (int64_t)ft * TM;
+    const bool valid = ft < a_tile_end;
+    fra = make_rsrc(A + a_row0 * lda, valid ? ((second ? p2.a_rows : p1.a_rows) - a_row0) * lda : 0);
+    frb = valid ? (second ? rb2 : rb1) : make_rsrc(p1.B, 0);
+    st.kbytes = second ? p2.kbytes : p1.kbytes;
+#pragma unroll
+    for (int i = 0; i < QA; ++i) st.offa[i] = ((qa0 + i) * RPL + rig) * (int32_t)lda + ca[i];
+#pragma unroll
+    for (int i = 0; i < QB; ++i) st.offb[i] = ((qb0 + i) * RPL + rig) * (int32_t)ldb + cb[i];
+  };
+  auto issue = [&](char* dst) __attribute__((always_inline)) {
+    dma_stage<TM, RB, QA, QB>(dst, fra, frb, st, ca, cb, qa0, qb0, fs * RB);
   };
   auto advance = [&]() __attribute__((always_inline)) {
-    const bool wrap = fs + 1 == (fp == 0 ? ks1 : ks2);
-    const int nfp = (fp == 0 && ks2 > 0) ? 1 : 0;
-    ft += (wrap && nfp == 0) ? 1 : 0;
-    fs = wrap ? 0 : fs + 1;
-    fp = wrap ? nfp : fp;
+    if (fs + 1 == (fp == 0 ? ks1 : ks2)) {
+      const int nfp = (fp == 0 && ks2 > 0) ? 1 : 0;
+      ft += nfp == 0 ? 1 : 0;
+      fp = nfp;
+      fs = 0;
+      refresh();
+    } else {
+      ++fs;
+    }
   };
 
   // One ring step on buffer I: wait for its loads (the NBUF-2 later stages
@@ -286,6 +308,7 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
   zero_acc(acc1);
   if constexpr (kDual) zero_acc(acc2);
   // prologue: the first NBUF-1 stages
+  refresh();
   static_for<0, NBUF - 1>([&](auto I) __attribute__((always_inline)) {
     issue(lds.b[I]);
     advance();
