@@ -21,6 +21,10 @@ times the top-k paths instead, on the 248k-vocabulary 16k-token top-k
 workload: one step = kd_topk_fwd + kd_topk_bwd (three terms, all weights 1,
 labels given), or kd_tail_fwd + kd_tail_bwd (tail-bucket divergence; the
 support defaults to the beta rule); their CPU baseline is the oracle on 48 tokens.
+--teacher-dim 256 gives the teacher the shapes of its rank-256 factorisation
+([N, 256] hidden states, [V, 256] unembedding): the sweep's work depends on the
+shapes only, so the factors are drawn with the workload's recipe instead of
+being computed by an SVD.
 """
 from __future__ import annotations
 
@@ -64,6 +68,9 @@ def parse():
                     help="kd: the full-vocabulary divergence (default); topk / tail: the top-k paths")
     ap.add_argument("--k", type=int, default=64, help="top-k size for --path topk / tail")
     ap.add_argument("--support", type=int, default=None, help="KD_SUPPORT_* bits for --path tail")
+    ap.add_argument("--teacher-dim", type=int, default=None,
+                    help="teacher hidden size for --path topk / tail (256: the shapes of a rank-256 factorised "
+                         "teacher, drawn with the same recipe)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of a "
                          "'--calibrate-copy' run into the traffic record and exit")
@@ -377,7 +384,7 @@ def bench_topk(args):
 
     kd.load_library()
     torch.cuda.set_device(0)
-    w = kdsynth.make(5)
+    w = kdsynth.make(5, d_t=args.teacher_dim)
     N, V, ds, dt_, tau, k, beta = w.N, w.V, w.d_s, w.d_t, w.tau, args.k, args.beta
     args.chunk_v = args.chunk_v or kd.default_chunk(N, V)
     dev = [torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() for a in (w.h_s, w.W_s, w.h_t, w.W_t)]

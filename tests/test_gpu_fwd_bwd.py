@@ -366,3 +366,22 @@ def test_default_chunk_backward():
     assert torch.equal(t0, tc) and torch.equal(l0, lc)
     ref = O.kd_topk_bwd(*arrays, 8, 1.1, None, np.ones(N), np.ones(N), None, sel=out["idx"].cpu().numpy())
     assert_grad_rows(t0.cpu().numpy(), ref, name="topk dh_s (default chunk)")
+
+
+@pytest.mark.parametrize("N,V,ds,dt,dtype", [
+    (300, 5000, 8, 136, "bf16"),   # pair 1 is one stage, pair 2 three with a 16-byte tail; 20 vocabulary tiles
+    (130, 1100, 72, 8, "bf16"),    # the reverse, and a ragged last vocabulary tile
+    (257, 3000, 8, 8, "f32"),      # one stage per pair: the fetch runs two stages ahead across pairs and tiles
+    (64, 600, 264, 40, "f32"),
+])
+def test_stage_ring_fetch_boundaries(N, V, ds, dt, dtype):
+    """The stage ring rebuilds its fetch state when the cursor moves to the
+    other operand pair or to the next vocabulary tile, and fetches past a
+    block's last tile read nothing. K extents of one to five 128-byte stages
+    with ragged tails, several tiles per block, both dtypes; fwd and bwd at
+    beta = 1/2 (two forward sweeps) against the oracle."""
+    kd, torch = _kd()
+    _say(f"ring fetch N={N} V={V} d_s={ds} d_t={dt} {dtype}")
+    arrays = kdsynth.small_case(90 + ds + dt, N, V, ds, dt, dtype=dtype)
+    grad = np.random.default_rng(ds).uniform(-1, 2, size=N)
+    run_case(kd, torch, arrays, 0.5, 1.2, grad=grad, chunk_V=1024)
