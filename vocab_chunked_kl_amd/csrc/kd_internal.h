@@ -31,6 +31,10 @@ constexpr int kDhWN = 2;
 constexpr int kDhThreads = 64 * kDhWM * kDhWN;
 constexpr int kDhRB = 128;
 constexpr int kDhBuf = 2;
+// Token tile of the student-only gradient sweep of the top-k / tail backward
+// (one accumulator: the dh GEMM's tile, wave layout and ring).
+constexpr int kDenseT = 256;
+constexpr int kDenseThreads = kDhThreads;
 // Token tiles grouped together in the block order: the 32 blocks that run at
 // once on one XCD are 8 token tiles x 4 vocabulary splits, the split that
 // minimises the operand bytes its L2 fetches (measured best of 4, 8, 16).

@@ -543,10 +543,14 @@ struct DenseArgs {
   int64_t ldg, g_col0;
 };
 
-__global__ __launch_bounds__(kLogitThreads, 1) void dense_g_kernel(DenseArgs a) {
-  constexpr int TM = kTileV, TN = kTileT, WM = kLogitWM, WN = kLogitWN;
+// One operand pair and one accumulator, so the block takes the dh GEMM's
+// 256 x 256 tile (256 vocabulary entries x 256 tokens, 64 x 128 per wave) and
+// its ring of two 64 KiB stages: half the token-operand bytes per flop of the
+// two-accumulator logit tile.
+__global__ __launch_bounds__(kDenseThreads, 1) void dense_g_kernel(DenseArgs a) {
+  constexpr int TM = kTileV, TN = kDenseT, WM = kDhWM, WN = kDhWN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
-  KD_RING_LDS_N(TM, TN, kLogitRB, kLogitBuf);
+  KD_RING_LDS_N(TM, TN, kDhRB, kDhBuf);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
   block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_splits, tt, sp);
@@ -597,7 +601,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void dense_g_kernel(DenseArgs a) 
         }
     }
   };
-  sweep<true, TM, TN, WM, WN, kLogitBuf, kLogitRB, false>(a.ps, a.ps, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<true, TM, TN, WM, WN, kDhBuf, kDhRB, false>(a.ps, a.ps, (int64_t)tt * TN, vt0, vt1, lds, epi);
 }
 
 // The listed entries of one vocabulary chunk overwrite their G elements: one
@@ -1076,7 +1080,7 @@ static hipError_t run_list_chunks(const Plan& p, DenseArgs a, const int32_t* lis
     a.n_vtiles = ctiles;
     a.n_splits = ctiles;
     a.g_col0 = c0;
-    hipLaunchKernelGGL(dense_g_kernel, dim3(p.n_tok_tiles * ctiles), dim3(kLogitThreads), 0, st, a);
+    hipLaunchKernelGGL(dense_g_kernel, dim3(a.n_tok_tiles * ctiles), dim3(kDenseThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     f.c0 = c0;
     f.ccols = ccols;
@@ -1104,7 +1108,7 @@ static DenseArgs dense_args(const Plan& p, const void* h_s, const void* W_s, flo
   a.N = p.N;
   a.V = p.V;
   a.c2 = kLog2e / tau;
-  a.n_tok_tiles = p.n_tok_tiles;
+  a.n_tok_tiles = (int)((p.N + kDenseT - 1) / kDenseT);
   a.tiles_per_split = 1;
   a.G = G;
   a.ldg = (int64_t)chunk_V * 2;
