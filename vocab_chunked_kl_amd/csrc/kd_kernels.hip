@@ -981,6 +981,11 @@ hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
   return hipGetLastError();
 }
 
+static int bwd_tiles_per_block(const Plan& p, int ctiles) {
+  const int wide = (ctiles + kBwdTilesPerBlock - 1) / kBwdTilesPerBlock;
+  return (int64_t)p.n_tok_tiles * wide >= kBwdWideMinBlocks ? kBwdTilesPerBlock : 1;
+}
+
 hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   const int mode = io.beta == 1.f ? kModeRKL : (io.beta == 0.f ? kModeFKL : kModeJSD);
   const int64_t np = padded_tokens(p);
@@ -1000,7 +1005,6 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   la.GT = io.dW ? GT : nullptr;
   la.ldgt = np * p.esz;
   la.Np = np;
-  la.tiles_per_split = 1;
   const int n_d_tiles = (p.d_s + kTileDhD - 1) / kTileDhD;
   hipError_t e;
   auto transpose = [&](const void* src, char* dst, int64_t rows, int64_t c0, int64_t cols, int64_t pitch) {
@@ -1029,9 +1033,10 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
     const int64_t kcols = (int64_t)ctiles * kTileV;
     la.vt_offset = (int)(c0 / kTileV);
     la.n_vtiles = ctiles;
-    la.n_splits = ctiles;
+    la.tiles_per_split = bwd_tiles_per_block(p, ctiles);
+    la.n_splits = (ctiles + la.tiles_per_split - 1) / la.tiles_per_split;
     la.g_col0 = c0;
-    const dim3 grid(p.n_tok_tiles * ctiles);
+    const dim3 grid(p.n_tok_tiles * la.n_splits);
     e = p.bf16 ? launch_bwdg_mode<true>(mode, grid, la, st) : launch_bwdg_mode<false>(mode, grid, la, st);
     if (e != hipSuccess) return e;
     if (io.dh) {
