@@ -314,6 +314,28 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
 // ---------------------------------------------------------------------------
 // Backward, step 1: G[n, v - c0] = grad[n] / tau * dloss_n / ds_v for one chunk.
 // ---------------------------------------------------------------------------
+
+// Store 16 consecutive bf16 gradient entries of one token from a 32 x 32 MFMA
+// block: rows 16 pr .. 16 pr + 15, where lane l holds rows 0-3 of each 8-row
+// group and lane l + 32 rows 4-7 (w2[h]: group 2 pr + h, packed in pairs).
+// One permlane32 swap per dword leaves lane l with rows 0-7 and lane l + 32
+// with rows 8-15, each written with one 16-byte store. Every lane takes part
+// in the swaps; the store is skipped for tokens past N (lanes l and l + 32
+// hold the same token).
+__device__ __forceinline__ void store_g16(char* G, int64_t ldg, int64_t n, int64_t N, int64_t col0,
+                                          const u32x2 (&w2)[2], int lane) {
+  const auto sx = __builtin_amdgcn_permlane32_swap(w2[0].x, w2[1].x, false, false);
+  const auto sy = __builtin_amdgcn_permlane32_swap(w2[0].y, w2[1].y, false, false);
+  if (G && n < N) {
+    u32x4 w;
+    w.x = sx[0];
+    w.y = sy[0];
+    w.z = sx[1];
+    w.w = sy[1];
+    *reinterpret_cast<u32x4*>(G + n * ldg + (col0 + 8 * (lane >> 5)) * 2) = w;
+  }
+}
+
 template <bool kBf16, int MODE>
 __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
   constexpr int TM = kTileV, TN = kTileT, WM = kLogitWM, WN = kLogitWN;
@@ -351,53 +373,54 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
+        for (int pr = 0; pr < 2; ++pr) {
           __builtin_amdgcn_sched_barrier(0);  // keep the groups apart: bounds register pressure
-          float g4[4];
+          u32x2 w2[2];                        // row groups 2 pr and 2 pr + 1, packed bf16
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = rg * 4 + e;
-            const int64_t v = vrow0 + mb * 32 + acc_row(r, lane);
-            const float x = zs[mb][nb][r], y = zt[mb][nb][r];
-            const float lq2 = fmaf(x, c2, -Ls2[nb]);
-            const float q = fast_exp2(lq2);
-            float g;
-            if constexpr (MODE == kModeRKL) {
-              g = q * fmaf(x - y, inv_tau, -K1[nb]);
-            } else if constexpr (MODE == kModeFKL) {
-              g = q - fast_exp2(fmaf(y, c2, -Lt2[nb]));
-            } else {
-              const float lp2 = fmaf(y, c2, -Lt2[nb]);
-              const float m = beta * fast_exp2(lp2) + omb * q;
-              g = (m > 1e-37f) ? omb * q * fmaf(lq2 - fast_log2(m), kLn2, -K1[nb]) : 0.f;
-            }
-            g4[e] = (v < a.V) ? g * gsc[nb] : 0.f;
-          }
-          if (a.GT && n < a.Np) {
-            // transposed copy for the weight gradient: token-contiguous rows;
-            // tokens past N carry g = 0, so the padding columns are zeros
+          for (int h = 0; h < 2; ++h) {
+            const int rg = 2 * pr + h;
+            float g4[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int64_t row = vrow0 + mb * 32 + 8 * rg + 4 * (lane >> 5) + e - a.g_col0;
-              char* dst = a.GT + row * a.ldgt;
-              if constexpr (kBf16)
-                *reinterpret_cast<uint16_t*>(dst + n * 2) = (uint16_t)f32_to_bf16_bits(g4[e]);
-              else
-                *reinterpret_cast<float*>(dst + n * 4) = g4[e];
+              const int r = rg * 4 + e;
+              const int64_t v = vrow0 + mb * 32 + acc_row(r, lane);
+              const float x = zs[mb][nb][r], y = zt[mb][nb][r];
+              const float lq2 = fmaf(x, c2, -Ls2[nb]);
+              const float q = fast_exp2(lq2);
+              float g;
+              if constexpr (MODE == kModeRKL) {
+                g = q * fmaf(x - y, inv_tau, -K1[nb]);
+              } else if constexpr (MODE == kModeFKL) {
+                g = q - fast_exp2(fmaf(y, c2, -Lt2[nb]));
+              } else {
+                const float lp2 = fmaf(y, c2, -Lt2[nb]);
+                const float m = beta * fast_exp2(lp2) + omb * q;
+                g = (m > 1e-37f) ? omb * q * fmaf(lq2 - fast_log2(m), kLn2, -K1[nb]) : 0.f;
+              }
+              g4[e] = (v < a.V) ? g * gsc[nb] : 0.f;
             }
-          }
-          if (a.G && n < a.N) {
-            const int64_t col = vrow0 + mb * 32 + 8 * rg + 4 * (lane >> 5) - a.g_col0;
-            char* dst = a.G + n * a.ldg;
+            if (a.GT && n < a.Np) {
+              // transposed copy for the weight gradient: token-contiguous rows;
+              // tokens past N carry g = 0, so the padding columns are zeros
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int64_t row = vrow0 + mb * 32 + 8 * rg + 4 * (lane >> 5) + e - a.g_col0;
+                char* dst = a.GT + row * a.ldgt;
+                if constexpr (kBf16)
+                  *reinterpret_cast<uint16_t*>(dst + n * 2) = (uint16_t)f32_to_bf16_bits(g4[e]);
+                else
+                  *reinterpret_cast<float*>(dst + n * 4) = g4[e];
+              }
+            }
             if constexpr (kBf16) {
-              u32x2 w;
-              w.x = f32_to_bf16_bits(g4[0]) | (f32_to_bf16_bits(g4[1]) << 16);
-              w.y = f32_to_bf16_bits(g4[2]) | (f32_to_bf16_bits(g4[3]) << 16);
-              *reinterpret_cast<u32x2*>(dst + col * 2) = w;
-            } else {
-              *reinterpret_cast<floatx4*>(dst + col * 4) = floatx4{g4[0], g4[1], g4[2], g4[3]};
+              w2[h].x = f32_to_bf16_bits(g4[0]) | (f32_to_bf16_bits(g4[1]) << 16);
+              w2[h].y = f32_to_bf16_bits(g4[2]) | (f32_to_bf16_bits(g4[3]) << 16);
+            } else if (a.G && n < a.N) {
+              const int64_t col = vrow0 + mb * 32 + 8 * rg + 4 * (lane >> 5) - a.g_col0;
+              *reinterpret_cast<floatx4*>(a.G + n * a.ldg + col * 4) = floatx4{g4[0], g4[1], g4[2], g4[3]};
             }
           }
+          if constexpr (kBf16) store_g16(a.G, a.ldg, n, a.N, vrow0 + mb * 32 + 16 * pr - a.g_col0, w2, lane);
         }
     }
   };
@@ -580,24 +603,24 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_g_kernel(DenseArgs a) 
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          float g4[4];
+        for (int pr = 0; pr < 2; ++pr) {
+          u32x2 w2[2];  // row groups 2 pr and 2 pr + 1, packed bf16
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = rg * 4 + e;
-            const int64_t v = vrow0 + mb * 32 + acc_row(r, lane);
-            const float zb = __builtin_bit_cast(float, f32_to_bf16_bits(zs[mb][nb][r]) << 16);
-            const float q = fast_exp2(fmaf(zb, a.c2, -Ls2[nb]));
-            const float rr = fast_exp2(fmaf(zb, kLog2e, -L12[nb]));
-            g4[e] = (v < a.V) ? fmaf(A[nb], q, C[nb] * rr) : 0.f;
+          for (int h = 0; h < 2; ++h) {
+            float g4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = (2 * pr + h) * 4 + e;
+              const int64_t v = vrow0 + mb * 32 + acc_row(r, lane);
+              const float zb = __builtin_bit_cast(float, f32_to_bf16_bits(zs[mb][nb][r]) << 16);
+              const float q = fast_exp2(fmaf(zb, a.c2, -Ls2[nb]));
+              const float rr = fast_exp2(fmaf(zb, kLog2e, -L12[nb]));
+              g4[e] = (v < a.V) ? fmaf(A[nb], q, C[nb] * rr) : 0.f;
+            }
+            w2[h].x = f32_to_bf16_bits(g4[0]) | (f32_to_bf16_bits(g4[1]) << 16);
+            w2[h].y = f32_to_bf16_bits(g4[2]) | (f32_to_bf16_bits(g4[3]) << 16);
           }
-          if (n < a.N) {
-            const int64_t col = vrow0 + mb * 32 + 8 * rg + 4 * (lane >> 5) - a.g_col0;
-            u32x2 w;
-            w.x = f32_to_bf16_bits(g4[0]) | (f32_to_bf16_bits(g4[1]) << 16);
-            w.y = f32_to_bf16_bits(g4[2]) | (f32_to_bf16_bits(g4[3]) << 16);
-            *reinterpret_cast<u32x2*>(a.G + n * a.ldg + col * 2) = w;
-          }
+          store_g16(a.G, a.ldg, n, a.N, vrow0 + mb * 32 + 16 * pr - a.g_col0, w2, lane);
         }
     }
   };
