@@ -20,6 +20,12 @@ constexpr int kLogitWN = 2;
 constexpr int kLogitThreads = 64 * kLogitWM * kLogitWN;
 constexpr int kLogitRB = 128;
 constexpr int kLogitBuf = 3;
+// Forward sweep for at most 64 tokens: the token tile shrinks to 64 rows, so
+// a stage is 40 KiB and a ring of four fills the 160 KiB of LDS: three
+// stages of unembedding rows in flight per CU instead of two, where the
+// sweep streams W from HBM.
+constexpr int kSmallT = 64;
+constexpr int kSmallBuf = 4;
 // Token tile of the top-k sweep (its per-token selection state lives in LDS).
 constexpr int kTopkT = 128;
 // dh tile: 256 tokens x 256 hidden units, 4 x 2 waves (64 x 128 per wave, one

@@ -40,16 +40,17 @@ namespace {
 
 constexpr float kNegInf = -INFINITY;
 
-// The NBUF (2 or 3) LDS stage buffers of a sweep ring, as separate objects.
+// The NBUF (2 to 4) LDS stage buffers of a sweep ring, as separate objects.
 #define KD_RING_LDS_N(TM, TN, RB, NBUF)                                                             \
   __shared__ __attribute__((aligned(16))) char ring0_[Ring<TM, TN, RB>::kBytes];                    \
   __shared__ __attribute__((aligned(16))) char ring1_[Ring<TM, TN, RB>::kBytes];                    \
   __shared__ __attribute__((aligned(16))) char ring2_[(NBUF) > 2 ? Ring<TM, TN, RB>::kBytes : 16]; \
-  const RingLds<NBUF> lds = ring_of<NBUF>(ring0_, ring1_, ring2_)
+  __shared__ __attribute__((aligned(16))) char ring3_[(NBUF) > 3 ? Ring<TM, TN, RB>::kBytes : 16]; \
+  const RingLds<NBUF> lds = ring_of<NBUF>(ring0_, ring1_, ring2_, ring3_)
 
 template <int NBUF>
-__device__ __forceinline__ RingLds<NBUF> ring_of(char* r0, char* r1, char* r2) {
-  char* all[3] = {r0, r1, r2};
+__device__ __forceinline__ RingLds<NBUF> ring_of(char* r0, char* r1, char* r2, char* r3) {
+  char* all[4] = {r0, r1, r2, r3};
   RingLds<NBUF> r;
 #pragma unroll
   for (int i = 0; i < NBUF; ++i) r.b[i] = all[i];
@@ -104,11 +105,12 @@ __device__ __forceinline__ void merge_record(float& ms, float& ls, float& mt, fl
 // Forward sweep. MODE: kModeFKL / kModeRKL (loss in one sweep), kModeLSE (only
 // the log-sum-exps, first JSD sweep), kModeJSD (mixture sums given the LSEs).
 // ---------------------------------------------------------------------------
-template <bool kBf16, int MODE>
+template <bool kBf16, int MODE, bool kSmall>
 __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
-  constexpr int TM = kTileV, TN = kTileT, WM = kLogitWM, WN = kLogitWN;
+  constexpr int TM = kTileV, TN = kSmall ? kSmallT : kTileT, WM = kLogitWM, WN = kLogitWN;
+  constexpr int NBUF = kSmall ? kSmallBuf : kLogitBuf;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
-  KD_RING_LDS_N(TM, TN, kLogitRB, kLogitBuf);
+  KD_RING_LDS_N(TM, TN, kLogitRB, NBUF);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
   block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_splits, tt, sp);
@@ -202,7 +204,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
       }
     }
   };
-  sweep<kBf16, TM, TN, WM, WN, kLogitBuf, kLogitRB, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<kBf16, TM, TN, WM, WN, NBUF, kLogitRB, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 
   // Lanes l and l ^ 32 hold the same tokens (other vocabulary rows).
 #pragma unroll
@@ -219,8 +221,10 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
   }
   // The WM waves with the same wn hold the vocabulary slices of the same
   // tokens: waves wm > 0 publish their records, wave wm = 0 merges them.
+  // The ring is drained: its first buffer holds the records.
   constexpr int kF = MODE == kModeJSD ? kJsdFields : kFwdFields;
-  __shared__ float red[(WM > 1 ? WM - 1 : 1) * kF * TN];
+  static_assert((WM - 1) * kF * TN * sizeof(float) <= Ring<TM, TN, kLogitRB>::kBytes, "records fit one stage");
+  float* red = reinterpret_cast<float*>(lds.b[0]);
   if (wm > 0 && lane < 32) {
     float* r = red + (wm - 1) * kF * TN;
 #pragma unroll
@@ -821,12 +825,21 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const char* __restrict__
 }
 
 template <bool kBf16>
-hipError_t launch_fwd_mode(int mode, dim3 grid, const LogitArgs& la, hipStream_t st) {
-  switch (mode) {
-    case kModeFKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeFKL>), grid, dim3(kLogitThreads), 0, st, la); break;
-    case kModeRKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeRKL>), grid, dim3(kLogitThreads), 0, st, la); break;
-    case kModeLSE: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeLSE>), grid, dim3(kLogitThreads), 0, st, la); break;
-    default: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeJSD>), grid, dim3(kLogitThreads), 0, st, la); break;
+hipError_t launch_fwd_mode(int mode, bool small, dim3 grid, const LogitArgs& la, hipStream_t st) {
+  if (small) {
+    switch (mode) {
+      case kModeFKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeFKL, true>), grid, dim3(kLogitThreads), 0, st, la); break;
+      case kModeRKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeRKL, true>), grid, dim3(kLogitThreads), 0, st, la); break;
+      case kModeLSE: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeLSE, true>), grid, dim3(kLogitThreads), 0, st, la); break;
+      default: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeJSD, true>), grid, dim3(kLogitThreads), 0, st, la); break;
+    }
+  } else {
+    switch (mode) {
+      case kModeFKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeFKL, false>), grid, dim3(kLogitThreads), 0, st, la); break;
+      case kModeRKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeRKL, false>), grid, dim3(kLogitThreads), 0, st, la); break;
+      case kModeLSE: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeLSE, false>), grid, dim3(kLogitThreads), 0, st, la); break;
+      default: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeJSD, false>), grid, dim3(kLogitThreads), 0, st, la); break;
+    }
   }
   return hipGetLastError();
 }
@@ -973,10 +986,11 @@ hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
   la.part = static_cast<float*>(io.workspace);
   const dim3 grid(p.n_tok_tiles * p.n_splits);
   const dim3 mgrid((unsigned)((p.N + 255) / 256));
+  const bool small = p.N <= kSmallT;  // one token tile either way; the 64-row tile has a deeper ring
   hipError_t e;
   if (io.beta == 0.f || io.beta == 1.f) {
     const int mode = io.beta == 1.f ? kModeRKL : kModeFKL;
-    e = p.bf16 ? launch_fwd_mode<true>(mode, grid, la, st) : launch_fwd_mode<false>(mode, grid, la, st);
+    e = p.bf16 ? launch_fwd_mode<true>(mode, small, grid, la, st) : launch_fwd_mode<false>(mode, small, grid, la, st);
     if (e != hipSuccess) return e;
     if (mode == kModeRKL)
       hipLaunchKernelGGL((merge_kernel<kModeRKL>), mgrid, dim3(256), 0, st, la.part, p.n_splits, p.N, la.inv_tau,
@@ -987,7 +1001,7 @@ hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
     return hipGetLastError();
   }
   // 0 < beta < 1: sweep 1 -> LSEs, sweep 2 -> mixture sums.
-  e = p.bf16 ? launch_fwd_mode<true>(kModeLSE, grid, la, st) : launch_fwd_mode<false>(kModeLSE, grid, la, st);
+  e = p.bf16 ? launch_fwd_mode<true>(kModeLSE, small, grid, la, st) : launch_fwd_mode<false>(kModeLSE, small, grid, la, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<kModeLSE>), mgrid, dim3(256), 0, st, la.part, p.n_splits, p.N, la.inv_tau,
                      io.loss, io.lse_s, io.lse_t, io.aux);
@@ -997,7 +1011,7 @@ hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
       kFwdFields * (size_t)p.n_splits * (size_t)p.N * sizeof(float), 256));
   lj.lse_s = io.lse_s;
   lj.lse_t = io.lse_t;
-  e = p.bf16 ? launch_fwd_mode<true>(kModeJSD, grid, lj, st) : launch_fwd_mode<false>(kModeJSD, grid, lj, st);
+  e = p.bf16 ? launch_fwd_mode<true>(kModeJSD, small, grid, lj, st) : launch_fwd_mode<false>(kModeJSD, small, grid, lj, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<kModeJSD>), mgrid, dim3(256), 0, st, lj.part, p.n_splits, p.N, la.inv_tau,
                      io.loss, io.lse_s, io.lse_t, io.aux);

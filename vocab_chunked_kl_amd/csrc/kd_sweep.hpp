@@ -11,7 +11,7 @@
 // both for the same (vocabulary, token) tile, as the block logit rebuild of
 // the Nitrobrew notes ("Nitrobrew 的两个动作") needs them side by side.
 //
-// Pipeline: a ring of NBUF (2 or 3) LDS stage buffers (RB = 128 bytes of K
+// Pipeline: a ring of NBUF (2 to 4) LDS stage buffers (RB = 128 bytes of K
 // per row each) filled by direct-to-LDS buffer loads (no staging registers, no LDS store
 // instructions). While stage g is multiplied, the loads of stages g+1 ..
 // g+NBUF-2 are in flight and stage g+NBUF-1 is being issued; one barrier per
@@ -202,7 +202,7 @@ struct RingLds {
 template <bool kBf16, int TM, int TN, int WM, int WN, int NBUF, int RB, bool kDual, class Epi>
 __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, int64_t b_row0, int a_tile_begin,
                                       int a_tile_end, const RingLds<NBUF>& lds, Epi&& epi) {
-  static_assert(NBUF == 2 || NBUF == 3, "ring of two or three stage buffers");
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring of two to four stage buffers");
   using F = RowFmt<RB>;
   constexpr int NW = WM * WN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
