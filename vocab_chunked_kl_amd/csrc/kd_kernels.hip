@@ -456,6 +456,44 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ W,
   }
 }
 
+// The bf16 transpose with 16-byte global accesses (d is a multiple of 8, so
+// every 8-element run of a row is 16-byte aligned): per 64 x 64 tile each
+// thread loads two 8-element runs of W rows, the tile goes through LDS with
+// a 65-element row pitch (the column reads of a wave then hit 32 distinct
+// banks), and each thread writes two 8-element runs of WT rows.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* __restrict__ W, uint16_t* __restrict__ WT,
+                                                             int64_t V, int32_t d, int64_t c0, int64_t pitch) {
+  __shared__ uint16_t tile[64][65];
+  const int64_t j0 = (int64_t)blockIdx.x * 64;
+  const int64_t d0 = (int64_t)blockIdx.y * 64;
+  const int c = threadIdx.x & 7, r = threadIdx.x >> 3;  // 8-element run, row (0..31)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int jr = r + 32 * h;
+    const int64_t v = c0 + j0 + jr, dd = d0 + 8 * c;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (v < V && dd < d) w = *reinterpret_cast<const u32x4*>(W + v * d + dd);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[jr][8 * c + 2 * e] = (uint16_t)(w[e] & 0xFFFFu);
+      tile[jr][8 * c + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int dr = r + 32 * h;
+    const int64_t dd = d0 + dr;
+    if (dd < d) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        w[e] = (uint32_t)tile[8 * c + 2 * e][dr] | ((uint32_t)tile[8 * c + 2 * e + 1][dr] << 16);
+      *reinterpret_cast<u32x4*>(WT + dd * pitch + j0 + 8 * c) = w;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Backward, step 3: dh[n, d] (+)= sum_j G[n, j] WsT[d, j] over one chunk, and
 // dW_s[c0 + j, d] = sum_n GT[j, n] hsT[d, n].
@@ -1047,7 +1085,7 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   auto transpose = [&](const void* src, char* dst, int64_t rows, int64_t c0, int64_t cols, int64_t pitch) {
     const dim3 tgrid((unsigned)(cols / 64), (unsigned)((p.d_s + 63) / 64));
     if (p.bf16)
-      hipLaunchKernelGGL(transpose_kernel<uint16_t>, tgrid, dim3(256), 0, st, static_cast<const uint16_t*>(src),
+      hipLaunchKernelGGL(transpose_bf16_kernel, tgrid, dim3(256), 0, st, static_cast<const uint16_t*>(src),
                          reinterpret_cast<uint16_t*>(dst), rows, p.d_s, c0, pitch);
     else
       hipLaunchKernelGGL(transpose_kernel<float>, tgrid, dim3(256), 0, st, static_cast<const float*>(src),
@@ -1129,7 +1167,7 @@ static hipError_t run_list_chunks(const Plan& p, DenseArgs a, const int32_t* lis
     hipLaunchKernelGGL(g_fix_kernel, dim3(fix_blocks), dim3(256), 0, st, f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 tgrid((unsigned)(kcols / 64), (unsigned)((p.d_s + 63) / 64));
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, tgrid, dim3(256), 0, st, static_cast<const uint16_t*>(W_s),
+    hipLaunchKernelGGL(transpose_bf16_kernel, tgrid, dim3(256), 0, st, static_cast<const uint16_t*>(W_s),
                        reinterpret_cast<uint16_t*>(WsT), p.V, p.d_s, c0, (int64_t)chunk_V);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     DhArgs da{};
