@@ -340,11 +340,12 @@ __device__ __forceinline__ void store_g16(char* G, int64_t ldg, int64_t n, int64
   }
 }
 
-template <bool kBf16, int MODE>
+template <bool kBf16, int MODE, bool kSmall>
 __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
-  constexpr int TM = kTileV, TN = kTileT, WM = kLogitWM, WN = kLogitWN;
+  constexpr int TM = kTileV, TN = kSmall ? kSmallT : kTileT, WM = kLogitWM, WN = kLogitWN;
+  constexpr int NBUF = kSmall ? kSmallBuf : kLogitBuf;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
-  KD_RING_LDS_N(TM, TN, kLogitRB, kLogitBuf);
+  KD_RING_LDS_N(TM, TN, kLogitRB, NBUF);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   int tt, sp;
   block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_splits, tt, sp);
@@ -428,7 +429,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
         }
     }
   };
-  sweep<kBf16, TM, TN, WM, WN, kLogitBuf, kLogitRB, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<kBf16, TM, TN, WM, WN, NBUF, kLogitRB, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 }
 
 // ---------------------------------------------------------------------------
@@ -883,11 +884,19 @@ hipError_t launch_fwd_mode(int mode, bool small, dim3 grid, const LogitArgs& la,
 }
 
 template <bool kBf16>
-hipError_t launch_bwdg_mode(int mode, dim3 grid, const LogitArgs& la, hipStream_t st) {
-  switch (mode) {
-    case kModeFKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeFKL>), grid, dim3(kLogitThreads), 0, st, la); break;
-    case kModeRKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeRKL>), grid, dim3(kLogitThreads), 0, st, la); break;
-    default: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeJSD>), grid, dim3(kLogitThreads), 0, st, la); break;
+hipError_t launch_bwdg_mode(int mode, bool small, dim3 grid, const LogitArgs& la, hipStream_t st) {
+  if (small) {
+    switch (mode) {
+      case kModeFKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeFKL, true>), grid, dim3(kLogitThreads), 0, st, la); break;
+      case kModeRKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeRKL, true>), grid, dim3(kLogitThreads), 0, st, la); break;
+      default: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeJSD, true>), grid, dim3(kLogitThreads), 0, st, la); break;
+    }
+  } else {
+    switch (mode) {
+      case kModeFKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeFKL, false>), grid, dim3(kLogitThreads), 0, st, la); break;
+      case kModeRKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeRKL, false>), grid, dim3(kLogitThreads), 0, st, la); break;
+      default: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeJSD, false>), grid, dim3(kLogitThreads), 0, st, la); break;
+    }
   }
   return hipGetLastError();
 }
@@ -915,6 +924,24 @@ LogitArgs logit_args(const Plan& p, const void* h_s, const void* W_s, const void
 // ---------------------------------------------------------------------------
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Few token tiles: a logit sweep streams W from HBM and its time is about
+// (waves of workgroups over the 256 CUs) x (tiles per workgroup + the fixed
+// cost of one, ~1.5 tiles); the tiles per workgroup that minimise it (the
+// measured best for the forward at 64..512 tokens).
+static int tiles_per_block_few_tokens(int n_tok_tiles, int n_vtiles) {
+  int tps = 1;
+  double best = 1e30;
+  for (int t = 1; t <= 8; ++t) {
+    const int64_t blocks = (int64_t)n_tok_tiles * ((n_vtiles + t - 1) / t);
+    const double cost = (double)((blocks + 255) / 256) * (t + 1.5);
+    if (cost < best) {
+      best = cost;
+      tps = t;
+    }
+  }
+  return tps;
+}
+
 Plan make_plan(int64_t N, int64_t V, int32_t d_s, int32_t d_t, bool bf16) {
   Plan p;
   p.N = N;
@@ -925,22 +952,7 @@ Plan make_plan(int64_t N, int64_t V, int32_t d_s, int32_t d_t, bool bf16) {
   p.esz = bf16 ? 2 : 4;
   p.n_tok_tiles = (int)((N + kTileT - 1) / kTileT);
   p.n_vtiles = (int)((V + kTileV - 1) / kTileV);
-  int tps = kFwdTilesPerBlock;
-  if (p.n_tok_tiles <= 4) {
-    // few token tiles: the forward streams W from HBM and its time is about
-    // (waves of workgroups over the 256 CUs) x (tiles per workgroup + the
-    // fixed cost of one, ~1.5 tiles); pick the tiles per workgroup that
-    // minimise it (the measured best at 64..512 tokens)
-    double best = 1e30;
-    for (int t = 1; t <= 8; ++t) {
-      const int64_t blocks = (int64_t)p.n_tok_tiles * ((p.n_vtiles + t - 1) / t);
-      const double cost = (double)((blocks + 255) / 256) * (t + 1.5);
-      if (cost < best) {
-        best = cost;
-        tps = t;
-      }
-    }
-  }
+  const int tps = p.n_tok_tiles <= 4 ? tiles_per_block_few_tokens(p.n_tok_tiles, p.n_vtiles) : kFwdTilesPerBlock;
   p.tiles_per_split = tps < p.n_vtiles ? tps : p.n_vtiles;
   p.n_splits = (p.n_vtiles + p.tiles_per_split - 1) / p.tiles_per_split;
   return p;
@@ -1057,6 +1069,7 @@ hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
 }
 
 static int bwd_tiles_per_block(const Plan& p, int ctiles) {
+  if (p.n_tok_tiles <= 4) return tiles_per_block_few_tokens(p.n_tok_tiles, ctiles);
   const int wide = (ctiles + kBwdTilesPerBlock - 1) / kBwdTilesPerBlock;
   return (int64_t)p.n_tok_tiles * wide >= kBwdWideMinBlocks ? kBwdTilesPerBlock : 1;
 }
@@ -1071,6 +1084,10 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   float* part = reinterpret_cast<float*>(static_cast<char*>(io.workspace) +
                                          bwd_base_bytes(p, io.chunk_V, io.dW != nullptr));
   LogitArgs la = logit_args(p, io.h_s, io.W_s, io.h_t, io.W_t, io.tau, io.beta);
+  // Up to 64 tokens the 64-row tile with a deeper ring (one token tile either
+  // way); not with dW_s, whose transposed gradient copy must also zero the
+  // token columns 64..127 of the 128-padded token extent.
+  const bool small = p.N <= kSmallT && io.dW == nullptr;
   la.lse_s = io.lse_s;
   la.lse_t = io.lse_t;
   la.aux = io.aux;
@@ -1112,7 +1129,7 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
     la.n_splits = (ctiles + la.tiles_per_split - 1) / la.tiles_per_split;
     la.g_col0 = c0;
     const dim3 grid(p.n_tok_tiles * la.n_splits);
-    e = p.bf16 ? launch_bwdg_mode<true>(mode, grid, la, st) : launch_bwdg_mode<false>(mode, grid, la, st);
+    e = p.bf16 ? launch_bwdg_mode<true>(mode, small, grid, la, st) : launch_bwdg_mode<false>(mode, small, grid, la, st);
     if (e != hipSuccess) return e;
     if (io.dh) {
       // dh_s (+)= G . W_s[chunk], with the chunk of W_s transposed to [d_s][chunk]
