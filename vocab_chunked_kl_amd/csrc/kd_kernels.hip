@@ -517,11 +517,16 @@ struct DhArgs {
   float* part;
 };
 
-template <bool kBf16>
+template <bool kBf16, bool kSmall>
 __global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
-  constexpr int TM = kTileDhT, TN = kTileDhD, WM = kDhWM, WN = kDhWN;
+  // kSmall (at most 64 output rows): a 64-row tile on 2 x 4 waves with a ring
+  // of four 40 KiB stages, three stages of the B operand in flight per CU
+  // instead of one.
+  constexpr int TM = kSmall ? kSmallT : kTileDhT, TN = kTileDhD;
+  constexpr int WM = kSmall ? 2 : kDhWM, WN = kSmall ? 4 : kDhWN;
+  constexpr int NBUF = kSmall ? kSmallBuf : kDhBuf;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
-  KD_RING_LDS_N(TM, TN, kDhRB, kDhBuf);
+  KD_RING_LDS_N(TM, TN, kDhRB, NBUF);
   const int L0 = xcd_remap(blockIdx.x, gridDim.x);
   const int per_split = a.n_tok_tiles * a.n_d_tiles;
   const int ks = L0 / per_split;  // 0 unless the contraction is split
@@ -570,7 +575,7 @@ __global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
         }
     }
   };
-  sweep<kBf16, TM, TN, WM, WN, kDhBuf, kDhRB, false>(pd, pd, (int64_t)dt * TN, tt, tt + 1, lds, epi);
+  sweep<kBf16, TM, TN, WM, WN, NBUF, kDhRB, false>(pd, pd, (int64_t)dt * TN, tt, tt + 1, lds, epi);
 }
 
 // dh (=|+=) the sum of the split contraction's partial tiles, in split order.
@@ -1015,10 +1020,15 @@ static hipError_t launch_dh(const Plan& p, bool bf16, DhArgs da, int32_t chunk_V
     da.part = part;
   }
   const dim3 grid((unsigned)(n_tok_tiles * n_d_tiles * da.n_ksplit));
-  if (bf16)
-    hipLaunchKernelGGL(dh_kernel<true>, grid, dim3(kDhThreads), 0, st, da);
+  const bool small = p.N <= kSmallT;  // one token tile either way
+  if (bf16 && small)
+    hipLaunchKernelGGL((dh_kernel<true, true>), grid, dim3(kDhThreads), 0, st, da);
+  else if (bf16)
+    hipLaunchKernelGGL((dh_kernel<true, false>), grid, dim3(kDhThreads), 0, st, da);
+  else if (small)
+    hipLaunchKernelGGL((dh_kernel<false, true>), grid, dim3(kDhThreads), 0, st, da);
   else
-    hipLaunchKernelGGL(dh_kernel<false>, grid, dim3(kDhThreads), 0, st, da);
+    hipLaunchKernelGGL((dh_kernel<false, false>), grid, dim3(kDhThreads), 0, st, da);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || da.n_ksplit == 1) return e;
   const int64_t count = p.N * (int64_t)p.d_s;
@@ -1112,9 +1122,9 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   auto gemm = [&](const DhArgs& da, int n_row_tiles) {
     const dim3 dgrid(n_row_tiles * n_d_tiles);
     if (p.bf16)
-      hipLaunchKernelGGL(dh_kernel<true>, dgrid, dim3(kDhThreads), 0, st, da);
+      hipLaunchKernelGGL((dh_kernel<true, false>), dgrid, dim3(kDhThreads), 0, st, da);
     else
-      hipLaunchKernelGGL(dh_kernel<false>, dgrid, dim3(kDhThreads), 0, st, da);
+      hipLaunchKernelGGL((dh_kernel<false, false>), dgrid, dim3(kDhThreads), 0, st, da);
     return hipGetLastError();
   };
   // h_s transposed once ([d_s][Np], zero past N): the token-contiguous B operand of dW
