@@ -36,6 +36,7 @@ constexpr float kNegInf = -INFINITY;
 constexpr int kTopkSplit = 65536;
 constexpr int kCandCap = 16;       // candidate buffer entries per token per round (one list)
 constexpr int kCandCap2 = 12;      // the same with two lists (both models ranked at once)
+constexpr int kInsertMax = 6;      // a full list takes up to this many candidates by insertion
 constexpr int kTopkFields = 6;     // m_s, l_s, m_t, l_t, m_1, l_1 (untempered student)
 
 struct TopkArgs {
@@ -145,6 +146,26 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
     const int cb = min(cntB[li][t], CAP);
     const int total = cs + cb;
     uint32_t* Sg = (li ? a.lists2 : a.lists) + ((int64_t)sp * a.N + (int64_t)tt * TN + t) * K;  // token < N
+    if (cs == K && cb <= kInsertMax) {
+      // a full list and a few candidates (the usual case once a split is
+      // under way): insert them one at a time. A candidate's rank is the
+      // number of list words above it (words are distinct); the words below
+      // move down one lane and the last one drops out.
+      uint32_t e = lane < K ? Sg[lane] : 0u;
+      for (int i = 0; i < cb; ++i) {
+        const uint32_t c = B[li][t][i];
+        const int rank = __popcll(__ballot(lane < K && e > c));
+        const uint32_t up = __shfl(e, lane > 0 ? lane - 1 : 0);
+        e = lane < rank ? e : (lane == rank ? c : up);
+      }
+      if (lane < K) Sg[lane] = e;
+      const uint32_t th = __shfl(e, K - 1);
+      if (lane == 0) {
+        cntB[li][t] = 0;
+        theta[li][t] = th;
+      }
+      return;
+    }
     uint32_t e0 = lane < cs ? Sg[lane] : (lane - cs < cb ? B[li][t][lane - cs] : 0u);
     const int j1 = lane + 64;
     uint32_t e1 = j1 - cs < cb ? B[li][t][j1 - cs] : 0u;  // cs <= 64 <= j1
