@@ -315,6 +315,68 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   }
 }
 
+// The same merge with one wave per token (four per workgroup), for few tokens,
+// where one thread per token leaves the GPU idle: lane l merges slices l,
+// l + 64, ..., then a butterfly over the lanes merges the 64 partial records
+// in a fixed order.
+template <int MODE>
+__global__ __launch_bounds__(256) void merge_wave_kernel(const float* __restrict__ part, int n_splits, int64_t N,
+                                                        float inv_tau, float* loss, float* lse_s, float* lse_t,
+                                                        float* aux) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;  // whole waves only
+  const int64_t S = n_splits;
+  if constexpr (MODE == kModeJSD) {
+    float sl = 0.f, sx = 0.f;
+    for (int s = lane; s < n_splits; s += 64) {
+      sl += part[(0 * S + s) * N + n];
+      sx += part[(1 * S + s) * N + n];
+    }
+    sl = wave_sum(sl);
+    sx = wave_sum(sx);
+    if (lane == 0) {
+      loss[n] = sl * kLn2;
+      if (aux) aux[n] = sx * kLn2;
+    }
+  } else {
+    float ms = kNegInf, ls = 0.f, mt = kNegInf, lt = 0.f, ac = 0.f;
+    for (int s = lane; s < n_splits; s += 64)
+      merge_record<MODE>(ms, ls, mt, lt, ac, part[(0 * S + s) * N + n], part[(1 * S + s) * N + n],
+                         part[(2 * S + s) * N + n], part[(3 * S + s) * N + n], part[(4 * S + s) * N + n]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+      merge_record<MODE>(ms, ls, mt, lt, ac, __shfl_xor(ms, o), __shfl_xor(ls, o), __shfl_xor(mt, o),
+                         __shfl_xor(lt, o), __shfl_xor(ac, o));
+    if (lane == 0) {
+      const float Ls = (ms + log2f(ls)) * kLn2;
+      const float Lt = (mt + log2f(lt)) * kLn2;
+      lse_s[n] = Ls;
+      lse_t[n] = Lt;
+      if (MODE == kModeRKL || MODE == kModeFKL) {
+        const float kl = (MODE == kModeRKL) ? (ac / ls) * inv_tau - Ls + Lt : (ac / lt) * inv_tau - Lt + Ls;
+        loss[n] = kl;
+        if (aux) aux[n] = kl;
+      }
+    }
+  }
+}
+
+// Launch the merge of the forward's partial records: one thread per token,
+// or one wave per token up to kMergeWaveMaxN tokens.
+constexpr int64_t kMergeWaveMaxN = 2048;
+template <int MODE>
+hipError_t launch_merge(const float* part, int n_splits, int64_t N, float inv_tau, float* loss, float* lse_s,
+                        float* lse_t, float* aux, hipStream_t st) {
+  if (N <= kMergeWaveMaxN)
+    hipLaunchKernelGGL((merge_wave_kernel<MODE>), dim3((unsigned)((N + 3) / 4)), dim3(256), 0, st, part, n_splits, N,
+                       inv_tau, loss, lse_s, lse_t, aux);
+  else
+    hipLaunchKernelGGL((merge_kernel<MODE>), dim3((unsigned)((N + 255) / 256)), dim3(256), 0, st, part, n_splits, N,
+                       inv_tau, loss, lse_s, lse_t, aux);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Backward, step 1: G[n, v - c0] = grad[n] / tau * dloss_n / ds_v for one chunk.
 // ---------------------------------------------------------------------------
@@ -1045,27 +1107,21 @@ hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
   la.vt_offset = 0;
   la.part = static_cast<float*>(io.workspace);
   const dim3 grid(p.n_tok_tiles * p.n_splits);
-  const dim3 mgrid((unsigned)((p.N + 255) / 256));
   const bool small = p.N <= kSmallT;  // one token tile either way; the 64-row tile has a deeper ring
   hipError_t e;
   if (io.beta == 0.f || io.beta == 1.f) {
     const int mode = io.beta == 1.f ? kModeRKL : kModeFKL;
     e = p.bf16 ? launch_fwd_mode<true>(mode, small, grid, la, st) : launch_fwd_mode<false>(mode, small, grid, la, st);
     if (e != hipSuccess) return e;
-    if (mode == kModeRKL)
-      hipLaunchKernelGGL((merge_kernel<kModeRKL>), mgrid, dim3(256), 0, st, la.part, p.n_splits, p.N, la.inv_tau,
-                         io.loss, io.lse_s, io.lse_t, io.aux);
-    else
-      hipLaunchKernelGGL((merge_kernel<kModeFKL>), mgrid, dim3(256), 0, st, la.part, p.n_splits, p.N, la.inv_tau,
-                         io.loss, io.lse_s, io.lse_t, io.aux);
-    return hipGetLastError();
+    return mode == kModeRKL
+               ? launch_merge<kModeRKL>(la.part, p.n_splits, p.N, la.inv_tau, io.loss, io.lse_s, io.lse_t, io.aux, st)
+               : launch_merge<kModeFKL>(la.part, p.n_splits, p.N, la.inv_tau, io.loss, io.lse_s, io.lse_t, io.aux, st);
   }
   // 0 < beta < 1: sweep 1 -> LSEs, sweep 2 -> mixture sums.
   e = p.bf16 ? launch_fwd_mode<true>(kModeLSE, small, grid, la, st) : launch_fwd_mode<false>(kModeLSE, small, grid, la, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<kModeLSE>), mgrid, dim3(256), 0, st, la.part, p.n_splits, p.N, la.inv_tau,
-                     io.loss, io.lse_s, io.lse_t, io.aux);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  e = launch_merge<kModeLSE>(la.part, p.n_splits, p.N, la.inv_tau, io.loss, io.lse_s, io.lse_t, io.aux, st);
+  if (e != hipSuccess) return e;
   LogitArgs lj = la;
   lj.part = reinterpret_cast<float*>(static_cast<char*>(io.workspace) + align_up(
       kFwdFields * (size_t)p.n_splits * (size_t)p.N * sizeof(float), 256));
@@ -1073,9 +1129,7 @@ hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
   lj.lse_t = io.lse_t;
   e = p.bf16 ? launch_fwd_mode<true>(kModeJSD, small, grid, lj, st) : launch_fwd_mode<false>(kModeJSD, small, grid, lj, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<kModeJSD>), mgrid, dim3(256), 0, st, lj.part, p.n_splits, p.N, la.inv_tau,
-                     io.loss, io.lse_s, io.lse_t, io.aux);
-  return hipGetLastError();
+  return launch_merge<kModeJSD>(lj.part, p.n_splits, p.N, la.inv_tau, io.loss, io.lse_s, io.lse_t, io.aux, st);
 }
 
 static int bwd_tiles_per_block(const Plan& p, int ctiles) {
