@@ -74,6 +74,31 @@ __device__ __forceinline__ float wave_dot_bf16(const uint16_t* __restrict__ h, c
   return __builtin_bit_cast(float, f32_to_bf16_bits(wave_sum(acc)) << 16);
 }
 
+// Four such dot products at once (rows v[j] of W; v[j] < 0: no row, result
+// unspecified), each accumulated and reduced exactly as wave_dot_bf16 does, so
+// the same bits, with the loads of the four rows in flight together.
+__device__ __forceinline__ void wave_dot4_bf16(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                                               const int64_t (&v)[4], int32_t d, int lane, float (&out)[4]) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int i = lane * 8; i < d; i += 64 * 8) {
+    const u32x4 hv = *reinterpret_cast<const u32x4*>(h + i);
+    u32x4 wv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wv[j] = v[j] >= 0 ? *reinterpret_cast<const u32x4*>(W + v[j] * d + i) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t hx = hv[e], wx = wv[j][e];
+        acc[j] = fmaf(__builtin_bit_cast(float, hx << 16), __builtin_bit_cast(float, wx << 16), acc[j]);
+        acc[j] = fmaf(__builtin_bit_cast(float, hx & 0xFFFF0000u), __builtin_bit_cast(float, wx & 0xFFFF0000u), acc[j]);
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out[j] = __builtin_bit_cast(float, f32_to_bf16_bits(wave_sum(acc[j])) << 16);
+}
+
 // --------------------------------------------------------------------------
 // Raw buffer resource over [base, base + bytes): loads past the end return
 // zero, which masks the vocabulary / token tails without branches.

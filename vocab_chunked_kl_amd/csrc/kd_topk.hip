@@ -457,13 +457,19 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
   int32_t vj;
   float tj;
   select_topk(a.lists, a.N, a.V, n, S, K, a.split, cand[wave], sel[wave], lane, vj, tj);
-  // student bf16 logits at the selected indices: one wave-wide dot product each
+  // student bf16 logits at the selected indices: one wave-wide dot product
+  // each, four at a time
   const uint16_t* h = a.h_s + n * a.d_s;
   float sj = 0.f;
-  for (int j = 0; j < K; ++j) {
-    const int32_t v = __shfl(vj, j);  // wave-uniform
-    const float zsv = v >= 0 ? wave_dot_bf16(h, a.W_s, v, a.d_s, lane) : kNegInf;
-    if (lane == j) sj = zsv;
+  for (int j0 = 0; j0 < K; j0 += 4) {
+    int64_t v4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v4[j] = j0 + j < K ? (int64_t)__shfl(vj, j0 + j) : -1;  // wave-uniform
+    float z[4];
+    wave_dot4_bf16(h, a.W_s, v4, a.d_s, lane, z);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane == j0 + j) sj = v4[j] >= 0 ? z[j] : kNegInf;
   }
   if (act) {
     a.idx[n * K + lane] = vj;
@@ -618,19 +624,36 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(TailArgs a) {
     __builtin_amdgcn_wave_barrier();
   }
 
-  // 2) the missing logits (wave-uniform loop: one wave-wide dot product each)
+  // 2) the missing logits, four consecutive support entries at a time (the
+  //    teacher's list, then the student's extras, then the label: runs that
+  //    miss the same model's logit), one wave-wide dot product each
   const uint16_t* hs = a.h_s + n * a.d_s;
   const uint16_t* ht = a.h_t + n * a.d_t;
-  for (int i = 0; i < cnt; ++i) {
-    const int32_t v = si[i];
-    const int kn = sk[i];
-    if (!(kn & 1)) {
-      const float z = wave_dot_bf16(ht, a.W_t, v, a.d_t, lane);
-      if (lane == 0) st[i] = z;
+  for (int i0 = 0; i0 < cnt; i0 += 4) {
+    int64_t vt[4], vs[4];
+    bool any_t = false, any_s = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool ok = i0 + j < cnt;
+      const int32_t v = ok ? si[i0 + j] : -1;
+      const int kn = ok ? sk[i0 + j] : 3;
+      vt[j] = (kn & 1) ? -1 : v;
+      vs[j] = (kn & 2) ? -1 : v;
+      any_t = any_t || vt[j] >= 0;
+      any_s = any_s || vs[j] >= 0;
     }
-    if (!(kn & 2)) {
-      const float z = wave_dot_bf16(hs, a.W_s, v, a.d_s, lane);
-      if (lane == 0) ss[i] = z;
+    float z[4];
+    if (any_t) {
+      wave_dot4_bf16(ht, a.W_t, vt, a.d_t, lane, z);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (lane == 0 && vt[j] >= 0) st[i0 + j] = z[j];
+    }
+    if (any_s) {
+      wave_dot4_bf16(hs, a.W_s, vs, a.d_s, lane, z);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (lane == 0 && vs[j] >= 0) ss[i0 + j] = z[j];
     }
   }
   __builtin_amdgcn_wave_barrier();
