@@ -103,18 +103,31 @@ def bf16_neighbours(x):
 
 
 def fp32_dot_error_bound(h, W, factor: float = 8.0):
-    """A statistical bound on |fp32-accumulated dot - exact dot| for every logit:
-    factor * sqrt(d) * 2^-24 * sum_i |h_i W_i|  ([rows, V] float64).
+    """A statistical bound on |fp32-accumulated dot - exact dot| for every logit
+    ([rows, V] float64):
 
-    READING: the kernel accumulates bf16 products in float32 in an order the
-    pages do not fix, so a logit lying within this distance of a bf16 rounding
-    midpoint may round either way on the GPU; only such logits may make the
-    top-k selection differ from this oracle's."""
-    hh = np.abs(as_f64(h))
-    d = hh.shape[1]
-    out = np.empty((hh.shape[0], W.shape[0]))
+        factor * 2^-24 * sqrt(d) * (|z| + sqrt(sum_i (h_i W_i)^2)).
+
+    READING ([Top-K KD], 二.1-二.2: logits are produced in bf16 from an fp32
+    accumulation; the pages fix neither the summation order nor its rounding):
+    the products of bf16 inputs are exact in fp32, so the error is the sum of
+    the roundings of at most d additions, each at most 2^-24 times the partial
+    sum it forms. For terms in an order unrelated to their values, partial sums
+    stay within a multiple of |z| (the drift) plus sqrt(sum x_i^2) (the spread
+    of a random walk), and the roundings add like independent draws, hence the
+    sqrt(d). A logit lying within this distance of a bf16 rounding midpoint may
+    round either way on the GPU; only such logits may make a top-k selection
+    differ from this oracle's. Pinned against float32 accumulation in the
+    orders a kernel takes (sequential, pairwise, per-lane blocks then a tree,
+    blocks of 16 exact products with rounded and truncated accumulation), and
+    against being vacuous (the share of logits it flags)."""
+    h64 = as_f64(h)
+    d = h64.shape[1]
+    h2 = h64 * h64
+    out = np.empty((h64.shape[0], W.shape[0]))
     for v0 in range(0, W.shape[0], _SLAB):
-        out[:, v0:v0 + _SLAB] = hh @ np.abs(as_f64(W[v0:v0 + _SLAB])).T
+        w = as_f64(W[v0:v0 + _SLAB])
+        out[:, v0:v0 + _SLAB] = np.abs(h64 @ w.T) + np.sqrt(h2 @ (w * w).T)
     return factor * np.sqrt(d) * 2.0 ** -24 * out
 
 
