@@ -43,7 +43,7 @@ import numpy as np
 
 __all__ = [
     "as_f64", "bf16_round", "bf16_neighbours", "logits", "lse", "log_softmax", "divergence",
-    "kd_fwd", "grad_student_logits", "kd_bwd", "kd_bwd_w", "topk_order", "topk_three_terms", "kd_topk_fwd",
+    "kd_fwd", "grad_student_logits", "kd_bwd", "kd_fwd_bwd", "kd_bwd_w", "topk_order", "topk_three_terms", "kd_topk_fwd",
     "fp32_dot_error_bound", "svd_teacher", "log1mexp", "topk_grad_student_logits", "kd_topk_bwd",
     "SUPPORT_TEACHER", "SUPPORT_STUDENT", "SUPPORT_LABEL", "tail_default_support", "tail_support_size",
     "tail_support", "tail_divergence", "kd_tail_fwd", "tail_grad_student_logits", "kd_tail_bwd",
@@ -232,18 +232,36 @@ def grad_student_logits(s, t, beta: float) -> np.ndarray:
     "仓库实现"] once its letters are read as p = student, q = teacher:
       beta = 0 : q - p
       beta = 1 : q (log q - log p - KL(q||p))
-      else     : (1 - beta) q (log q - log m - KL(q||m))"""
+      else     : (1 - beta) q (log q - log m - KL(q||m))
+
+    Evaluation. Both centred forms are w q (d - sum_u q_u d_u) with
+    d = log q - log p (beta = 1) or log q - log m. When one entry a holds
+    nearly all of q, its d - sum q d is tiny while both terms are of the size
+    of the log-sum-exps, and the fp64 rounding of the sum over V terms swamps
+    it. Subtracting d_a from every d first changes nothing algebraically (the
+    weighted mean moves by the same d_a) but makes the dominant term of the
+    sum exactly zero, so c = d - d_a and g = w q (c - sum_u q_u c_u) keep
+    their relative precision. For beta = 0 the dominant entry's q_a - p_a is
+    taken as the equal sum over the other entries of p - q (both
+    distributions sum to one)."""
     lq = log_softmax(s)
     lp = log_softmax(t)
     q = np.exp(lq)
+    a = np.argmax(lq, axis=-1)[..., None]
     if beta == 0.0:
-        return q - np.exp(lp)
+        g = q - np.exp(lp)
+        np.put_along_axis(g, a, 0.0, axis=-1)
+        np.put_along_axis(g, a, -np.sum(g, axis=-1, keepdims=True), axis=-1)
+        return g
     if beta == 1.0:
-        kl = np.sum(q * (lq - lp), axis=-1, keepdims=True)
-        return q * (lq - lp - kl)
-    lm = np.logaddexp(np.log(beta) + lp, np.log1p(-beta) + lq)
-    kl_qm = np.sum(q * (lq - lm), axis=-1, keepdims=True)
-    return (1.0 - beta) * q * (lq - lm - kl_qm)
+        d = lq - lp
+        w = 1.0
+    else:
+        lm = np.logaddexp(np.log(beta) + lp, np.log1p(-beta) + lq)
+        d = lq - lm
+        w = 1.0 - beta
+    c = d - np.take_along_axis(d, a, axis=-1)
+    return w * q * (c - np.sum(q * c, axis=-1, keepdims=True))
 
 
 def kd_bwd(h_s, W_s, h_t, W_t, beta: float, tau: float, grad_loss=None) -> np.ndarray:
@@ -260,6 +278,24 @@ def kd_bwd(h_s, W_s, h_t, W_t, beta: float, tau: float, grad_loss=None) -> np.nd
     for v0 in range(0, W_s.shape[0], _SLAB):
         out += g[:, v0:v0 + _SLAB] @ as_f64(W_s[v0:v0 + _SLAB])
     return out
+
+
+def kd_fwd_bwd(h_s, W_s, h_t, W_t, beta: float, tau: float, grad_loss=None):
+    """``kd_fwd`` and ``kd_bwd`` of the same rows from one evaluation of the
+    logits: returns (dict(loss, lse_s, lse_t, aux), dL/dh_s)."""
+    if tau <= 0:
+        raise ValueError("tau must be positive")
+    s = logits(h_s, W_s) / tau
+    t = logits(h_t, W_t) / tau
+    loss, aux = divergence(s, t, beta)
+    fwd = dict(loss=loss, lse_s=lse(s), lse_t=lse(t), aux=aux)
+    g = grad_student_logits(s, t, beta) / tau
+    if grad_loss is not None:
+        g = g * np.asarray(grad_loss, dtype=np.float64)[:, None]
+    dh = np.zeros((g.shape[0], W_s.shape[1]))
+    for v0 in range(0, W_s.shape[0], _SLAB):
+        dh += g[:, v0:v0 + _SLAB] @ as_f64(W_s[v0:v0 + _SLAB])
+    return fwd, dh
 
 
 def kd_bwd_w(h_s, W_s, h_t, W_t, beta: float, tau: float, grad_loss=None) -> np.ndarray:

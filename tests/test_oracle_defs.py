@@ -220,6 +220,12 @@ def test_gradient_matches_finite_differences(beta, tau):
     gl = np.array([0.5, -2.0])
     an2 = O.kd_bwd(h_s, W_s, h_t, W_t, beta, tau, grad_loss=gl)
     assert np.allclose(an2, an * gl[:, None], rtol=1e-13, atol=1e-15)
+    # the one-pass forward + backward: the same gradient against finite
+    # differences and the same loss against the pure-Python loop
+    fwd, dh = O.kd_fwd_bwd(h_s, W_s, h_t, W_t, beta, tau, grad_loss=gl)
+    assert np.allclose(dh, fd * gl[:, None], atol=4e-9, rtol=1e-7)
+    want = brute.loss_rows(h_s.tolist(), W_s.tolist(), h_t.tolist(), W_t.tolist(), beta, tau)
+    assert np.allclose(fwd["loss"], want, rtol=1e-12, atol=1e-14)
 
 
 @pytest.mark.parametrize("beta", BETAS)
