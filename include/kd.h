@@ -80,6 +80,10 @@ typedef enum {
 
 /*
  * kd_workspace_size - device workspace (bytes) that `op` needs for this shape.
+ *   Source: ricardokevins notes, "Nitrobrew tweet analysis", the evaluation
+ *   table's working-set row (peak memory falls from the full [tokens, V]
+ *   logits to one vocabulary chunk, O(tokens * chunk_V)), and the chunk size
+ *   argument of the forward_kl / reverse_kl listing under "VeRL PR".
  *   op: KD_OP_FWD (kd_fwd), KD_OP_BWD (kd_bwd without dW_s), KD_OP_BWD_W
  *   (kd_bwd with dW_s), KD_OP_TOPK (kd_topk_fwd), KD_OP_TOPK_BWD
  *   (kd_topk_bwd: KD_OP_BWD's chunk buffers plus O(N k) floats), KD_OP_TAIL
@@ -91,9 +95,10 @@ typedef enum {
  *   The backward's workspace is O(N * chunk_V) (the gradient tile G of one
  *   vocabulary chunk, in the input dtype) plus O(chunk_V * d_s) for one
  *   transposed chunk of W_s; KD_OP_BWD_W adds a transposed copy of G and of
- *   h_s (O(N * chunk_V + N * d_s)). The forward's is O(N * V / 1024) floats
- *   of partial statistics. Writes the size to *bytes (host pointer). Pure
- *   host function.
+ *   h_s (O(N * chunk_V + N * d_s)); kd_bwd's also holds O(N * chunk_V / 256)
+ *   floats for its dominant-entry correction. The forward's is at most 256
+ *   partial records of 5 floats per token (7 for 0 < beta < 1), whatever V:
+ *   O(N). Writes the size to *bytes (host pointer). Pure host function.
  */
 kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t d_t, kd_dtype dtype,
                             float beta, int32_t chunk_V, int32_t k, size_t* bytes);
@@ -148,6 +153,10 @@ kd_status kd_fwd(const void* h_s, const void* W_s, const void* h_t, const void* 
  *     else:      g = (1 - beta) q (log q - log m - KL(q || m))
  *   dh_s[n, :] = grad_loss[n] * sum_v (g[n, v] / tau) W_s[v, :]
  *   dW_s[v, :] = sum_n grad_loss[n] * (g[n, v] / tau) h_s[n, :]
+ *   For dh_s, the entry whose student probability exceeds 0.6 (at most one
+ *   per token) takes minus the sum of the token's other entries (g sums to
+ *   zero over v for every beta): its own formula cancels terms of the size
+ *   of the log-sum-exps, which fp32 cannot resolve when q saturates.
  *
  *   lse_s, lse_t, aux (device, [N] fp32, read): as written by kd_fwd with the
  *         same inputs, beta and tau (aux unused when beta == 0, may be NULL).

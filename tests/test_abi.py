@@ -14,7 +14,14 @@ pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libkd.so not bu
 
 def header_symbols():
     text = open(os.path.join(ROOT, "include", "kd.h")).read()
-    return sorted(set(re.findall(r"^(?:kd_status|const char\*|int32_t)\s+(kd_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^(?:kd_status|const char\*|int32_t|size_t)\s+(kd_\w+)\s*\(", text, flags=re.M)))
+
+
+def _chunk_buffers(kd, n, v, d, cv):
+    """The backward's per-chunk buffers (kd_bwd's size without its
+    dominant-entry correction), which the top-k and tail backward share."""
+    al = lambda x: -(-x // 256) * 256  # noqa: E731
+    return kd.workspace_size(kd.KD_OP_BWD, n, v, d, d, kd.KD_BF16, chunk_V=cv) - al((cv // 256) * n * 4) - 2 * al(n * 4)
 
 
 def test_header_symbols_exported():
@@ -39,7 +46,9 @@ def test_workspace_sizes():
     N, V, ds, dt = 32768, 151936, 2560, 4096
     for cv in (2048, 8192):
         b = kd.workspace_size(kd.KD_OP_BWD, N, V, ds, dt, kd.KD_BF16, chunk_V=cv)
-        assert b == N * cv * 2 + ds * cv * 2
+        # G chunk, W_s chunk transposed, then the dominant-entry correction's
+        # per-split sums of one chunk, their total and the index, per token
+        assert b == N * cv * 2 + ds * cv * 2 + (cv // 256) * N * 4 + 2 * N * 4
         # with dW_s: plus the chunk transposed [chunk_V, Np] and h_s transposed [d_s, Np],
         # Np = N rounded up to the 128-token tile
         for n in (N, 300):
@@ -71,7 +80,17 @@ def test_workspace_sizes():
                         (32768, 2560, 16384, 1)):
         base = al(n * cv * 2) + al(d * cv * 2)
         want = base + (al(s * n * d * 4) if s > 1 else 0)
+        # kd_bwd's dominant-entry correction: per-split sums of one chunk, their total, the index
+        want += al((cv // 256) * n * 4) + 2 * al(n * 4)
         assert kd.workspace_size(kd.KD_OP_BWD, n, V, d, dt, kd.KD_BF16, chunk_V=cv) == want, (n, d, cv)
+    # the forward keeps at most 256 partial records of 5 (+2 for 0 < beta < 1) floats per
+    # token, whatever the vocabulary: O(N), within the backward's O(N chunk_V)
+    for n, v in ((64, 151936), (32768, 151936), (8192, 248320), (4096, 1 << 20), (100, 3 << 20)):
+        for beta in (1.0, 0.5):
+            got = kd.workspace_size(kd.KD_OP_FWD, n, v, ds, dt, kd.KD_BF16, beta=beta)
+            cap = al(5 * 256 * n * 4) + (al(2 * 256 * n * 4) if beta == 0.5 else 0)
+            assert got <= cap, (n, v, got, cap)
+            assert got <= n * kd.default_chunk(n, v) * 2 + 512, (n, v)
     with pytest.raises(kd.KDError):
         kd.workspace_size(kd.KD_OP_BWD, N, V, ds, dt, kd.KD_BF16, chunk_V=1000)
     with pytest.raises(kd.KDError):
@@ -187,8 +206,7 @@ def test_topk_bwd_validation():
     need = kd.workspace_size(kd.KD_OP_TOPK_BWD, 8, 100, 64, 64, kd.KD_BF16, chunk_V=256, k=8)
     al = lambda x: -(-x // 256) * 256  # noqa: E731
     # chunk buffers + two per-token coefficients + the (k + 1)-entry list's indices and values
-    assert need == kd.workspace_size(kd.KD_OP_BWD, 8, 100, 64, 64, kd.KD_BF16, chunk_V=256) + 2 * al(8 * 4) + \
-        2 * al(8 * 9 * 4)
+    assert need == _chunk_buffers(kd, 8, 100, 64, 256) + 2 * al(8 * 4) + 2 * al(8 * 9 * 4)
     assert call(ws_bytes=need - 1) == 3
 
 
@@ -216,7 +234,7 @@ def test_tail_validation_and_workspace():
         al(6 * S * N * 4) + 2 * al(S * N * 16 * 4)
     # chunk buffers + one per-token coefficient + values for the largest support (2k + 1)
     assert kd.workspace_size(kd.KD_OP_TAIL_BWD, N, V, 64, 64, kd.KD_BF16, chunk_V=256, k=16) == \
-        kd.workspace_size(kd.KD_OP_BWD, N, V, 64, 64, kd.KD_BF16, chunk_V=256) + al(N * 4) + al(N * 33 * 4)
+        _chunk_buffers(kd, N, V, 64, 256) + al(N * 4) + al(N * 33 * 4)
 
     def fwd(**kw):
         a = dict(h_s=FAKE, W_s=FAKE, h_t=FAKE, W_t=FAKE, N=8, V=100, d_s=64, d_t=64, k=4, support=1, beta=0.0,

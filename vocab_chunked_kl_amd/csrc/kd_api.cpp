@@ -14,6 +14,7 @@
 
 namespace {
 
+
 thread_local char g_last_error[256] = "";
 
 kd_status fail(kd_status s, const char* what) {
@@ -114,7 +115,7 @@ kd_status kd_workspace_size(kd_op op, int64_t N, int64_t V, int32_t d_s, int32_t
       return KD_OK;
     case KD_OP_BWD:
     case KD_OP_BWD_W:
-      *bytes = kd::bwd_workspace_bytes(p, chunk_V, op == KD_OP_BWD_W);
+      *bytes = kd::kd_bwd_workspace_bytes(p, chunk_V, op == KD_OP_BWD_W);
       return KD_OK;
     case KD_OP_TOPK:
       if (k < 1 || k > KD_TOPK_MAX || k > V) return fail(KD_ERR_INVALID_ARG, "k outside [1, min(V, KD_TOPK_MAX)]");
@@ -177,7 +178,7 @@ kd_status kd_bwd(const void* h_s, const void* W_s, const void* h_t, const void* 
   if (dW_s && 256 * ((N + 127) / 128 * 128) * esz >= kMaxTileBytes)
     return fail(KD_ERR_UNSUPPORTED, "too many tokens for dW_s");
   const kd::Plan p = kd::make_plan(N, V, d_s, d_t, dtype == KD_BF16);
-  const size_t need = kd::bwd_workspace_bytes(p, chunk_V, dW_s != nullptr);
+  const size_t need = kd::kd_bwd_workspace_bytes(p, chunk_V, dW_s != nullptr);
   if (!workspace || ws_bytes < need)
     return fail(KD_ERR_WORKSPACE, dW_s ? "workspace smaller than kd_workspace_size(BWD_W)"
                                        : "workspace smaller than kd_workspace_size(BWD)");

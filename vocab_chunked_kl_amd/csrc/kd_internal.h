@@ -44,19 +44,17 @@ constexpr int kDenseThreads = kDhThreads;
 // Token tiles grouped together in the block order: the 32 blocks that run at
 // once on one XCD are 8 token tiles x 4 vocabulary splits, the split that
 // minimises the operand bytes its L2 fetches (measured best of 4, 8, 16).
-#ifndef KD_TOK_GROUP
-#define KD_TOK_GROUP 8
-#endif
-constexpr int kTokGroup = KD_TOK_GROUP;
+constexpr int kTokGroup = 8;
 // Vocabulary tiles per forward workgroup (1024 vocabulary entries; chosen per
 // shape for up to 4 token tiles, see make_plan): blocks that run together
 // finish together, which keeps their shared operand rows in L2; each writes
 // one partial record per token. Measured against 1 to 8: equal to 8 at 32k
 // tokens, at or near the best at 1024 to 4096 tokens.
-#ifndef KD_FWD_TILES_PER_BLOCK
-#define KD_FWD_TILES_PER_BLOCK 4
-#endif
-constexpr int kFwdTilesPerBlock = KD_FWD_TILES_PER_BLOCK;
+constexpr int kFwdTilesPerBlock = 4;
+// Largest number of forward partial records per token: past 256 splits
+// (V > 262144 at four tiles per workgroup) the workgroups take more tiles, so
+// the forward workspace stays within 7 * 256 floats per token for any V.
+constexpr int kFwdMaxSplits = 256;
 // Vocabulary tiles per gradient-tile workgroup (bwdg_kernel): two halve the
 // pipeline ramps per tile (measured 2 % faster than 1 on the 32k-token
 // backward, and 4 no better than 2) as long as the chunk's grid keeps at
@@ -82,6 +80,8 @@ Plan make_plan(int64_t N, int64_t V, int32_t d_s, int32_t d_t, bool bf16);
 size_t align_up(size_t x, size_t a);
 size_t fwd_workspace_bytes(const Plan& p, bool jsd);
 size_t bwd_workspace_bytes(const Plan& p, int32_t chunk_V, bool with_dW);
+// kd_bwd's workspace: the chunk buffers plus its dominant-entry correction.
+size_t kd_bwd_workspace_bytes(const Plan& p, int32_t chunk_V, bool with_dW);
 
 struct FwdIO {
   const void *h_s, *W_s, *h_t, *W_t;

@@ -73,7 +73,19 @@ struct LogitArgs {
   char* GT;          // the same chunk transposed, [chunk][Np] (null: not written)
   int64_t ldgt;      // GT row pitch in bytes
   int64_t Np;        // tokens rounded up to the token tile (GT columns written)
+  // Dominant-entry correction of dL/dh_s (null: off): per (split, token) the
+  // sum of the G entries as stored, [n_splits][N]; per token the vocabulary
+  // index of the entry whose student probability exceeds kBigQ (-1: none).
+  float* esum;
+  int32_t* big;
 };
+
+// A student probability above this belongs to at most one entry per token:
+// the dominant entry, whose gradient the backward takes from the zero-sum
+// identity instead of its own (cancelling) formula. kBigLq2Lo is the wider
+// log2 threshold of the cheap per-tile check that guards the exact test.
+constexpr float kBigLq2 = -0.73696559f;    // log2(0.6)
+constexpr float kBigLq2Lo = -0.86249648f;  // log2(0.55)
 
 __device__ __forceinline__ void merge_online(float& m, float& l, float m2, float l2) {
   const float mm = fmaxf(m, m2);
@@ -432,11 +444,18 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
     }
   }
 
+  // Sum of this lane's stored G entries per token, over the block's tiles.
+  float es[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) es[nb] = 0.f;
+  const bool fix = a.esum != nullptr;
+
   auto epi = [&](int vt, auto& zs, auto& zt) {
     const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int64_t n = tok0 + nb * 32 + (lane & 31);
+      float lqmax = kNegInf;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -453,6 +472,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
               const int64_t v = vrow0 + mb * 32 + acc_row(r, lane);
               const float x = zs[mb][nb][r], y = zt[mb][nb][r];
               const float lq2 = fmaf(x, c2, -Ls2[nb]);
+              lqmax = fmaxf(lqmax, lq2);
               const float q = fast_exp2(lq2);
               float g;
               if constexpr (MODE == kModeRKL) {
@@ -482,16 +502,100 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
             if constexpr (kBf16) {
               w2[h].x = f32_to_bf16_bits(g4[0]) | (f32_to_bf16_bits(g4[1]) << 16);
               w2[h].y = f32_to_bf16_bits(g4[2]) | (f32_to_bf16_bits(g4[3]) << 16);
-            } else if (a.G && n < a.N) {
-              const int64_t col = vrow0 + mb * 32 + 8 * rg + 4 * (lane >> 5) - a.g_col0;
-              *reinterpret_cast<floatx4*>(a.G + n * a.ldg + col * 4) = floatx4{g4[0], g4[1], g4[2], g4[3]};
+              // the stored values, widened back to fp32
+              es[nb] += (__builtin_bit_cast(float, w2[h].x << 16) + __builtin_bit_cast(float, w2[h].x & 0xFFFF0000u)) +
+                        (__builtin_bit_cast(float, w2[h].y << 16) + __builtin_bit_cast(float, w2[h].y & 0xFFFF0000u));
+            } else {
+              es[nb] += (g4[0] + g4[1]) + (g4[2] + g4[3]);
+              if (a.G && n < a.N) {
+                const int64_t col = vrow0 + mb * 32 + 8 * rg + 4 * (lane >> 5) - a.g_col0;
+                *reinterpret_cast<floatx4*>(a.G + n * a.ldg + col * 4) = floatx4{g4[0], g4[1], g4[2], g4[3]};
+              }
             }
           }
           if constexpr (kBf16) store_g16(a.G, a.ldg, n, a.N, vrow0 + mb * 32 + 16 * pr - a.g_col0, w2, lane);
         }
+      // The dominant entry (q > 0.6, at most one per token) records its index;
+      // the wide threshold keeps the exact test off tiles that cannot hold it.
+      if (fix && __ballot(lqmax > kBigLq2Lo) != 0ull) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t v = vrow0 + mb * 32 + acc_row(r, lane);
+            if (v < a.V && n < a.N && fmaf(zs[mb][nb][r], c2, -Ls2[nb]) > kBigLq2) a.big[n] = (int32_t)v;
+          }
+      }
     }
   };
   sweep<kBf16, TM, TN, WM, WN, NBUF, kLogitRB, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+
+  if (!fix) return;
+  // Per token the block's sum of stored entries: lanes l and l ^ 32 hold the
+  // same token; waves wm > 0 publish theirs in the drained ring, wave wm = 0
+  // adds them in a fixed order and writes the block's record.
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) es[nb] += __shfl_xor(es[nb], 32);
+  float* red = reinterpret_cast<float*>(lds.b[0]);
+  if (wm > 0 && lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) red[(wm - 1) * TN + wn * (TN / WN) + nb * 32 + lane] = es[nb];
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = wn * (TN / WN) + nb * 32 + lane;
+      float t = es[nb];
+#pragma unroll
+      for (int w = 0; w < WM - 1; ++w) t += red[w * TN + col];
+      const int64_t n = (int64_t)tt * TN + col;
+      if (n < a.N) a.esum[(int64_t)sp * a.N + n] = t;
+    }
+  }
+}
+
+// Dominant-entry correction, before the first chunk: no token has one yet.
+__global__ __launch_bounds__(256) void big_init_kernel(int32_t* big, int64_t N) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < N; i += (int64_t)gridDim.x * 256) big[i] = -1;
+}
+
+// After each chunk: etot[n] (=|+=) the chunk's per-split sums, in split order.
+__global__ __launch_bounds__(256) void esum_reduce_kernel(const float* __restrict__ part, int n_split, int64_t N,
+                                                          float* __restrict__ etot, int first) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float t = 0.f;
+  for (int s = 0; s < n_split; ++s) t += part[(int64_t)s * N + n];
+  etot[n] = first ? t : etot[n] + t;
+}
+
+// After the last chunk. The gradient entries of a token sum to zero for every
+// beta (the beta table of ars-opd-rebuild "03 · 层 2：White-box OPD 基线",
+// section 2.3, differentiated), so the dominant entry's exact value is minus
+// the sum of all others. Its own formula cancels terms of the size of the
+// log-sum-exps, which fp32 cannot resolve when the student is saturated; so
+// the stored value g_a is replaced by -(sum of the others as stored): with E
+// the sum of every stored entry, dh_s[n] -= E * W_s[a].
+template <typename T>
+__global__ __launch_bounds__(256) void big_fix_kernel(const int32_t* __restrict__ big, const float* __restrict__ etot,
+                                                      const T* __restrict__ W_s, int32_t d_s, int64_t N,
+                                                      float* __restrict__ dh) {
+  for (int64_t n = blockIdx.x; n < N; n += gridDim.x) {
+    const int64_t v = big[n];
+    if (v < 0) continue;
+    const float e = etot[n];
+    const T* w = W_s + v * d_s;
+    float* o = dh + n * d_s;
+    for (int i = threadIdx.x; i < d_s; i += 256) {
+      float wi;
+      if constexpr (sizeof(T) == 2)
+        wi = __builtin_bit_cast(float, (uint32_t)w[i] << 16);
+      else
+        wi = w[i];
+      o[i] = fmaf(-e, wi, o[i]);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -995,10 +1099,10 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // (waves of workgroups over the 256 CUs) x (tiles per workgroup + the fixed
 // cost of one, ~1.5 tiles); the tiles per workgroup that minimise it (the
 // measured best for the forward at 64..512 tokens).
-static int tiles_per_block_few_tokens(int n_tok_tiles, int n_vtiles) {
-  int tps = 1;
+static int tiles_per_block_few_tokens(int n_tok_tiles, int n_vtiles, int t_min) {
+  int tps = t_min;
   double best = 1e30;
-  for (int t = 1; t <= 8; ++t) {
+  for (int t = t_min; t <= (t_min > 8 ? t_min : 8); ++t) {
     const int64_t blocks = (int64_t)n_tok_tiles * ((n_vtiles + t - 1) / t);
     const double cost = (double)((blocks + 255) / 256) * (t + 1.5);
     if (cost < best) {
@@ -1019,7 +1123,10 @@ Plan make_plan(int64_t N, int64_t V, int32_t d_s, int32_t d_t, bool bf16) {
   p.esz = bf16 ? 2 : 4;
   p.n_tok_tiles = (int)((N + kTileT - 1) / kTileT);
   p.n_vtiles = (int)((V + kTileV - 1) / kTileV);
-  const int tps = p.n_tok_tiles <= 4 ? tiles_per_block_few_tokens(p.n_tok_tiles, p.n_vtiles) : kFwdTilesPerBlock;
+  // at most kFwdMaxSplits partial records per token, whatever V
+  const int t_min = (p.n_vtiles + kFwdMaxSplits - 1) / kFwdMaxSplits;
+  int tps = p.n_tok_tiles <= 4 ? tiles_per_block_few_tokens(p.n_tok_tiles, p.n_vtiles, t_min) : kFwdTilesPerBlock;
+  tps = tps > t_min ? tps : t_min;
   p.tiles_per_split = tps < p.n_vtiles ? tps : p.n_vtiles;
   p.n_splits = (p.n_vtiles + p.tiles_per_split - 1) / p.tiles_per_split;
   return p;
@@ -1061,6 +1168,17 @@ size_t bwd_workspace_bytes(const Plan& p, int32_t chunk_V, bool with_dW) {
   const int s = dh_ksplit(p, chunk_V);
   return bwd_base_bytes(p, chunk_V, with_dW) +
          (s > 1 ? align_up((size_t)s * p.N * p.d_s * sizeof(float), 256) : 0);
+}
+
+// kd_bwd's dominant-entry correction after the chunk buffers: the per-split
+// sums of one chunk (at most chunk_V / 256 splits), their running total and
+// the dominant index, per token.
+static size_t bwd_fix_bytes(const Plan& p, int32_t chunk_V) {
+  return align_up((size_t)(chunk_V / kTileV) * p.N * sizeof(float), 256) + 2 * align_up((size_t)p.N * 4, 256);
+}
+
+size_t kd_bwd_workspace_bytes(const Plan& p, int32_t chunk_V, bool with_dW) {
+  return bwd_workspace_bytes(p, chunk_V, with_dW) + bwd_fix_bytes(p, chunk_V);
 }
 
 // dh (+)= G . W_s[chunk] for one chunk (kcols contracted entries), split over
@@ -1133,7 +1251,7 @@ hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
 }
 
 static int bwd_tiles_per_block(const Plan& p, int ctiles) {
-  if (p.n_tok_tiles <= 4) return tiles_per_block_few_tokens(p.n_tok_tiles, ctiles);
+  if (p.n_tok_tiles <= 4) return tiles_per_block_few_tokens(p.n_tok_tiles, ctiles, 1);
   const int wide = (ctiles + kBwdTilesPerBlock - 1) / kBwdTilesPerBlock;
   return (int64_t)p.n_tok_tiles * wide >= kBwdWideMinBlocks ? kBwdTilesPerBlock : 1;
 }
@@ -1147,6 +1265,10 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   char* hsT = GT + align_up((size_t)io.chunk_V * np * p.esz, 256);
   float* part = reinterpret_cast<float*>(static_cast<char*>(io.workspace) +
                                          bwd_base_bytes(p, io.chunk_V, io.dW != nullptr));
+  char* fixw = static_cast<char*>(io.workspace) + bwd_workspace_bytes(p, io.chunk_V, io.dW != nullptr);
+  float* esum = reinterpret_cast<float*>(fixw);
+  float* etot = reinterpret_cast<float*>(fixw + align_up((size_t)(io.chunk_V / kTileV) * p.N * sizeof(float), 256));
+  int32_t* big = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(etot) + align_up((size_t)p.N * 4, 256));
   LogitArgs la = logit_args(p, io.h_s, io.W_s, io.h_t, io.W_t, io.tau, io.beta);
   // Up to 64 tokens the 64-row tile with a deeper ring (one token tile either
   // way); not with dW_s, whose transposed gradient copy must also zero the
@@ -1161,6 +1283,9 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   la.GT = io.dW ? GT : nullptr;
   la.ldgt = np * p.esz;
   la.Np = np;
+  la.esum = io.dh ? esum : nullptr;
+  la.big = io.dh ? big : nullptr;
+  const unsigned tok_blocks = (unsigned)((p.N + 255) / 256);
   const int n_d_tiles = (p.d_s + kTileDhD - 1) / kTileDhD;
   hipError_t e;
   auto transpose = [&](const void* src, char* dst, int64_t rows, int64_t c0, int64_t cols, int64_t pitch) {
@@ -1183,6 +1308,10 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   };
   // h_s transposed once ([d_s][Np], zero past N): the token-contiguous B operand of dW
   if (io.dW && (e = transpose(io.h_s, hsT, p.N, 0, np, np)) != hipSuccess) return e;
+  if (io.dh) {
+    hipLaunchKernelGGL(big_init_kernel, dim3(tok_blocks < 1024 ? tok_blocks : 1024), dim3(256), 0, st, big, p.N);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   for (int64_t c0 = 0; c0 < p.V; c0 += io.chunk_V) {
     const int64_t ccols = (p.V - c0 < io.chunk_V) ? p.V - c0 : io.chunk_V;
     const int ctiles = (int)((ccols + kTileV - 1) / kTileV);
@@ -1206,6 +1335,9 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
       da.dh = io.dh;
       da.first = c0 == 0;
       if ((e = launch_dh(p, p.bf16, da, io.chunk_V, kcols, part, st)) != hipSuccess) return e;
+      hipLaunchKernelGGL(esum_reduce_kernel, dim3(tok_blocks), dim3(256), 0, st, esum, la.n_splits, p.N, etot,
+                         c0 == 0 ? 1 : 0);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (io.dW) {
       // dW_s[chunk] = G^T . h_s: rows of the chunk, contracted over the tokens
@@ -1220,6 +1352,16 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
       dw.n_ksplit = 1;
       if ((e = gemm(dw, dw.n_tok_tiles)) != hipSuccess) return e;
     }
+  }
+  if (io.dh) {
+    const dim3 fgrid((unsigned)(p.N < 4096 ? p.N : 4096));
+    if (p.bf16)
+      hipLaunchKernelGGL(big_fix_kernel<uint16_t>, fgrid, dim3(256), 0, st, big, etot,
+                         static_cast<const uint16_t*>(io.W_s), p.d_s, p.N, io.dh);
+    else
+      hipLaunchKernelGGL(big_fix_kernel<float>, fgrid, dim3(256), 0, st, big, etot, static_cast<const float*>(io.W_s),
+                         p.d_s, p.N, io.dh);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
 }
