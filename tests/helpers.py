@@ -50,20 +50,14 @@ def assert_close(name, gpu, ref, rtol=RTOL, atol=ATOL):
 
 U32 = 2.0 ** -24  # unit roundoff of fp32
 
+# (test, rows, exact, flagged) of every top-k / tail acceptance run in this
+# session; tests/conftest.py prints them at the end of the run.
+PARITY_COUNTS = []
 
-def grad_floor(lse_s, lse_t, loss, W_s, tau):
-    """Per-row absolute floor below which an fp32 evaluation of dL/dh_s cannot
-    be resolved: the gradient term of a saturated entry is a difference of
-    O(|L_s| + |L_t| + |KL|) quantities, each carrying fp32 rounding of relative
-    size 2^-24, and enters dh_s scaled by a W_s row and 1/tau. Eight roundings
-    are allowed for. Rows whose exact gradient is below the floor are compared
-    absolutely (|gpu - ref| <= floor)."""
-    from oracle import kd_oracle as O
-    wmax = 0.0
-    for v0 in range(0, W_s.shape[0], 16384):
-        w = O.as_f64(W_s[v0:v0 + 16384])
-        wmax = max(wmax, float(np.sqrt(np.max(np.sum(w * w, axis=1)))))
-    return 8 * U32 * (2 * np.abs(lse_s) + 2 * np.abs(lse_t) + np.abs(loss)) * wmax / tau
+
+def record_counts(what, rows, exact, flagged):
+    PARITY_COUNTS.append((what, int(rows), int(exact), int(flagged)))
+    print(f"{what}: rows {rows} exact {exact} flagged {flagged}", flush=True)
 
 
 def wgrad_floor(h_s, W_s, h_t, W_t, beta, tau, grad=None):
@@ -87,8 +81,9 @@ def wgrad_floor(h_s, W_s, h_t, W_t, beta, tau, grad=None):
 
 def assert_grad_rows(gpu, ref, name="dh_s", floor=None):
     """Per row: cosine >= COS_MIN and max|d|/max|ref| <= MAXREL; rows whose
-    reference norm is below ``floor`` (see grad_floor) must instead agree to
-    within the floor. The cosine over all rows together must also hold."""
+    reference norm is below 1e-12 (or below ``floor``, see wgrad_floor) must
+    instead agree to within max(that, 1e-6). The cosine over all rows
+    together must also hold."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     for i in range(ref.shape[0]):
@@ -105,93 +100,149 @@ def assert_grad_rows(gpu, ref, name="dh_s", floor=None):
     assert gcos >= COS_MIN, f"{name}: global cosine {gcos:.7f}"
 
 
-def check_topk_rows(out, h_s, W_s, h_t, W_t, rows, k, tau, labels=None, factor=8.0):
+class _Rounding:
+    """Oracle roundings of one row's exact logits z (over the whole vocabulary)
+    and, on demand for a set of columns, the bf16 values the GPU may return:
+    it rounds (nearest even) an fp32 accumulation within the oracle's bound B
+    of z, so any bf16 value from round(z - B) to round(z + B) is admissible
+    (one value, or the two neighbours of a midpoint, or several steps for
+    logits near zero, where B spans more than one bf16 step)."""
+
+    def __init__(self, h_row, W, z, factor):
+        from oracle import kd_oracle as O
+        self.O, self.h, self.W, self.z, self.factor = O, h_row, W, z, factor
+        self.r = O.bf16_round(z)
+
+    def admissible(self, cols):
+        """(lo, hi): the smallest and largest admissible bf16 value per column."""
+        O = self.O
+        cols = np.asarray(cols, dtype=np.int64)
+        if cols.size == 0:
+            return np.zeros(0), np.zeros(0)
+        z = self.z[cols]
+        b = O.fp32_dot_error_bound(self.h[None], self.W[cols], self.factor)[0]
+        return O.bf16_round(z - b), O.bf16_round(z + b)
+
+    def ambiguous(self, cols):
+        lo, hi = self.admissible(cols)
+        return lo < hi
+
+    def step(self, cols):
+        lo, hi, _ = self.O.bf16_neighbours(self.z[np.asarray(cols, dtype=np.int64)])
+        return np.abs(hi - lo)
+
+
+def _ranked_list_ok(i, rk, vals, head, k, V, what):
+    """The ranked list ``head`` (values ``vals``) is ordered by (value desc,
+    index asc) and no other entry can outrank its last element under any
+    admissible rounding."""
+    for j in range(k - 1):
+        assert (vals[j] > vals[j + 1]) or (vals[j] == vals[j + 1] and head[j] < head[j + 1]), f"row {i}: {what} order {j}"
+    last_v, last_i = vals[k - 1], head[k - 1]
+    rest = np.ones(V, bool)
+    rest[head] = False
+    # entries that can outrank it have an admissible value >= last_v; their own
+    # rounding is then within the bound of last_v, so a superset is r >= last_v - 1
+    cand = np.flatnonzero(rest & (rk.r >= last_v - 1.0))
+    minkey = rk.admissible(cand)[0]
+    above = (minkey > last_v) | ((minkey == last_v) & (cand < last_i))
+    assert not above.any(), f"row {i}: {what} entries {cand[above][:5]} must outrank the last ranked entry"
+
+
+def _near_kth(rk, k):
+    """Columns whose oracle rounding lies within four bf16 steps of the k-th
+    largest one: where a differing rounding can change a top-k selection."""
+    kth = np.partition(rk.r, -k)[-k]
+    col = np.argpartition(rk.r, -k)[-k]
+    return np.flatnonzero(np.abs(rk.r - kth) <= 4 * rk.step([col])[0])
+
+
+def _values_ok(i, rk, cols, vals, what):
+    lo, hi = rk.admissible(cols)
+    ok = (vals >= lo) & (vals <= hi)
+    assert ok.all(), f"row {i}: {what} values {vals[~ok][:4]} vs oracle {rk.r[cols][~ok][:4]}"
+
+
+def check_topk_rows(out, h_s, W_s, h_t, W_t, rows, k, tau, labels=None, factor=8.0, block=64):
     """Acceptance of kd_topk_fwd on ``rows`` against the fp64 oracle.
 
     The kernel rounds fp32-accumulated logits to bf16, the oracle rounds the
     exact logits; a logit within the fp32 accumulation bound of a bf16
     rounding midpoint may round either way (``ambiguous``). Per row:
-      * every returned teacher / student value is the oracle's rounding, or the
-        other neighbour for an ambiguous logit;
+      * every returned teacher / student value is an admissible rounding: a
+        bf16 value within the fp32 accumulation bound of the exact logit;
       * the list is ordered by (value desc, index asc) and no other vocabulary
         entry can rank above its last element under any admissible rounding;
       * the list equals the oracle's own top-k unless an ambiguous logit is
         involved (returned as ``flagged``);
       * the three terms and both LSEs match the oracle evaluated on the
         kernel's own roundings of the selected logits (tolerances above).
-    Returns (exact_rows, flagged_rows)."""
+    Rows are processed ``block`` at a time. Returns (exact_rows, flagged_rows)."""
     from oracle import kd_oracle as O
-    idx = out["idx"].cpu().numpy()[rows]
-    vt = out["val"].cpu().numpy()[rows].astype(np.float64)
-    vs = out["val_s"].cpu().numpy()[rows].astype(np.float64)
-    zt = O.logits(h_t[rows], W_t)
-    zs = O.logits(h_s[rows], W_s)
-    bt = O.fp32_dot_error_bound(h_t[rows], W_t, factor)
-    bs = O.fp32_dot_error_bound(h_s[rows], W_s, factor)
+    rows = np.asarray(rows)
+    idx_all = out["idx"].cpu().numpy()
+    vt_all = out["val"].cpu().numpy()
+    vs_all = out["val_s"].cpu().numpy()
+    res = {f: out[f].cpu().numpy() for f in ("binary", "cond", "p_mass", "q_mass", "lse_s", "lse_t")}
+    ce_all = out["ce"].cpu().numpy() if labels is not None else None
+    V = W_t.shape[0]
     exact = flagged = 0
-    for i in range(len(rows)):
-        rt, rs = O.bf16_round(zt[i]), O.bf16_round(zs[i])
-        lo_t, hi_t, mid_t = O.bf16_neighbours(zt[i])
-        lo_s, hi_s, mid_s = O.bf16_neighbours(zs[i])
-        amb_t = np.abs(zt[i] - mid_t) <= bt[i]
-        amb_s = np.abs(zs[i] - mid_s) <= bs[i]
-        alt_t = np.where(rt == lo_t, hi_t, lo_t)
-        alt_s = np.where(rs == lo_s, hi_s, lo_s)
-        sel = idx[i].astype(np.int64)
-        assert len(set(sel.tolist())) == k and sel.min() >= 0 and sel.max() < W_t.shape[0], f"row {i}: bad indices"
-        okt = (vt[i] == rt[sel]) | (amb_t[sel] & (vt[i] == alt_t[sel]))
-        oks = (vs[i] == rs[sel]) | (amb_s[sel] & (vs[i] == alt_s[sel]))
-        assert okt.all(), f"row {i}: teacher values {vt[i][~okt][:4]} vs {rt[sel][~okt][:4]}"
-        assert oks.all(), f"row {i}: student values {vs[i][~oks][:4]} vs {rs[sel][~oks][:4]}"
-        for j in range(k - 1):
-            assert (vt[i][j] > vt[i][j + 1]) or (vt[i][j] == vt[i][j + 1] and sel[j] < sel[j + 1]), f"row {i}: order at {j}"
-        rest = np.ones(W_t.shape[0], bool)
-        rest[sel] = False
-        minkey = np.where(amb_t, np.minimum(rt, alt_t), rt)
-        last_v, last_i = vt[i][-1], sel[-1]
-        v_idx = np.arange(W_t.shape[0])
-        above = rest & ((minkey > last_v) | ((minkey == last_v) & (v_idx < last_i)))
-        assert not above.any(), f"row {i}: entries {v_idx[above][:5]} must outrank the last selected"
-        ref_sel = O.topk_order(rt[None], k)[0]
-        if np.array_equal(ref_sel, sel):
-            exact += 1
-        else:
-            flagged += 1
-            assert (amb_t & ((np.abs(rt - last_v) <= 2 * np.abs(hi_t - lo_t)))).any(), f"row {i}: differs without ambiguity"
-        zt_b, zs_b = rt.copy(), rs.copy()
-        zt_b[sel] = vt[i]
-        zs_b[sel] = vs[i]
-        ref = O.topk_three_terms(zs_b[None], zt_b[None], sel[None], tau)
-        for name, key in (("binary", "binary"), ("cond", "cond"), ("p_mass", "p_mass"), ("q_mass", "q_mass"),
-                          ("lse_s", "lse_s"), ("lse_t", "lse_t")):
-            g = float(out[name].cpu().numpy()[rows[i]])
-            assert_close(f"row {i} {name}", np.array([g]), ref[key])
-        if labels is not None:
-            y = int(labels[rows[i]])
-            g = float(out["ce"].cpu().numpy()[rows[i]])
-            if y == -100:
-                assert np.isnan(g)
+    for b0 in range(0, len(rows), block):
+        rb = rows[b0:b0 + block]
+        zt_blk = O.logits(h_t[rb], W_t)
+        zs_blk = O.logits(h_s[rb], W_s)
+        for j, n in enumerate(rb):
+            i = b0 + j
+            rt = _Rounding(h_t[n], W_t, zt_blk[j], factor)
+            rs = _Rounding(h_s[n], W_s, zs_blk[j], factor)
+            sel = idx_all[n].astype(np.int64)
+            vt = vt_all[n].astype(np.float64)
+            vs = vs_all[n].astype(np.float64)
+            assert len(set(sel.tolist())) == k and sel.min() >= 0 and sel.max() < V, f"row {i}: bad indices"
+            _values_ok(i, rt, sel, vt, "teacher")
+            _values_ok(i, rs, sel, vs, "student")
+            _ranked_list_ok(i, rt, vt, sel, k, V, "teacher")
+            zt_b, zs_b = rt.r.copy(), rs.r.copy()
+            zt_b[sel] = vt
+            zs_b[sel] = vs
+            if np.array_equal(O.topk_order(rt.r[None], k)[0], sel):
+                exact += 1
             else:
-                cands = [rs[y]] + ([alt_s[y]] if amb_s[y] else [])
-                oks_ce = []
-                for c in cands:
-                    zz = zs_b.copy()
-                    zz[y] = c
-                    ce_ref = O.lse(zz) - c
-                    oks_ce.append(close(np.array([g]), np.array([ce_ref]))[0])
-                assert any(oks_ce), f"row {i} ce {g} vs {O.lse(zs_b) - rs[y]}"
+                # explained by the kernel's own (admissible) roundings of the listed
+                # logits, or else by an ambiguous logit near the k-th key
+                flagged += 1
+                assert np.array_equal(O.topk_order(zt_b[None], k)[0], sel) or \
+                    rt.ambiguous(_near_kth(rt, k)).any(), f"row {i}: differs without ambiguity"
+            ref = O.topk_three_terms(zs_b[None], zt_b[None], sel[None], tau)
+            for name in ("binary", "cond", "p_mass", "q_mass", "lse_s", "lse_t"):
+                assert_close(f"row {i} {name}", res[name][n:n + 1], ref[name])
+            if labels is not None:
+                y = int(labels[n])
+                g = float(ce_all[n])
+                if y == -100:
+                    assert np.isnan(g)
+                else:
+                    lo_y, hi_y = rs.admissible([y])
+                    cands = sorted({float(rs.r[y]), float(lo_y[0]), float(hi_y[0])})
+                    oks_ce = []
+                    for c in cands:
+                        zz = zs_b.copy()
+                        zz[y] = c
+                        oks_ce.append(close(np.array([g]), np.array([O.lse(zz) - c]))[0])
+                    assert any(oks_ce), f"row {i} ce {g} vs {O.lse(zs_b) - zs_b[y]}"
+    record_counts(f"top-k k={k} V={V}", len(rows), exact, flagged)
     return exact, flagged
 
 
-def check_tail_rows(out, h_s, W_s, h_t, W_t, rows, k, beta, tau, support, labels=None, factor=8.0):
+def check_tail_rows(out, h_s, W_s, h_t, W_t, rows, k, beta, tau, support, labels=None, factor=8.0, block=64):
     """Acceptance of kd_tail_fwd on ``rows`` against the fp64 oracle.
 
     As for the top-k terms, a logit within the fp32 accumulation bound of a
     bf16 rounding midpoint may round either way (``ambiguous``). Per row:
       * the support holds distinct vocabulary indices in a prefix, -1 / NaN
         after it, and its size is what the support bits allow;
-      * every returned teacher / student value is the oracle's rounding, or
-        the other neighbour for an ambiguous logit;
+      * every returned teacher / student value is an admissible rounding: a
+        bf16 value within the fp32 accumulation bound of the exact logit;
       * the ranked model's list (the teacher's when its bit is set, else the
         student's) is ordered by (value desc, index asc) and no other entry
         can outrank its last element under any admissible rounding;
@@ -199,62 +250,60 @@ def check_tail_rows(out, h_s, W_s, h_t, W_t, rows, k, beta, tau, support, labels
         involved (returned as ``flagged``);
       * loss, masses and LSEs match the oracle's tail divergence evaluated on
         the kernel's support and its own roundings of the support's logits.
-    Returns (exact_rows, flagged_rows)."""
+    Rows are processed ``block`` at a time. Returns (exact_rows, flagged_rows)."""
     from oracle import kd_oracle as O
     T, S, L = O.SUPPORT_TEACHER, O.SUPPORT_STUDENT, O.SUPPORT_LABEL
+    rows = np.asarray(rows)
     V = W_t.shape[0]
-    sup = out["sup_idx"].cpu().numpy()[rows]
-    vt = out["sup_t"].cpu().numpy()[rows].astype(np.float64)
-    vs = out["sup_s"].cpu().numpy()[rows].astype(np.float64)
-    res = {f: out[f].cpu().numpy()[rows] for f in ("loss", "p_mass", "q_mass", "lse_s", "lse_t")}
-    zt = O.logits(h_t[rows], W_t)
-    zs = O.logits(h_s[rows], W_s)
-    bt = O.fp32_dot_error_bound(h_t[rows], W_t, factor)
-    bs = O.fp32_dot_error_bound(h_s[rows], W_s, factor)
+    sup_all = out["sup_idx"].cpu().numpy()
+    vt_all = out["sup_t"].cpu().numpy()
+    vs_all = out["sup_s"].cpu().numpy()
+    res = {f: out[f].cpu().numpy() for f in ("loss", "p_mass", "q_mass", "lse_s", "lse_t")}
     exact = flagged = 0
-    v_idx = np.arange(V)
-    for i in range(len(rows)):
-        rt, rs = O.bf16_round(zt[i]), O.bf16_round(zs[i])
-        lo_t, hi_t, mid_t = O.bf16_neighbours(zt[i])
-        lo_s, hi_s, mid_s = O.bf16_neighbours(zs[i])
-        amb_t = np.abs(zt[i] - mid_t) <= bt[i]
-        amb_s = np.abs(zs[i] - mid_s) <= bs[i]
-        alt_t = np.where(rt == lo_t, hi_t, lo_t)
-        alt_s = np.where(rs == lo_s, hi_s, lo_s)
-        n = int(np.sum(sup[i] >= 0))
-        row = sup[i, :n].astype(np.int64)
-        assert np.all(sup[i, n:] == -1) and np.all(np.isnan(vt[i, n:])) and np.all(np.isnan(vs[i, n:])), \
-            f"row {i}: padding"
-        assert len(set(row.tolist())) == n and (n == 0 or (row.min() >= 0 and row.max() < V)), f"row {i}: indices"
-        lab = None if labels is None else int(labels[rows[i]])
-        ranked = (support & T) + (support & S) // 2
-        assert k <= n <= k * ranked + (1 if support & L else 0), f"row {i}: support size {n}"
-        okt = (vt[i, :n] == rt[row]) | (amb_t[row] & (vt[i, :n] == alt_t[row]))
-        oks = (vs[i, :n] == rs[row]) | (amb_s[row] & (vs[i, :n] == alt_s[row]))
-        assert okt.all(), f"row {i}: teacher values {vt[i, :n][~okt][:4]} vs {rt[row][~okt][:4]}"
-        assert oks.all(), f"row {i}: student values {vs[i, :n][~oks][:4]} vs {rs[row][~oks][:4]}"
-        if support & L and lab is not None and 0 <= lab < V:
-            assert lab in row.tolist(), f"row {i}: label {lab} missing"
-        # the first ranked list: ordered, and nothing outranks its last element
-        vals, r_, amb, alt = (vt[i], rt, amb_t, alt_t) if support & T else (vs[i], rs, amb_s, alt_s)
-        head = row[:k]
-        for j in range(k - 1):
-            assert (vals[j] > vals[j + 1]) or (vals[j] == vals[j + 1] and head[j] < head[j + 1]), f"row {i}: order {j}"
-        rest = np.ones(V, bool)
-        rest[head] = False
-        minkey = np.where(amb, np.minimum(r_, alt), r_)
-        above = rest & ((minkey > vals[k - 1]) | ((minkey == vals[k - 1]) & (v_idx < head[-1])))
-        assert not above.any(), f"row {i}: entries {v_idx[above][:5]} must outrank the last ranked entry"
-        ref_sup = O.tail_support(rs[None], rt[None], k, support, None if lab is None else np.array([lab]))[0]
-        if np.array_equal(ref_sup[ref_sup >= 0], row):
-            exact += 1
-        else:
-            flagged += 1
-            assert (amb_t | amb_s).any(), f"row {i}: support differs without ambiguity"
-        zt_b, zs_b = rt.copy(), rs.copy()
-        zt_b[row] = vt[i, :n]
-        zs_b[row] = vs[i, :n]
-        ref = O.tail_divergence(zs_b[None], zt_b[None], row[None], beta, tau)
-        for f in ("loss", "p_mass", "q_mass", "lse_s", "lse_t"):
-            assert_close(f"row {i} {f}", res[f][i:i + 1], ref[f])
+    for b0 in range(0, len(rows), block):
+        rb = rows[b0:b0 + block]
+        zt_blk = O.logits(h_t[rb], W_t)
+        zs_blk = O.logits(h_s[rb], W_s)
+        for j, nn in enumerate(rb):
+            i = b0 + j
+            rt = _Rounding(h_t[nn], W_t, zt_blk[j], factor)
+            rs = _Rounding(h_s[nn], W_s, zs_blk[j], factor)
+            vt = vt_all[nn].astype(np.float64)
+            vs = vs_all[nn].astype(np.float64)
+            n = int(np.sum(sup_all[nn] >= 0))
+            row = sup_all[nn, :n].astype(np.int64)
+            assert np.all(sup_all[nn, n:] == -1) and np.all(np.isnan(vt[n:])) and np.all(np.isnan(vs[n:])), \
+                f"row {i}: padding"
+            assert len(set(row.tolist())) == n and (n == 0 or (row.min() >= 0 and row.max() < V)), f"row {i}: indices"
+            lab = None if labels is None else int(labels[nn])
+            ranked = (support & T) + (support & S) // 2
+            assert k <= n <= k * ranked + (1 if support & L else 0), f"row {i}: support size {n}"
+            _values_ok(i, rt, row, vt[:n], "teacher")
+            _values_ok(i, rs, row, vs[:n], "student")
+            if support & L and lab is not None and 0 <= lab < V:
+                assert lab in row.tolist(), f"row {i}: label {lab} missing"
+            # the first ranked list: ordered, and nothing outranks its last element
+            vals, rk = (vt, rt) if support & T else (vs, rs)
+            _ranked_list_ok(i, rk, vals, row[:k], k, V, "ranked")
+            zt_b, zs_b = rt.r.copy(), rs.r.copy()
+            zt_b[row] = vt[:n]
+            zs_b[row] = vs[:n]
+            labs = None if lab is None else np.array([lab])
+            ref_sup = O.tail_support(rs.r[None], rt.r[None], k, support, labs)[0]
+            if np.array_equal(ref_sup[ref_sup >= 0], row):
+                exact += 1
+            else:
+                # explained by the kernel's own (admissible) roundings of the support's
+                # logits (order or membership), or else by an ambiguous logit near a
+                # ranked model's k-th key (a rounding the kernel does not return)
+                flagged += 1
+                own = O.tail_support(zs_b[None], zt_b[None], k, support, labs)[0]
+                amb = np.array_equal(own[own >= 0], row) or \
+                    (bool(support & T) and rt.ambiguous(_near_kth(rt, k)).any()) or \
+                    (bool(support & S) and rs.ambiguous(_near_kth(rs, k)).any())
+                assert amb, f"row {i}: support differs without ambiguity"
+            ref = O.tail_divergence(zs_b[None], zt_b[None], row[None], beta, tau)
+            for f in ("loss", "p_mass", "q_mass", "lse_s", "lse_t"):
+                assert_close(f"row {i} {f}", res[f][nn:nn + 1], ref[f])
+    record_counts(f"tail k={k} beta={beta} support={support} V={V}", len(rows), exact, flagged)
     return exact, flagged

@@ -40,8 +40,9 @@ KD_OP_FWD, KD_OP_BWD, KD_OP_TOPK, KD_OP_BWD_W, KD_OP_TOPK_BWD, KD_OP_TAIL, KD_OP
 KD_SUPPORT_TEACHER, KD_SUPPORT_STUDENT, KD_SUPPORT_LABEL = 1, 2, 4
 KD_TOPK_MAX = 64
 KD_TOPK_MAX_V = 524288
-EXPORTED = ("kd_workspace_size", "kd_default_chunk", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_tail_fwd", "kd_tail_bwd",
-            "kd_gather_rows", "kd_scatter_rows", "kd_status_string", "kd_last_error")
+EXPORTED = ("kd_workspace_size", "kd_default_chunk", "kd_fwd", "kd_bwd",
+            "kd_topk_fwd", "kd_topk_bwd", "kd_tail_fwd", "kd_tail_bwd", "kd_gather_rows", "kd_scatter_rows",
+            "kd_status_string", "kd_last_error")
 
 
 class KDError(RuntimeError):
@@ -494,18 +495,37 @@ class _TopK(torch.autograd.Function):
 
 def topk_kd(xs, xt, ws, wt, k=64, labels=None, temperature=1.0, ignore_index=-100, chunk_V=0):
     """Top-k three-term KD terms per token: dict with ``binary``, ``cond``,
-    ``ce`` (when labels are given; these three carry the gradient to ``xs``),
-    masses, LSEs and the selection."""
+    ``ce`` (when labels are given; these three carry the gradient to ``xs``,
+    one value per position), masses, LSEs and the selection.
+
+    Tokens whose label is ``ignore_index`` are gathered out before the sweep
+    ([Top-K KD] 二.4), as in the other losses: their binary / cond / ce are 0
+    and get no gradient, and the other entries of the dict (masses, LSEs,
+    ``idx``, ...) then cover the kept tokens only, listed in ``rows`` (None
+    when every token is kept)."""
     d_s, d_t = xs.shape[-1], xt.shape[-1]
+    xs2 = xs.reshape(-1, d_s).contiguous()
+    xt2 = xt.reshape(-1, d_t).contiguous()
+    n_all = xs2.shape[0]
     lab = None
+    rows = None
     if labels is not None:
         lab = labels.reshape(-1).to(torch.int32).contiguous()
-        lab = torch.where(lab == ignore_index, torch.full_like(lab, -100), lab)
-    xs2 = xs.reshape(-1, d_s).contiguous()
+        valid = lab != ignore_index
+        if not bool(valid.all()):
+            rows = torch.nonzero(valid).reshape(-1).to(torch.int32)
+            if rows.numel() == 0:  # nothing carries a loss
+                zero = _no_tokens(xs, xt, ws, wt, (n_all,), "none")
+                return dict(binary=zero, cond=zero.clone(), ce=zero.clone(), rows=rows)
+            xs2, xt2 = _Rows.apply(xs2, rows), _Rows.apply(xt2, rows)
+            lab = lab.index_select(0, rows.long()).contiguous()
     holder = {}
-    binary, cond, ce = _TopK.apply(xs2, ws.contiguous(), xt.reshape(-1, d_t).contiguous(), wt.contiguous(), int(k),
-                                   float(temperature), lab, int(chunk_V), holder)
-    holder.update(binary=binary, cond=cond, ce=ce if lab is not None else None)
+    binary, cond, ce = _TopK.apply(xs2, ws.contiguous(), xt2, wt.contiguous(), int(k), float(temperature), lab,
+                                   int(chunk_V), holder)
+    if rows is not None:  # back to one value per position, 0 where ignored
+        binary, cond, ce = (_Unrows.apply(t.reshape(-1, 1).contiguous(), rows, n_all).reshape(-1)
+                            for t in (binary, cond, ce))
+    holder.update(binary=binary, cond=cond, ce=ce if lab is not None else None, rows=rows)
     return holder
 
 
