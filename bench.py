@@ -145,13 +145,35 @@ def cpu_baseline(w, beta, rows_n, path="kd", with_dw=False, k=64, support=None):
         O.kd_tail_bwd(hs, w.W_s, ht, w.W_t, k, beta, w.tau, sup=out["sup"])
         what = f"tail-bucket divergence (k={k}, beta={beta}) + its dL/dh_s"
     dt = time.perf_counter() - t0
+    host = host_info()
+    # the oracle's arithmetic runs in BLAS (the GEMMs) and numpy's elementwise
+    # loops (one thread): the threads it used are the BLAS pool's
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": host["blas_threads"], "kind": "oracle",
+            "sample": f"{len(rows)} of {w.N} tokens of the same workload ({what}, fp64 numpy/BLAS), {dt:.1f} s",
+            "host": host}
+
+
+def host_info():
+    """Host cores available to this process, CPU model and BLAS library and
+    threads numpy uses (threadpoolctl)."""
+    info = {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": None, "blas": None, "blas_threads": 1}
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     try:
         from threadpoolctl import threadpool_info
-        threads = max(int(i.get("num_threads", 1)) for i in threadpool_info()) if threadpool_info() else 1
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if blas:
+            info["blas"] = f"{blas[0].get('internal_api')} {blas[0].get('version')}"
+            info["blas_threads"] = max(int(i.get("num_threads", 1)) for i in blas)
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} of {w.N} tokens of the same workload ({what}, fp64 numpy/BLAS), {dt:.1f} s"}
+        info["blas_threads"] = info["affinity_cores"]
+    return info
 
 
 def main():
