@@ -141,6 +141,28 @@ kd_status kd_fwd(const void* h_s, const void* W_s, const void* h_t, const void* 
                  float* lse_t, float* aux, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * kd_fwd_noalloc - kd_fwd without a workspace argument and without any device
+ *   allocation, for callers that cannot allocate: code under HIP graph
+ *   capture, tight serving loops, harnesses that forbid hipMalloc.
+ *   Same arguments, results and kernels as kd_fwd (bit for bit), minus
+ *   workspace / ws_bytes. The forward's partial records go to a fixed
+ *   scratch array of kd_fwd_noalloc_max_scratch() bytes (144 MiB) that the
+ *   library holds on each GPU it runs on until the process ends; a shape
+ *   whose kd_workspace_size(KD_OP_FWD, ...) exceeds it returns
+ *   KD_ERR_WORKSPACE (before any HIP call that touches the GPU). The array's
+ *   device address is looked up once per device, on the first call with that
+ *   device current. Calls on one GPU share the array: calls that overlap on
+ *   one GPU (other streams, other host threads) race and must be ordered by
+ *   the caller.
+ */
+kd_status kd_fwd_noalloc(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
+                         int32_t d_s, int32_t d_t, float beta, float tau, kd_dtype dtype, float* loss, float* lse_s,
+                         float* lse_t, float* aux, void* stream);
+
+/* Size in bytes of kd_fwd_noalloc's scratch array. Pure host function. */
+size_t kd_fwd_noalloc_max_scratch(void);
+
+/*
  * kd_bwd - gradient of sum_n grad_loss[n] * loss[n] with respect to h_s and,
  *   optionally, W_s.
  *   Source: Nitrobrew notes, "仓库实现": the gradient is recomputed block by

@@ -26,7 +26,7 @@ import os
 import torch
 
 __all__ = [
-    "KDError", "load_library", "workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd",
+    "KDError", "load_library", "workspace_size", "kd_fwd", "kd_fwd_noalloc", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd",
     "kd_tail_fwd", "kd_tail_bwd", "kd_gather_rows", "kd_scatter_rows",
     "forward_kl", "reverse_kl", "jsd", "topk_kd", "tail_kd", "tail_default_support", "KD_TOPK_MAX",
     "KD_SUPPORT_TEACHER", "KD_SUPPORT_STUDENT", "KD_SUPPORT_LABEL",
@@ -40,7 +40,7 @@ KD_OP_FWD, KD_OP_BWD, KD_OP_TOPK, KD_OP_BWD_W, KD_OP_TOPK_BWD, KD_OP_TAIL, KD_OP
 KD_SUPPORT_TEACHER, KD_SUPPORT_STUDENT, KD_SUPPORT_LABEL = 1, 2, 4
 KD_TOPK_MAX = 64
 KD_TOPK_MAX_V = 524288
-EXPORTED = ("kd_workspace_size", "kd_default_chunk", "kd_fwd", "kd_bwd",
+EXPORTED = ("kd_workspace_size", "kd_default_chunk", "kd_fwd", "kd_fwd_noalloc", "kd_fwd_noalloc_max_scratch", "kd_bwd",
             "kd_topk_fwd", "kd_topk_bwd", "kd_tail_fwd", "kd_tail_bwd", "kd_gather_rows", "kd_scatter_rows",
             "kd_status_string", "kd_last_error")
 
@@ -77,11 +77,14 @@ def load_library(path: str = LIB_PATH):
                                 vp, vp, vp, vp, vp, vp, sz, vp]
     lib.kd_tail_bwd.argtypes = [vp, vp, i64, i64, i32, i32, i32, f32, f32, ctypes.c_int, vp, vp, vp, vp, vp, vp, i32,
                                 vp, vp, sz, vp]
+    lib.kd_fwd_noalloc.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, f32, f32, ctypes.c_int, vp, vp, vp, vp, vp]
+    lib.kd_fwd_noalloc_max_scratch.argtypes = []
+    lib.kd_fwd_noalloc_max_scratch.restype = sz
     lib.kd_default_chunk.argtypes = [i64, i64, ctypes.c_int]
     lib.kd_default_chunk.restype = i32
     lib.kd_gather_rows.argtypes = [vp, i64, i64, vp, i64, vp, vp]
     lib.kd_scatter_rows.argtypes = [vp, i64, i64, vp, vp, i64, vp]
-    for fn in ("kd_workspace_size", "kd_fwd", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_tail_fwd", "kd_tail_bwd",
+    for fn in ("kd_workspace_size", "kd_fwd", "kd_fwd_noalloc", "kd_bwd", "kd_topk_fwd", "kd_topk_bwd", "kd_tail_fwd", "kd_tail_bwd",
                "kd_gather_rows", "kd_scatter_rows"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.kd_status_string.argtypes = [ctypes.c_int]
@@ -167,6 +170,23 @@ def kd_fwd(h_s, W_s, h_t, W_t, beta: float, tau: float, workspace=None, stream=N
     _check(lib.kd_fwd(_ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t), N, V, d_s, d_t, float(beta), float(tau), dt,
                       _ptr(loss), _ptr(lse_s), _ptr(lse_t), _ptr(aux), _ptr(ws), ws.numel() * ws.element_size(),
                       _stream(stream)))
+    return loss, lse_s, lse_t, aux
+
+
+def kd_fwd_noalloc(h_s, W_s, h_t, W_t, beta: float, tau: float, out=None, stream=None):
+    """kd_fwd without a workspace: the library's fixed per-GPU scratch holds
+    the partial records. ``out``: optional (loss, lse_s, lse_t, aux) fp32 [N]
+    tensors to write (else new ones). Returns (loss, lse_s, lse_t, aux)."""
+    lib = load_library()
+    N, V, d_s, d_t, dt = _inputs(h_s, W_s, h_t, W_t)
+    if out is None:
+        out = tuple(torch.empty(N, dtype=torch.float32, device=h_s.device) for _ in range(4))
+    for t in out:
+        if t.dtype != torch.float32 or t.numel() != N or not t.is_contiguous():
+            raise ValueError(f"outputs must be contiguous fp32 tensors of {N} elements")
+    loss, lse_s, lse_t, aux = out
+    _check(lib.kd_fwd_noalloc(_ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t), N, V, d_s, d_t, float(beta), float(tau), dt,
+                              _ptr(loss), _ptr(lse_s), _ptr(lse_t), _ptr(aux), _stream(stream)))
     return loss, lse_s, lse_t, aux
 
 

@@ -7,6 +7,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
@@ -14,6 +15,18 @@
 
 namespace {
 
+// kd_fwd_noalloc's scratch: the forward's partial records live in this array
+// instead of a caller workspace. Each GPU the library runs on holds its own
+// copy until the process ends; calls on one GPU share it. In host code the
+// name is only a stand-in: its device address comes from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = (size_t)144 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+// Device address of `scratch` on each device, looked up once per device (with
+// that device current) on the first kd_fwd_noalloc call there.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
 
 thread_local char g_last_error[256] = "";
 
@@ -157,6 +170,51 @@ kd_status kd_fwd(const void* h_s, const void* W_s, const void* h_t, const void* 
   hipError_t e = kd::run_fwd(p, io, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KD_OK : hip_fail(e, "kd_fwd launch");
 }
+
+kd_status kd_fwd_noalloc(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
+                         int32_t d_s, int32_t d_t, float beta, float tau, kd_dtype dtype, float* loss, float* lse_s,
+                         float* lse_t, float* aux, void* stream) {
+  g_last_error[0] = 0;
+  kd_status s = check_common(h_s, W_s, h_t, W_t, N, V, d_s, d_t, dtype);
+  if (s != KD_OK) return s;
+  if (bad_beta(beta)) return fail(KD_ERR_INVALID_ARG, "beta outside [0, 1]");
+  if (bad_tau(tau)) return fail(KD_ERR_INVALID_ARG, "tau must be positive and finite");
+  if (!loss || !lse_s || !lse_t) return fail(KD_ERR_INVALID_ARG, "null output pointer (loss, lse_s, lse_t)");
+  if (!aux && beta > 0.f) return fail(KD_ERR_INVALID_ARG, "aux may be null only for beta == 0");
+  if (!aligned4(loss) || !aligned4(lse_s) || !aligned4(lse_t) || (aux && !aligned4(aux)))
+    return fail(KD_ERR_UNSUPPORTED, "outputs must be 4-byte aligned");
+  const kd::Plan p = kd::make_plan(N, V, d_s, d_t, dtype == KD_BF16);
+  const size_t need = kd::fwd_workspace_bytes(p, beta > 0.f && beta < 1.f);
+  if (need > kNoAllocScratchBytes) {
+    snprintf(g_last_error, sizeof(g_last_error),
+             "kd_fwd_noalloc: this shape needs %zu bytes of scratch, above its fixed %zu (use kd_fwd with a workspace)",
+             need, kNoAllocScratchBytes);
+    return KD_ERR_WORKSPACE;
+  }
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "kd_fwd_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(KD_ERR_UNSUPPORTED, "kd_fwd_noalloc: device index above 63");
+  void* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      e = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !g_scratch_ptr[dev]) {
+        g_scratch_ptr[dev] = nullptr;
+        return hip_fail(e, "kd_fwd_noalloc: hipGetSymbolAddress(scratch)");
+      }
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  // every partial record the merge reads is written by the sweep first: the
+  // previous call's contents need no clearing
+  kd::FwdIO io{h_s, W_s, h_t, W_t, beta, tau, loss, lse_s, lse_t, aux, ptr};
+  e = kd::run_fwd(p, io, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KD_OK : hip_fail(e, "kd_fwd_noalloc launch");
+}
+
+size_t kd_fwd_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
 
 kd_status kd_bwd(const void* h_s, const void* W_s, const void* h_t, const void* W_t, int64_t N, int64_t V,
                  int32_t d_s, int32_t d_t, float beta, float tau, kd_dtype dtype, int32_t chunk_V,
