@@ -29,11 +29,16 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Round an fp32 value to bf16 (nearest, ties to even); finite inputs.
+// Round fp32 to bf16, nearest with ties to even (gfx950's v_cvt_pk_bf16_f32,
+// which rounds finite values, ties and denormals alike the same way as the
+// integer form u + 0x7FFF + ((u >> 16) & 1) taken over the top 16 bits).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // Wave64 reductions (every lane receives the result).

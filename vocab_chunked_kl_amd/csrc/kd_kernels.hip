@@ -500,8 +500,8 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
               }
             }
             if constexpr (kBf16) {
-              w2[h].x = f32_to_bf16_bits(g4[0]) | (f32_to_bf16_bits(g4[1]) << 16);
-              w2[h].y = f32_to_bf16_bits(g4[2]) | (f32_to_bf16_bits(g4[3]) << 16);
+              w2[h].x = pack_bf16x2(g4[0], g4[1]);
+              w2[h].y = pack_bf16x2(g4[2], g4[3]);
               // the stored values, widened back to fp32
               es[nb] += (__builtin_bit_cast(float, w2[h].x << 16) + __builtin_bit_cast(float, w2[h].x & 0xFFFF0000u)) +
                         (__builtin_bit_cast(float, w2[h].y << 16) + __builtin_bit_cast(float, w2[h].y & 0xFFFF0000u));
@@ -831,8 +831,8 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_g_kernel(DenseArgs a) 
               const float rr = fast_exp2(fmaf(zb, kLog2e, -L12[nb]));
               g4[e] = (v < a.V) ? fmaf(A[nb], q, C[nb] * rr) : 0.f;
             }
-            w2[h].x = f32_to_bf16_bits(g4[0]) | (f32_to_bf16_bits(g4[1]) << 16);
-            w2[h].y = f32_to_bf16_bits(g4[2]) | (f32_to_bf16_bits(g4[3]) << 16);
+            w2[h].x = pack_bf16x2(g4[0], g4[1]);
+            w2[h].y = pack_bf16x2(g4[2], g4[3]);
           }
           store_g16(a.G, a.ldg, n, a.N, vrow0 + mb * 32 + 16 * pr - a.g_col0, w2, lane);
         }
