@@ -14,8 +14,9 @@
 // ordered by one 32-bit word: (order-preserving bf16 key << 16) | (0xFFFF -
 // index within the split), i.e. key descending, then index ascending. Only
 // values above the token's current k-th word enter a small candidate buffer;
-// after each tile the buffers are merged into the running lists by a bitonic
-// sort in registers.
+// a buffer that is nearly full (or overflowed, or at the block's last tile) is
+// merged into the running list: by insertion once the list holds k words,
+// else by a bitonic sort in registers.
 //
 // Merge kernel (one wave per token): merge the per-split log-sum-exps and
 // top-k lists, recompute the student logits at the selected indices and at
@@ -36,7 +37,8 @@ constexpr float kNegInf = -INFINITY;
 constexpr int kTopkSplit = 65536;
 constexpr int kCandCap = 16;       // candidate buffer entries per token per round (one list)
 constexpr int kCandCap2 = 12;      // the same with two lists (both models ranked at once)
-constexpr int kInsertMax = 6;      // a full list takes up to this many candidates by insertion
+constexpr int kInsertMax = 16;     // a full list takes up to this many candidates by insertion
+constexpr int kMergeSlack = 4;     // a buffer is merged once at most this many slots are free
 constexpr int kTopkFields = 6;     // m_s, l_s, m_t, l_t, m_1, l_1 (untempered student)
 
 struct TopkArgs {
@@ -305,10 +307,16 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
         }
       }
       const int any = __syncthreads_or(ov);
+      // a round that overflowed, and the block's last tile, merge every
+      // buffer; otherwise a buffer waits until it holds CAP - kMergeSlack
+      // candidates (the threshold lags meanwhile, so a few more entries pass
+      // the test, but each list row, long evicted from L2 by the unembedding
+      // stream, is read and written once per several candidates)
+      const int at = (any || vt + 1 == vt1) ? 1 : CAP - kMergeSlack;
       for (int t = wave; t < TN; t += NW)
 #pragma unroll
         for (int li = 0; li < NL; ++li)
-          if (cntB[li][t] > 0) merge_token(li, t);
+          if (cntB[li][t] >= at) merge_token(li, t);
       __syncthreads();
       if (!any) break;
     }
