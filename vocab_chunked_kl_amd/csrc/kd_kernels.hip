@@ -150,7 +150,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
   }
   const float beta = a.beta, omb = 1.f - a.beta;
 
-  auto epi = [&](int vt, auto& zs, auto& zt) {
+  auto epi = [&](int vt, auto& zs, auto& zt, char*) {
     const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
     const bool full = (int64_t)(vt + 1) * TM <= a.V;
 #pragma unroll
@@ -450,7 +450,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
   for (int nb = 0; nb < NB; ++nb) es[nb] = 0.f;
   const bool fix = a.esum != nullptr;
 
-  auto epi = [&](int vt, auto& zs, auto& zt) {
+  auto epi = [&](int vt, auto& zs, auto& zt, char*) {
     const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -713,7 +713,7 @@ __global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
   // Read-modify-write of dh, one 32-row slice at a time: all loads of the
   // slice are issued before its stores, so they overlap instead of forming a
   // chain of dependent round trips.
-  auto epi = [&](int tile, auto& acc, auto&) {
+  auto epi = [&](int tile, auto& acc, auto&, char*) {
     const int64_t d0 = (int64_t)dt * TN + wn * (TN / WN) + (lane & 31);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -809,7 +809,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_g_kernel(DenseArgs a) 
       }
     }
   }
-  auto epi = [&](int vt, auto& zs, auto&) {
+  auto epi = [&](int vt, auto& zs, auto&, char*) {
     const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {

@@ -313,6 +313,18 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
     issue(lds.b[I]);
     advance();
   });
+  // The epilogue also gets the stage buffer that the tile's last step read:
+  // no load targets it until the next step's barrier, so an epilogue may use
+  // it as scratch after a barrier of its own (other waves may still be
+  // reading their last fragments from it until then).
+  auto idle_stage = [&](int r) __attribute__((always_inline)) {
+    const int i = (r + NBUF - 1) % NBUF;
+    char* b = lds.b[0];
+    static_for<1, NBUF>([&](auto I) __attribute__((always_inline)) {
+      if (i == decltype(I)::value) b = lds.b[decltype(I)::value];
+    });
+    return b;
+  };
   int rot = 0;
   for (int tile = a_tile_begin; tile < a_tile_end; ++tile) {
     run(acc1, ks1, rot);
@@ -322,10 +334,10 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
         run(acc2, ks2, rot);
         rot = (rot + ks2) % NBUF;
       }
-      epi(tile, acc1, acc2);
+      epi(tile, acc1, acc2, idle_stage(rot));
       zero_acc(acc2);
     } else {
-      epi(tile, acc1, acc1);
+      epi(tile, acc1, acc1, idle_stage(rot));
     }
     zero_acc(acc1);
   }

@@ -39,6 +39,10 @@ constexpr int kCandCap = 16;       // candidate buffer entries per token per rou
 constexpr int kCandCap2 = 12;      // the same with two lists (both models ranked at once)
 constexpr int kInsertMax = 16;     // a full list takes up to this many candidates by insertion
 constexpr int kMergeSlack = 4;     // a buffer is merged once at most this many slots are free
+// A block's first tile fills empty lists: every entry passes the test, so with
+// one list its candidates go to the idle ring stage, 64 entries per token, and
+// the bitonic merge takes up to 128 words at once (4 rounds instead of 16).
+constexpr int kCandCapFirst = 64;
 constexpr int kTopkFields = 6;     // m_s, l_s, m_t, l_t, m_1, l_1 (untempered student)
 
 struct TopkArgs {
@@ -105,6 +109,9 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
   constexpr int NL = kTwo ? 2 : 1;                // lists: 0 teacher-ranked, 1 student-ranked
   constexpr int CAP = kTwo ? kCandCap2 : kCandCap;
+  constexpr int CAPF = kTwo ? kCandCap2 : kCandCapFirst;
+  static_assert(NL * TN * CAPF * sizeof(uint32_t) <= Ring<TM, TN>::kBytes, "first-tile buffers fit one stage");
+  static_assert(CAPF <= 64, "list and buffer fit the 128-word merge");
   // LDS: a three-stage ring, the candidate buffers and per-token counters.
   // The running top-k lists live in the per-split output rows of the
   // workspace (each token's row is read and written only by the wave that
@@ -138,14 +145,20 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
     ls[nb] = lt[nb] = l1[nb] = 0.f;
   }
 
-  // merge token t's candidate buffer into its state (one wave): the <= 80
+  // merge token t's candidate buffer into its state (one wave): the <= 128
   // words (S then B, zero-padded to 128, two per lane: element i = lane + 64 h)
   // are sorted descending by a bitonic network in registers (words are
   // distinct and nonzero, so the zeros sink), and the first min(total, k)
   // become the new state
+  // the candidate buffers of the current tile: B (CAP per token and list), or
+  // on a block's first tile the idle ring stage (CAPF)
+  uint32_t* cbuf = &B[0][0][0];
+  int ccap = CAP;
   auto merge_token = [&](int li, int t) {
     const int cs = cntS[li][t];
-    const int cb = min(cntB[li][t], CAP);
+    const int cap = kTwo ? CAP : ccap;
+    const int cb = min(cntB[li][t], cap);
+    const uint32_t* Bt = (kTwo ? &B[0][0][0] : cbuf) + (li * TN + t) * cap;
     const int total = cs + cb;
     uint32_t* Sg = (li ? a.lists2 : a.lists) + ((int64_t)sp * a.N + (int64_t)tt * TN + t) * K;  // token < N
     if (cs == K && cb <= kInsertMax) {
@@ -155,7 +168,7 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
       // move down one lane and the last one drops out.
       uint32_t e = lane < K ? Sg[lane] : 0u;
       for (int i = 0; i < cb; ++i) {
-        const uint32_t c = B[li][t][i];
+        const uint32_t c = Bt[i];
         const int rank = __popcll(__ballot(lane < K && e > c));
         const uint32_t up = __shfl(e, lane > 0 ? lane - 1 : 0);
         e = lane < rank ? e : (lane == rank ? c : up);
@@ -168,9 +181,9 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
       }
       return;
     }
-    uint32_t e0 = lane < cs ? Sg[lane] : (lane - cs < cb ? B[li][t][lane - cs] : 0u);
+    uint32_t e0 = lane < cs ? Sg[lane] : (lane - cs < cb ? Bt[lane - cs] : 0u);
     const int j1 = lane + 64;
-    uint32_t e1 = j1 - cs < cb ? B[li][t][j1 - cs] : 0u;  // cs <= 64 <= j1
+    uint32_t e1 = j1 - cs < cb ? Bt[j1 - cs] : 0u;  // cs <= 64 <= j1
 #pragma unroll
     for (int k = 2; k <= 128; k <<= 1) {
 #pragma unroll
@@ -199,7 +212,7 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
     }
   };
 
-  auto epi = [&](int vt, auto& zs, auto& zt) {
+  auto epi = [&](int vt, auto& zs, auto& zt, char* idle) {
     const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
     const bool full = (int64_t)(vt + 1) * TM <= a.V;
     // 1) round both logit tiles to bf16; 2) online LSEs of the tempered values
@@ -270,6 +283,14 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
 #pragma unroll
         for (int i = 0; i < kDoneWords; ++i) done[li][nb][i] = 0u;
     const int rel0 = (int)(vrow0 - vbase);
+    // (two lists: their registers leave no room for this, B serves throughout)
+    bool first = false;
+    if constexpr (!kTwo) {
+      first = vt == vt0;
+      cbuf = first ? reinterpret_cast<uint32_t*>(idle) : &B[0][0][0];
+      ccap = first ? CAPF : CAP;
+      if (first) __syncthreads();  // every wave is done with its fragments of the idle stage
+    }
     while (true) {
       int ov = 0;
 #pragma unroll
@@ -296,8 +317,15 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
               const uint32_t w = (key << 16) | (0xFFFFu - (uint32_t)rel);
               if (ok && tok_ok && w > th && !((done[li][nb][bit >> 5] >> (bit & 31)) & 1u)) {
                 const int slot = atomicAdd(&cntB[li][col], 1);
-                if (slot < CAP) {
-                  B[li][col][slot] = w;
+                if constexpr (kTwo) {
+                  if (slot < CAP) {
+                    B[li][col][slot] = w;
+                    done[li][nb][bit >> 5] |= 1u << (bit & 31);
+                  } else {
+                    ov = 1;
+                  }
+                } else if (slot < ccap) {
+                  cbuf[col * ccap + slot] = w;
                   done[li][nb][bit >> 5] |= 1u << (bit & 31);
                 } else {
                   ov = 1;
@@ -312,7 +340,7 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
       // candidates (the threshold lags meanwhile, so a few more entries pass
       // the test, but each list row, long evicted from L2 by the unembedding
       // stream, is read and written once per several candidates)
-      const int at = (any || vt + 1 == vt1) ? 1 : CAP - kMergeSlack;
+      const int at = (any || first || vt + 1 == vt1) ? 1 : CAP - kMergeSlack;
       for (int t = wave; t < TN; t += NW)
 #pragma unroll
         for (int li = 0; li < NL; ++li)
