@@ -560,14 +560,27 @@ __global__ __launch_bounds__(256) void big_init_kernel(int32_t* big, int64_t N) 
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < N; i += (int64_t)gridDim.x * 256) big[i] = -1;
 }
 
-// After each chunk: etot[n] (=|+=) the chunk's per-split sums, in split order.
+// After each chunk: etot[n] (=|+=) the chunk's per-split sums. A block takes
+// 64 tokens; wave w sums the splits w, w + 4, w + 8, ... of its lane's token
+// (eight loads in flight), then the four partial sums are added in wave
+// order: a fixed order, so the result is the same on every run.
+constexpr int kEsumTok = 64;
 __global__ __launch_bounds__(256) void esum_reduce_kernel(const float* __restrict__ part, int n_split, int64_t N,
                                                           float* __restrict__ etot, int first) {
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
+  __shared__ float red[4][kEsumTok];
+  const int tl = threadIdx.x % kEsumTok, w = threadIdx.x / kEsumTok;
+  const int64_t n = (int64_t)blockIdx.x * kEsumTok + tl;
   float t = 0.f;
-  for (int s = 0; s < n_split; ++s) t += part[(int64_t)s * N + n];
-  etot[n] = first ? t : etot[n] + t;
+  if (n < N) {
+#pragma unroll 8
+    for (int s = w; s < n_split; s += 4) t += part[(int64_t)s * N + n];
+  }
+  red[w][tl] = t;
+  __syncthreads();
+  if (w == 0 && n < N) {
+    const float u = (red[0][tl] + red[1][tl]) + (red[2][tl] + red[3][tl]);
+    etot[n] = first ? u : etot[n] + u;
+  }
 }
 
 // After the last chunk. The gradient entries of a token sum to zero for every
@@ -1335,8 +1348,8 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
       da.dh = io.dh;
       da.first = c0 == 0;
       if ((e = launch_dh(p, p.bf16, da, io.chunk_V, kcols, part, st)) != hipSuccess) return e;
-      hipLaunchKernelGGL(esum_reduce_kernel, dim3(tok_blocks), dim3(256), 0, st, esum, la.n_splits, p.N, etot,
-                         c0 == 0 ? 1 : 0);
+      hipLaunchKernelGGL(esum_reduce_kernel, dim3((unsigned)((p.N + kEsumTok - 1) / kEsumTok)), dim3(256), 0, st,
+                         esum, la.n_splits, p.N, etot, c0 == 0 ? 1 : 0);
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (io.dW) {
