@@ -149,4 +149,10 @@ __device__ __forceinline__ int xcd_remap(int b, int nblocks) {
   return (b & 7) * (nblocks >> 3) + (b >> 3);
 }
 
+// The XCD-ordered kernels launch their grid rounded up to a multiple of 8, so
+// that the remap applies whatever the tile count (otherwise the token tiles of
+// one vocabulary split would land on different XCDs and each fetch the same
+// unembedding rows); the blocks past the tile count leave at once.
+__host__ __device__ constexpr int xcd_grid(int n) { return (n + 7) & ~7; }
+
 }  // namespace kd

@@ -124,6 +124,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
   KD_RING_LDS_N(TM, TN, kLogitRB, NBUF);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
+  if (L >= a.n_tok_tiles * a.n_splits) return;  // grid padding
   int tt, sp;
   block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_splits, tt, sp);
   const int vt0 = sp * a.tiles_per_split;
@@ -421,6 +422,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
   KD_RING_LDS_N(TM, TN, kLogitRB, NBUF);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
+  if (L >= a.n_tok_tiles * a.n_splits) return;  // grid padding
   int tt, sp;
   block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_splits, tt, sp);
   const int vt0 = a.vt_offset + sp * a.tiles_per_split;
@@ -707,6 +709,7 @@ __global__ __launch_bounds__(kDhThreads, 1) void dh_kernel(DhArgs a) {
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
   KD_RING_LDS_N(TM, TN, kDhRB, NBUF);
   const int L0 = xcd_remap(blockIdx.x, gridDim.x);
+  if (L0 >= a.n_tok_tiles * a.n_d_tiles * a.n_ksplit) return;  // grid padding
   const int per_split = a.n_tok_tiles * a.n_d_tiles;
   const int ks = L0 / per_split;  // 0 unless the contraction is split
   int tt, dt;
@@ -802,6 +805,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_g_kernel(DenseArgs a) 
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
   KD_RING_LDS_N(TM, TN, kDhRB, kDhBuf);
   const int L = xcd_remap(blockIdx.x, gridDim.x);
+  if (L >= a.n_tok_tiles * a.n_splits) return;  // grid padding
   int tt, sp;
   block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_splits, tt, sp);
   const int vt0 = a.vt_offset + sp * a.tiles_per_split;
@@ -1212,7 +1216,7 @@ static hipError_t launch_dh(const Plan& p, bool bf16, DhArgs da, int32_t chunk_V
     da.kspan = (int32_t)(per * kTileV * p.esz);
     da.part = part;
   }
-  const dim3 grid((unsigned)(n_tok_tiles * n_d_tiles * da.n_ksplit));
+  const dim3 grid((unsigned)xcd_grid(n_tok_tiles * n_d_tiles * da.n_ksplit));
   const bool small = p.N <= kSmallT;  // one token tile either way
   if (bf16 && small)
     hipLaunchKernelGGL((dh_kernel<true, true>), grid, dim3(kDhThreads), 0, st, da);
@@ -1237,7 +1241,7 @@ hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
   la.n_vtiles = p.n_vtiles;
   la.vt_offset = 0;
   la.part = static_cast<float*>(io.workspace);
-  const dim3 grid(p.n_tok_tiles * p.n_splits);
+  const dim3 grid(xcd_grid(p.n_tok_tiles * p.n_splits));
   const bool small = p.N <= kSmallT;  // one token tile either way; the 64-row tile has a deeper ring
   hipError_t e;
   if (io.beta == 0.f || io.beta == 1.f) {
@@ -1312,7 +1316,7 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
     return hipGetLastError();
   };
   auto gemm = [&](const DhArgs& da, int n_row_tiles) {
-    const dim3 dgrid(n_row_tiles * n_d_tiles);
+    const dim3 dgrid(xcd_grid(n_row_tiles * n_d_tiles));
     if (p.bf16)
       hipLaunchKernelGGL((dh_kernel<true, false>), dgrid, dim3(kDhThreads), 0, st, da);
     else
@@ -1334,7 +1338,7 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
     la.tiles_per_split = bwd_tiles_per_block(p, ctiles);
     la.n_splits = (ctiles + la.tiles_per_split - 1) / la.tiles_per_split;
     la.g_col0 = c0;
-    const dim3 grid(p.n_tok_tiles * la.n_splits);
+    const dim3 grid(xcd_grid(p.n_tok_tiles * la.n_splits));
     e = p.bf16 ? launch_bwdg_mode<true>(mode, small, grid, la, st) : launch_bwdg_mode<false>(mode, small, grid, la, st);
     if (e != hipSuccess) return e;
     if (io.dh) {
@@ -1396,7 +1400,7 @@ static hipError_t run_list_chunks(const Plan& p, DenseArgs a, const int32_t* lis
     a.n_vtiles = ctiles;
     a.n_splits = ctiles;
     a.g_col0 = c0;
-    hipLaunchKernelGGL(dense_g_kernel, dim3(a.n_tok_tiles * ctiles), dim3(kDenseThreads), 0, st, a);
+    hipLaunchKernelGGL(dense_g_kernel, dim3(xcd_grid(a.n_tok_tiles * ctiles)), dim3(kDenseThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     f.c0 = c0;
     f.ccols = ccols;

@@ -122,6 +122,7 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
   __shared__ uint32_t theta[NL][TN];       // k-th word once full, else 0
 
   const int L = xcd_remap(blockIdx.x, gridDim.x);
+  if (L >= a.n_tok_tiles * a.n_splits) return;  // grid padding
   int tt, sp;
   block_coords<kTokGroup>(L, a.n_tok_tiles, a.n_splits, tt, sp);
   const int vt0 = sp * a.tiles_per_split;
@@ -768,7 +769,7 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   a.lists = reinterpret_cast<uint32_t*>(static_cast<char*>(io.workspace) +
                                         align_up((size_t)kTopkFields * a.n_splits * p.N * sizeof(float), 256));
   const bool sep1 = (io.labels != nullptr || io.lse_s1 != nullptr) && io.tau != 1.f;
-  const dim3 grid(a.n_tok_tiles * a.n_splits);
+  const dim3 grid(xcd_grid(a.n_tok_tiles * a.n_splits));
   if (sep1)
     hipLaunchKernelGGL((topk_sweep_kernel<true, false>), grid, dim3(kTopkThreads), 0, st, a);
   else
@@ -838,7 +839,7 @@ hipError_t run_tail(const Plan& p, const TailIO& io, hipStream_t st) {
   const size_t list_bytes = align_up((size_t)a.n_splits * p.N * io.k * sizeof(uint32_t), 256);
   uint32_t* lists_t = reinterpret_cast<uint32_t*>(ws + part_bytes);
   uint32_t* lists_s = reinterpret_cast<uint32_t*>(ws + part_bytes + list_bytes);
-  const dim3 grid(a.n_tok_tiles * a.n_splits);
+  const dim3 grid(xcd_grid(a.n_tok_tiles * a.n_splits));
   // one sweep: the teacher's list, the student's (the same sweep with the
   // two operand pairs exchanged) or both at once
   const bool rank_t = io.support & KD_SUPPORT_TEACHER, rank_s = io.support & KD_SUPPORT_STUDENT;
