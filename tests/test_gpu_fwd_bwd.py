@@ -141,6 +141,19 @@ def test_workload_rkl_v152k_n4k_all_rows():
     run_case(kd, torch, (w.h_s, w.W_s, w.h_t, w.W_t), 1.0, w.tau, chunk_V=0)
 
 
+@pytest.mark.parametrize("n,beta", [(192, 1.0), (256, 1.0), (256, 0.5), (512, 1.0)])
+def test_small_n_sweep_shapes_all_rows(n, beta):
+    """The small-N sweep's shapes (the 4k-token workload's vocabulary and
+    hidden sizes at a few hundred tokens), every row, forward and dL/dh_s at
+    the default (whole-vocabulary) chunk. These forward grids (token tiles x
+    vocabulary splits: 238 blocks at 256 tokens, 476 at 512) are not
+    multiples of 8, so they run rounded up with idle padding blocks."""
+    kd, torch = _kd()
+    w = workload(2)
+    _say(f"{w.name} shapes N={n} V={w.V} beta={beta} all rows, default chunk")
+    run_case(kd, torch, (w.h_s[:n], w.W_s, w.h_t[:n], w.W_t), beta, w.tau, chunk_V=0)
+
+
 @pytest.mark.parametrize("beta", [0.0, 0.5, 1.0])
 def test_workload_jsd_sweep_v152k_n32k_1024_rows(beta):
     """1024 seeded rows (first and last included) of the benchmarked workload,
