@@ -799,7 +799,11 @@ struct DenseArgs {
 // One operand pair and one accumulator, so the block takes the dh GEMM's
 // 256 x 256 tile (256 vocabulary entries x 256 tokens, 64 x 128 per wave) and
 // its ring of two 64 KiB stages: half the token-operand bytes per flop of the
-// two-accumulator logit tile.
+// two-accumulator logit tile. kR: the untempered softmax r differs from q
+// (a CE term at tau != 1); otherwise C is 0 or r equals q bit for bit (at
+// tau = 1 the forward returns the same LSE for both), and one exponential
+// per entry serves.
+template <bool kR>
 __global__ __launch_bounds__(kDenseThreads, 1) void dense_g_kernel(DenseArgs a) {
   constexpr int TM = kTileV, TN = kDenseT, WM = kDhWM, WN = kDhWN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
@@ -845,7 +849,7 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_g_kernel(DenseArgs a) 
               const int64_t v = vrow0 + mb * 32 + acc_row(r, lane);
               const float zb = __builtin_bit_cast(float, f32_to_bf16_bits(zs[mb][nb][r]) << 16);
               const float q = fast_exp2(fmaf(zb, a.c2, -Ls2[nb]));
-              const float rr = fast_exp2(fmaf(zb, kLog2e, -L12[nb]));
+              const float rr = kR ? fast_exp2(fmaf(zb, kLog2e, -L12[nb])) : q;
               g4[e] = (v < a.V) ? fmaf(A[nb], q, C[nb] * rr) : 0.f;
             }
             w2[h].x = pack_bf16x2(g4[0], g4[1]);
@@ -1400,7 +1404,10 @@ static hipError_t run_list_chunks(const Plan& p, DenseArgs a, const int32_t* lis
     a.n_vtiles = ctiles;
     a.n_splits = ctiles;
     a.g_col0 = c0;
-    hipLaunchKernelGGL(dense_g_kernel, dim3(xcd_grid(a.n_tok_tiles * ctiles)), dim3(kDenseThreads), 0, st, a);
+    if (a.dense_c && a.c2 != kLog2e)
+      hipLaunchKernelGGL(dense_g_kernel<true>, dim3(xcd_grid(a.n_tok_tiles * ctiles)), dim3(kDenseThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(dense_g_kernel<false>, dim3(xcd_grid(a.n_tok_tiles * ctiles)), dim3(kDenseThreads), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     f.c0 = c0;
     f.ccols = ccols;
