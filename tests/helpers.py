@@ -307,3 +307,29 @@ def check_tail_rows(out, h_s, W_s, h_t, W_t, rows, k, beta, tau, support, labels
                 assert_close(f"row {i} {f}", res[f][nn:nn + 1], ref[f])
     record_counts(f"tail k={k} beta={beta} support={support} V={V}", len(rows), exact, flagged)
     return exact, flagged
+
+
+def exact_shifted_case(seed, N, V, d, shift=100.0):
+    """A case whose logits are exact in bf16 and whose student logits all lie
+    past the range of exp in fp32: hidden units in {0, 1}, unembedding entries
+    in {0, +-1/2}, and for the student a last hidden unit of ``shift`` against
+    an unembedding column of ones (a column of ``shift`` would instead scale
+    the bf16 rounding residue of the stored gradient, whose exact entries sum
+    to zero, into dL/dh_s). Every logit is then a multiple of 1/2
+    summed exactly in fp32; the student's lie near ``shift`` (kept below 128,
+    where bf16 still has steps of 1/2), so rounding them to bf16 is exact and
+    the softmax is that of the unshifted logits. The spread is small, so a
+    top-k of a few thousand entries holds little of either model's mass (the
+    mass outside it comes from a difference of log-sum-exps whose fp32
+    spacing grows with the offset)."""
+    g = np.random.default_rng(seed)
+    vals = np.array([-0.5, 0.0, 0.5], np.float32)
+    h_s = g.integers(0, 2, (N, d)).astype(np.float32)
+    W_s = vals[g.integers(0, 3, (V, d))]
+    h_t = g.integers(0, 2, (N, d)).astype(np.float32)
+    W_t = vals[g.integers(0, 3, (V, d))]
+    h_s[:, -1] = shift
+    W_s[:, -1] = 1.0
+    z = h_s @ W_s.T
+    assert z.min() > 89.0 and z.max() < 127.5, (z.min(), z.max())
+    return tuple(kdsynth.f32_to_bf16_bits(x) for x in (h_s, W_s, h_t, W_t))

@@ -10,7 +10,7 @@ import pytest
 
 import kdsynth
 from oracle import kd_oracle as O
-from tests.helpers import assert_close, assert_grad_rows, check_tail_rows, to_dev, workload
+from tests.helpers import assert_close, assert_grad_rows, check_tail_rows, exact_shifted_case, to_dev, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -52,6 +52,18 @@ def _case(kd, torch, arrays, k, beta, tau, support, labels, rows, grad_seed=None
 
 
 CASES = [(1, 0.5, T | L), (8, 0.0, T), (8, 1.0, S), (8, 0.5, T | S), (64, 0.3, T | S | L), (5, 1.0, S | L)]
+
+
+@pytest.mark.parametrize("beta,support", [(0.5, T | S), (1.0, S)])
+def test_tail_bwd_logits_past_exp_range(beta, support):
+    """Student logits near 100 (every logit raised by the same amount: the
+    divergence is unchanged, exp of a logit overflows fp32): forward and
+    backward against the oracle on every row."""
+    kd, torch = _kd()
+    N, V = 64, 3000
+    arrays = exact_shifted_case(29, N, V, 16)
+    print(f"tail shifted student logits N={N} V={V} beta={beta} support={support}", flush=True)
+    _case(kd, torch, arrays, 8, beta, 1.5, support, None, np.arange(N), grad_seed=36)
 
 
 @pytest.mark.parametrize("k,beta,support", CASES)

@@ -11,7 +11,7 @@ import pytest
 
 import kdsynth
 from oracle import kd_oracle as O
-from tests.helpers import assert_grad_rows, check_topk_rows, to_dev, workload
+from tests.helpers import assert_grad_rows, check_topk_rows, exact_shifted_case, to_dev, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -140,6 +140,18 @@ def test_topk_bwd_without_labels_and_k_equals_v():
     arrays = kdsynth.small_case(23, N, V, 16, 16)
     print("topk bwd k == V, no labels", flush=True)
     _bwd_case(kd, torch, arrays, 64, 1.0, None, np.arange(N), seed=32)
+
+
+@pytest.mark.parametrize("tau", [1.0, 1.5])
+def test_topk_bwd_logits_past_exp_range_without_ce(tau):
+    """Student logits near 100 and no CE term: the dense part of the gradient
+    (A q) must not evaluate exp of an unnormalised logit (which overflows and
+    turned 0 * inf into NaN); every row against the oracle."""
+    kd, torch = _kd()
+    N, V = 64, 3000
+    arrays = exact_shifted_case(27, N, V, 16)
+    print(f"topk bwd shifted student logits N={N} V={V} tau={tau}", flush=True)
+    _bwd_case(kd, torch, arrays, 8, tau, None, np.arange(N), seed=35)
 
 
 def test_topk_bwd_workload_v248k_1024_rows():
