@@ -20,7 +20,7 @@ import pytest
 
 import kdsynth
 from oracle import kd_oracle as O
-from tests.helpers import assert_close, assert_grad_rows, to_dev, upload, wgrad_floor, workload
+from tests.helpers import assert_close, assert_grad_rows, exact_shifted_case, to_dev, upload, wgrad_floor, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -99,6 +99,18 @@ def test_degenerate_shapes(N, V):
     for beta in (0.0, 0.5, 1.0):
         _say(f"degenerate N={N} V={V} beta={beta}")
         run_case(kd, torch, arrays, beta, 1.0, chunk_V=256)
+
+
+@pytest.mark.parametrize("beta", [0.0, 0.5, 1.0])
+def test_student_logits_offset_by_100(beta):
+    """Student logits exact in bf16 and all near 100 (a hidden unit of 100
+    against a column of ones; the softmax is that of the unshifted logits):
+    the log-sum-exps near 100 cancel against each other in the loss and in
+    the gradient's centring; every row against the oracle."""
+    kd, torch = _kd()
+    arrays = exact_shifted_case(41, 150, 3000, 16)
+    _say(f"student logits offset by 100 N=150 V=3000 beta={beta}")
+    run_case(kd, torch, arrays, beta, 1.5, chunk_V=1024)
 
 
 def test_identical_distributions_give_zero():
