@@ -287,15 +287,7 @@ def main():
     step_flops = fwd_flops * (2 if jsd else 1) + bwd_flops
     tok_s = N / (ms_step / 1e3)
     achieved = fwd_flops * (2 if jsd else 1) / (fwd_ms / 1e3) / 1e12
-    traffic = None
-    if os.path.exists(args.traffic):
-        try:
-            with open(args.traffic) as f:
-                tr = json.load(f)
-            if tr.get("kernel_source_hash") == kernel_hash():
-                traffic = tr.get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = recorded_traffic(args.traffic)
     out = {
         "metric": ("tokens/s + MFMA % of peak for fused chunked KL fwd+bwd, V=151936, N=32k" if args.workload == 3
                    else f"tokens/s + MFMA % of peak for fused chunked KL fwd+bwd, V={V}, N={N}"),
@@ -485,6 +477,17 @@ def bench_topk(args):
         torch.cuda.empty_cache()
         res["cpu_baseline"] = cpu_baseline(w, beta, args.cpu_rows, path=args.path, k=k, support=support)
     print(json.dumps(res), flush=True)
+
+
+def recorded_traffic(path):
+    """The forward sweep's HBM bytes per launch from a traffic record, or
+    None when there is none or it was taken on other kernel sources."""
+    try:
+        with open(path) as f:
+            tr = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return tr.get("bytes_per_launch") if tr.get("kernel_source_hash") == kernel_hash() else None
 
 
 def kernel_hash() -> str:

@@ -1,6 +1,7 @@
-"""Host-side logic of bench.py (CPU only): the one-GPU refusal and the
+"""Host-side logic of bench.py (CPU only): the one-GPU refusal, the
 traffic arithmetic (counter CSVs -> bytes per launch, scaled by the copy
-kernel's reading)."""
+kernel's reading) and the rule that a traffic record counts only for the
+kernel sources it was taken on."""
 import csv
 import json
 import os
@@ -45,3 +46,16 @@ def test_traffic_summary_scales_by_the_copy_kernel(tmp_path):
     assert rec["fetch_kib"] == 1500.0 and rec["write_kib"] == 10.0
     assert rec["bytes_per_launch"] == 1500.0 * 1024 * 2 + 10.0 * 1024
     assert rec["kernel_source_hash"] == bench.kernel_hash()
+
+
+def test_traffic_record_counts_only_for_its_sources(tmp_path):
+    sys.path.insert(0, ROOT)
+    import bench
+    rec = tmp_path / "t.json"
+    rec.write_text(json.dumps({"bytes_per_launch": 123.0, "kernel_source_hash": bench.kernel_hash()}))
+    assert bench.recorded_traffic(str(rec)) == 123.0
+    rec.write_text(json.dumps({"bytes_per_launch": 123.0, "kernel_source_hash": "0" * 16}))
+    assert bench.recorded_traffic(str(rec)) is None
+    rec.write_text("not json")
+    assert bench.recorded_traffic(str(rec)) is None
+    assert bench.recorded_traffic(str(tmp_path / "missing.json")) is None
