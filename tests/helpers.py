@@ -309,7 +309,7 @@ def check_tail_rows(out, h_s, W_s, h_t, W_t, rows, k, beta, tau, support, labels
     return exact, flagged
 
 
-def exact_shifted_case(seed, N, V, d, shift=100.0):
+def exact_shifted_case(seed, N, V, d, shift=100.0, head=0.0, n_head=8):
     """A case whose logits are exact in bf16 and whose student logits all lie
     past the range of exp in fp32: hidden units in {0, 1}, unembedding entries
     in {0, +-1/2}, and for the student a last hidden unit of ``shift`` against
@@ -319,15 +319,22 @@ def exact_shifted_case(seed, N, V, d, shift=100.0):
     summed exactly in fp32; the student's lie near ``shift`` (kept below 128,
     where bf16 still has steps of 1/2), so rounding them to bf16 is exact and
     the softmax is that of the unshifted logits. The spread is small, so a
-    top-k of a few thousand entries holds little of either model's mass (the
-    mass outside it comes from a difference of log-sum-exps whose fp32
-    spacing grows with the offset)."""
+    top-k of a few thousand entries holds little of either model's mass.
+    With a nonzero ``head`` the first ``n_head`` vocabulary rows lead both
+    models by ``head`` (a hidden unit of 1 against that column), so a top-k
+    of ``n_head`` holds most of both masses and the binary term of the
+    top-k decomposition is near zero."""
     g = np.random.default_rng(seed)
     vals = np.array([-0.5, 0.0, 0.5], np.float32)
     h_s = g.integers(0, 2, (N, d)).astype(np.float32)
     W_s = vals[g.integers(0, 3, (V, d))]
     h_t = g.integers(0, 2, (N, d)).astype(np.float32)
     W_t = vals[g.integers(0, 3, (V, d))]
+    if head:
+        for h, W in ((h_s, W_s), (h_t, W_t)):
+            h[:, -2] = 1.0
+            W[:, -2] = 0.0
+            W[:n_head, -2] = head
     h_s[:, -1] = shift
     W_s[:, -1] = 1.0
     z = h_s @ W_s.T

@@ -51,7 +51,6 @@ struct TopkArgs {
   int32_t d_s;
   int k;
   float c2;       // log2(e) / tau
-  float inv_tau;
   int n_tok_tiles, n_splits, tiles_per_split, n_vtiles;
   int swap;        // ps / pt hold the teacher / student pair: rank the student
   float* part;     // [kTopkFields][n_splits][N]
@@ -419,7 +418,7 @@ struct MergeArgs {
   int64_t N, V;
   int32_t d_s;
   int k, n_splits, split;  // split: vocabulary entries per split
-  float tau, inv_tau;
+  float c2;  // log2(e) / tau, the factor the sweep's base-2 maxima were formed with
   const float* part;
   const uint32_t* lists;
   const int32_t* labels;
@@ -513,17 +512,23 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
     if (a.val_t) a.val_t[n * K + lane] = tj;
     if (a.val_s) a.val_s[n * K + lane] = sj;
   }
-  const float t2 = tj * a.inv_tau, s2 = sj * a.inv_tau;
-  const float mtK = wave_max(act ? t2 : kNegInf), msK = wave_max(act ? s2 : kNegInf);
-  const float et = act ? expf(t2 - mtK) : 0.f, es = act ? expf(s2 - msK) : 0.f;
+  // The set's log-sum-exps in the sweep's base-2 frame: each selected logit is
+  // taken relative to the whole vocabulary's maximum with one fused
+  // multiply-add, so log P, log Q and the conditional term are formed from
+  // small numbers and a logit offset common to a row costs them no precision
+  // (a difference of two fp32 log-sum-exps near 100 is good to only ~1e-5).
+  const float dt = act ? fmaf(tj, a.c2, -mt) : kNegInf, ds = act ? fmaf(sj, a.c2, -ms) : kNegInf;
+  const float mtK = wave_max(dt), msK = wave_max(ds);
+  const float et = act ? exp2f(dt - mtK) : 0.f, es = act ? exp2f(ds - msK) : 0.f;
   const float set = wave_sum(et), ses = wave_sum(es);
-  const float LKt = mtK + logf(set), LKs = msK + logf(ses);
+  const float LKt = mtK + log2f(set), LKs = msK + log2f(ses);  // base 2, relative to mt and ms
   // Tail masses below fp32 resolution are held at 2^-24 so that their logs stay
   // finite; with the whole vocabulary selected there is no tail at all.
   const bool all = (int64_t)K >= a.V;
-  const float logP = fminf(LKt - Lt, -5.9604645e-8f), logQ = fminf(LKs - Ls, -5.9604645e-8f);
-  const float cterm = act ? (et / set) * ((t2 - LKt) - (s2 - LKs)) : 0.f;
-  const float condv = wave_sum(cterm);
+  const float logP = fminf((LKt - log2f(lt)) * kLn2, -5.9604645e-8f);
+  const float logQ = fminf((LKs - log2f(ls)) * kLn2, -5.9604645e-8f);
+  const float cterm = act ? (et / set) * ((dt - LKt) - (ds - LKs)) : 0.f;
+  const float condv = wave_sum(cterm) * kLn2;
   if (lane == 0) {
     const float P = expf(logP), Q = expf(logQ);
     const float l1P = log1mexp_f32(logP), l1Q = log1mexp_f32(logQ);
@@ -539,8 +544,11 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(MergeArgs a) {
   if (a.labels) {
     const int32_t y = a.labels[n];
     if (y >= 0 && y < a.V) {
+      // untempered LSE minus the label's logit, both relative to the untempered
+      // maximum (with tau = 1 the tempered record is the untempered one)
       const float zy = wave_dot_bf16(h, a.W_s, y, a.d_s, lane);
-      if (lane == 0) a.ce[n] = L1 - zy;
+      const float m1u = a.sep1 ? m1 : ms, l1u = a.sep1 ? l1 : ls;
+      if (lane == 0) a.ce[n] = (log2f(l1u) - fmaf(zy, kLog2e, -m1u)) * kLn2;
     } else if (lane == 0) {
       a.ce[n] = NAN;
     }
@@ -564,7 +572,8 @@ struct TailArgs {
   int64_t N, V;
   int32_t d_s, d_t;
   int k, n_splits, split, support, smax;  // split: vocabulary entries per split
-  float beta, inv_tau;
+  float beta;
+  float c2;  // log2(e) / tau, the factor the sweep's base-2 maxima were formed with
   const float* part;
   const uint32_t *lists_t, *lists_s;
   const int32_t* labels;
@@ -696,13 +705,16 @@ __global__ __launch_bounds__(256) void tail_merge_kernel(TailArgs a) {
   __builtin_amdgcn_wave_barrier();
 
   // 3) bucket log-probabilities: three slots per lane cover 2k + 1 <= 129 entries
+  //    (each logit relative to the vocabulary's base-2 maximum with one fused
+  //    multiply-add, so a logit offset common to a row costs no precision)
+  const float l2t = log2f(lt), l2s = log2f(ls);
   float lp[3], lq[3];
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const int i = lane + 64 * j;
     const bool ok = i < cnt;
-    lp[j] = ok ? st[i] * a.inv_tau - Lt : kNegInf;
-    lq[j] = ok ? ss[i] * a.inv_tau - Ls : kNegInf;
+    lp[j] = ok ? (fmaf(st[i], a.c2, -mt) - l2t) * kLn2 : kNegInf;
+    lq[j] = ok ? (fmaf(ss[i], a.c2, -ms) - l2s) * kLn2 : kNegInf;
   }
   const float logP = wave_lse3(lp[0], lp[1], lp[2]);
   const float logQ = wave_lse3(lq[0], lq[1], lq[2]);
@@ -759,7 +771,6 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   a.d_s = p.d_s;
   a.k = io.k;
   a.c2 = kLog2e / io.tau;
-  a.inv_tau = 1.f / io.tau;
   a.n_tok_tiles = (int)((p.N + kTopkT - 1) / kTopkT);
   a.n_vtiles = p.n_vtiles;
   a.n_splits = (int)((p.V + kTopkSplit - 1) / kTopkSplit);
@@ -785,8 +796,7 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   m.k = io.k;
   m.n_splits = a.n_splits;
   m.split = a.tiles_per_split * kTileV;
-  m.tau = io.tau;
-  m.inv_tau = 1.f / io.tau;
+  m.c2 = a.c2;
   m.part = a.part;
   m.lists = a.lists;
   m.labels = io.labels;
@@ -827,7 +837,6 @@ hipError_t run_tail(const Plan& p, const TailIO& io, hipStream_t st) {
   a.d_s = p.d_s;
   a.k = io.k;
   a.c2 = kLog2e / io.tau;
-  a.inv_tau = 1.f / io.tau;
   a.n_tok_tiles = (int)((p.N + kTopkT - 1) / kTopkT);
   a.n_vtiles = p.n_vtiles;
   a.n_splits = (int)((p.V + kTopkSplit - 1) / kTopkSplit);
@@ -875,7 +884,7 @@ hipError_t run_tail(const Plan& p, const TailIO& io, hipStream_t st) {
   m.support = io.support;
   m.smax = tail_support_slots(io.k, io.support);
   m.beta = io.beta;
-  m.inv_tau = 1.f / io.tau;
+  m.c2 = a.c2;
   m.part = a.part;
   m.lists_t = lists_t;
   m.lists_s = lists_s;
