@@ -48,6 +48,24 @@ def test_bf16_round_agrees_with_bit_route_on_float32_values():
     assert np.array_equal(O.bf16_round(x.astype(np.float64)), f32_rne_bits(x))
 
 
+def test_log1mexp_against_scalar_routes_and_its_branch_point():
+    """log(1 - e^a), the log of the mass outside a top-k set from the set's
+    log-mass a [Top-K KD, 一.2 binary term]: pinned per element to Python's
+    scalar math (log of -expm1 near 0, log1p of -exp far from it, each exact
+    to a few ulps where it is used), on both sides of the branch point
+    -log 2, at a = 0 (no mass outside: -inf) and at a tiny |a| where the
+    naive log(1 - exp(a)) loses every digit."""
+    a = np.concatenate([-np.logspace(-300, 3, 400), [-math.log(2.0) * (1 + 1e-15), -math.log(2.0),
+                                                       -math.log(2.0) * (1 - 1e-15), -1e-20]])
+    got = O.log1mexp(a)
+    for x, g in zip(a.tolist(), got.tolist()):
+        ref = math.log(-math.expm1(x)) if x > -0.5 else math.log1p(-math.exp(x))
+        assert abs(g - ref) <= 4e-16 * abs(ref), (x, g, ref)
+    assert O.log1mexp(np.array([0.0]))[0] == -np.inf
+    assert abs(O.log1mexp(np.array([-1e-20]))[0] - math.log(1e-20)) < 1e-12
+    assert 1.0 - math.exp(-1e-20) == 0.0  # the naive form has nothing left to take the log of
+
+
 def test_bf16_neighbours_bracket():
     g = np.random.default_rng(1)
     x = g.normal(0, 10, 10000)
