@@ -309,7 +309,7 @@ def check_tail_rows(out, h_s, W_s, h_t, W_t, rows, k, beta, tau, support, labels
     return exact, flagged
 
 
-def exact_shifted_case(seed, N, V, d, shift=100.0, head=0.0, n_head=8):
+def exact_shifted_case(seed, N, V, d, shift=100.0, head=0.0, n_head=8, teacher=False):
     """A case whose logits are exact in bf16 and whose student logits all lie
     past the range of exp in fp32: hidden units in {0, 1}, unembedding entries
     in {0, +-1/2}, and for the student a last hidden unit of ``shift`` against
@@ -323,7 +323,8 @@ def exact_shifted_case(seed, N, V, d, shift=100.0, head=0.0, n_head=8):
     With a nonzero ``head`` the first ``n_head`` vocabulary rows lead both
     models by ``head`` (a hidden unit of 1 against that column), so a top-k
     of ``n_head`` holds most of both masses and the binary term of the
-    top-k decomposition is near zero."""
+    top-k decomposition is near zero. With ``teacher`` the teacher's logits
+    are raised the same way instead of the student's."""
     g = np.random.default_rng(seed)
     vals = np.array([-0.5, 0.0, 0.5], np.float32)
     h_s = g.integers(0, 2, (N, d)).astype(np.float32)
@@ -335,8 +336,9 @@ def exact_shifted_case(seed, N, V, d, shift=100.0, head=0.0, n_head=8):
             h[:, -2] = 1.0
             W[:, -2] = 0.0
             W[:n_head, -2] = head
-    h_s[:, -1] = shift
-    W_s[:, -1] = 1.0
-    z = h_s @ W_s.T
+    h, W = (h_t, W_t) if teacher else (h_s, W_s)
+    h[:, -1] = shift
+    W[:, -1] = 1.0
+    z = h @ W.T
     assert z.min() > 89.0 and z.max() < 127.5, (z.min(), z.max())
     return tuple(kdsynth.f32_to_bf16_bits(x) for x in (h_s, W_s, h_t, W_t))

@@ -66,18 +66,20 @@ def test_tail_bwd_logits_past_exp_range(beta, support):
     _case(kd, torch, arrays, 8, beta, 1.5, support, None, np.arange(N), grad_seed=36)
 
 
+@pytest.mark.parametrize("teacher", [False, True])
 @pytest.mark.parametrize("head", [0.0, 14.0])
 @pytest.mark.parametrize("beta,support", [(0.5, T | S), (1.0, T)])
-def test_tail_keeps_precision_under_a_common_student_offset(beta, support, head):
-    """Student logits raised by 100 (an offset the softmax ignores): loss and
-    masses against the oracle to an absolute 4e-6, the precision of unshifted
-    logits. With ``head`` the support holds all but a few percent of both
-    masses. A bucket log-probability formed as a logit minus an fp32
+def test_tail_keeps_precision_under_a_common_offset(beta, support, head, teacher):
+    """One model's logits raised by 100 (an offset the softmax ignores): loss
+    and masses against the oracle to an absolute 4e-6, the precision of
+    unshifted logits. With ``head`` the support holds all but a few percent
+    of both masses. A bucket log-probability formed as a logit minus an fp32
     log-sum-exp near 67 (tau = 1.5) is good to only about 1e-5."""
     kd, torch = _kd()
     N, V, k, tau = 64, 3000, 8, 1.5
-    arrays = exact_shifted_case(33, N, V, 16, head=head)
-    print(f"tail shifted student logits head={head} beta={beta} support={support} N={N} V={V}", flush=True)
+    arrays = exact_shifted_case(33, N, V, 16, head=head, teacher=teacher)
+    who = "teacher" if teacher else "student"
+    print(f"tail shifted {who} logits head={head} beta={beta} support={support} N={N} V={V}", flush=True)
     dev = [to_dev(x) for x in arrays]
     out = kd.kd_tail_fwd(*dev, k, beta, tau, support)
     torch.cuda.synchronize()

@@ -154,9 +154,10 @@ def test_topk_bwd_logits_past_exp_range_without_ce(tau):
     _bwd_case(kd, torch, arrays, 8, tau, None, np.arange(N), seed=35)
 
 
+@pytest.mark.parametrize("teacher", [False, True])
 @pytest.mark.parametrize("head", [0.0, 14.0])
-def test_topk_terms_keep_precision_under_a_common_student_offset(head):
-    """Student logits raised by 100 (an offset the softmax ignores): the
+def test_topk_terms_keep_precision_under_a_common_offset(head, teacher):
+    """One model's logits raised by 100 (an offset the softmax ignores): the
     terms, the masses and the CE against the oracle to an absolute 4e-6, the
     precision of unshifted logits. With ``head`` the teacher's top-8 holds
     all but a few percent of both masses, so the binary term is near zero.
@@ -164,9 +165,10 @@ def test_topk_terms_keep_precision_under_a_common_student_offset(head):
     near 67 (tau = 1.5) is good to only about 1e-5 and fails this bound."""
     kd, torch = _kd()
     N, V, k, tau = 64, 3000, 8, 1.5
-    arrays = exact_shifted_case(31, N, V, 16, head=head)
+    arrays = exact_shifted_case(31, N, V, 16, head=head, teacher=teacher)
     labels = kdsynth.uniform_labels(9, N, V)
-    print(f"topk fwd shifted student logits head={head} N={N} V={V} k={k} tau={tau}", flush=True)
+    who = "teacher" if teacher else "student"
+    print(f"topk fwd shifted {who} logits head={head} N={N} V={V} k={k} tau={tau}", flush=True)
     out = _run(kd, torch, arrays, k, tau, labels)
     ref = O.kd_topk_fwd(*arrays, k, tau, labels=labels)
     assert np.array_equal(out["idx"].cpu().numpy(), ref["idx"])  # exact logits: no rounding ties
