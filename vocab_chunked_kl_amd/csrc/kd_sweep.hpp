@@ -16,7 +16,8 @@
 // instructions). While stage g is multiplied, the loads of stages g+1 ..
 // g+NBUF-2 are in flight and stage g+NBUF-1 is being issued; one barrier per
 // stage recycles the buffer read in the previous step. The stage sequence
-// (tile by tile: pair 1, then pair 2) runs on continuously through the ring.
+// (tile by tile: pair 1, then pair 2, each padded to whole turns of the ring)
+// runs on continuously through the ring.
 #pragma once
 
 #include <type_traits>
@@ -220,9 +221,16 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
 #pragma unroll
   for (int j = 0; j < F::kSub; ++j) colx[j] = ((2 * j + (lane >> 5)) ^ F::swz(r32)) * 16;
 
-  // stages per pair; the ring position carries over from run to run
-  const int ks1 = (p1.kbytes + RB - 1) / RB;
-  const int ks2 = kDual ? (p2.kbytes + RB - 1) / RB : 0;
+  // Stages per pair, rounded up to whole turns of the ring: the stages past a
+  // pair's K extent load nothing (every lane past the end writes zeros) and
+  // add exact zeros. So every pair starts at ring position 0 and the step
+  // loop has one shape. With a pair's start position and tail length known
+  // only at run time, the loop copies per start position were entered from
+  // several histories of outstanding loads, and the compiler, unable to tell
+  // which stage buffer those loads target, drained them all (vmcnt(0)) before
+  // the first fragment read of every ring turn in two of the three copies.
+  const int ks1 = ((p1.kbytes + RB - 1) / RB + NBUF - 1) / NBUF * NBUF;
+  const int ks2 = kDual ? ((p2.kbytes + RB - 1) / RB + NBUF - 1) / NBUF * NBUF : 0;
   if (a_tile_end <= a_tile_begin || ks1 == 0) return;
 
   // Load geometry: row group q (8 rows of 128 bytes) of the A tile is load
@@ -285,23 +293,11 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
                                             [&]() __attribute__((always_inline)) { issue(lds.b[(i + NBUF - 1) % NBUF]); });
     advance();
   };
-  // Run `ks` stages into `acc` starting at ring position `rot`: one unrolled
-  // copy of the loop per starting position, so buffer indices stay constant.
-  auto run = [&](floatx16(&acc)[MB][NB], int ks, int rot) __attribute__((always_inline)) {
-    static_for<0, NBUF>([&](auto R) __attribute__((always_inline)) {
-      constexpr int r = decltype(R)::value;
-      if (rot == r) {
-        int s = 0;
-        for (; s + NBUF <= ks; s += NBUF)
-          static_for<0, NBUF>([&](auto I) __attribute__((always_inline)) { step(acc, std::integral_constant<int, (r + I) % NBUF>{}); });
-        static_for<0, NBUF - 1>([&](auto I) __attribute__((always_inline)) {
-          if (s < ks) {
-            step(acc, std::integral_constant<int, (r + I) % NBUF>{});
-            ++s;
-          }
-        });
-      }
-    });
+  // Run `ks` stages (whole turns of the ring) into `acc`; buffer indices are
+  // compile-time constants.
+  auto run = [&](floatx16(&acc)[MB][NB], int ks) __attribute__((always_inline)) {
+    for (int s = 0; s < ks; s += NBUF)
+      static_for<0, NBUF>([&](auto I) __attribute__((always_inline)) { step(acc, I); });
   };
 
   floatx16 acc1[MB][NB], acc2[kDual ? MB : 1][kDual ? NB : 1];
@@ -313,31 +309,18 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
     issue(lds.b[I]);
     advance();
   });
-  // The epilogue also gets the stage buffer that the tile's last step read:
-  // no load targets it until the next step's barrier, so an epilogue may use
-  // it as scratch after a barrier of its own (other waves may still be
-  // reading their last fragments from it until then).
-  auto idle_stage = [&](int r) __attribute__((always_inline)) {
-    const int i = (r + NBUF - 1) % NBUF;
-    char* b = lds.b[0];
-    static_for<1, NBUF>([&](auto I) __attribute__((always_inline)) {
-      if (i == decltype(I)::value) b = lds.b[decltype(I)::value];
-    });
-    return b;
-  };
-  int rot = 0;
+  // The epilogue also gets the stage buffer that the tile's last step read
+  // (the ring's last): no load targets it until the next step's barrier, so
+  // an epilogue may use it as scratch after a barrier of its own (other waves
+  // may still be reading their last fragments from it until then).
   for (int tile = a_tile_begin; tile < a_tile_end; ++tile) {
-    run(acc1, ks1, rot);
-    rot = (rot + ks1) % NBUF;
+    run(acc1, ks1);
     if constexpr (kDual) {
-      if (ks2 > 0) {
-        run(acc2, ks2, rot);
-        rot = (rot + ks2) % NBUF;
-      }
-      epi(tile, acc1, acc2, idle_stage(rot));
+      if (ks2 > 0) run(acc2, ks2);
+      epi(tile, acc1, acc2, lds.b[NBUF - 1]);
       zero_acc(acc2);
     } else {
-      epi(tile, acc1, acc1, idle_stage(rot));
+      epi(tile, acc1, acc1, lds.b[NBUF - 1]);
     }
     zero_acc(acc1);
   }
