@@ -117,7 +117,7 @@ __device__ __forceinline__ void merge_record(float& ms, float& ls, float& mt, fl
 // Forward sweep. MODE: kModeFKL / kModeRKL (loss in one sweep), kModeLSE (only
 // the log-sum-exps, first JSD sweep), kModeJSD (mixture sums given the LSEs).
 // ---------------------------------------------------------------------------
-template <bool kBf16, int MODE, bool kSmall>
+template <bool kBf16, int MODE, bool kSmall, int kR2>
 __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
   constexpr int TM = kTileV, TN = kSmall ? kSmallT : kTileT, WM = kLogitWM, WN = kLogitWN;
   constexpr int NBUF = kSmall ? kSmallBuf : kLogitBuf;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
       }
     }
   };
-  sweep<kBf16, TM, TN, WM, WN, NBUF, kLogitRB, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<kBf16, TM, TN, WM, WN, NBUF, kLogitRB, true, kR2>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 
   // Lanes l and l ^ 32 hold the same tokens (other vocabulary rows).
 #pragma unroll
@@ -415,7 +415,7 @@ __device__ __forceinline__ void store_g16(char* G, int64_t ldg, int64_t n, int64
   }
 }
 
-template <bool kBf16, int MODE, bool kSmall>
+template <bool kBf16, int MODE, bool kSmall, int kR2>
 __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
   constexpr int TM = kTileV, TN = kSmall ? kSmallT : kTileT, WM = kLogitWM, WN = kLogitWN;
   constexpr int NBUF = kSmall ? kSmallBuf : kLogitBuf;
@@ -530,7 +530,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
       }
     }
   };
-  sweep<kBf16, TM, TN, WM, WN, NBUF, kLogitRB, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  sweep<kBf16, TM, TN, WM, WN, NBUF, kLogitRB, true, kR2>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 
   if (!fix) return;
   // Per token the block's sum of stored entries: lanes l and l ^ 32 hold the
@@ -1055,42 +1055,49 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const char* __restrict__
   }
 }
 
-template <bool kBf16>
-hipError_t launch_fwd_mode(int mode, bool small, dim3 grid, const LogitArgs& la, hipStream_t st) {
-  if (small) {
-    switch (mode) {
-      case kModeFKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeFKL, true>), grid, dim3(kLogitThreads), 0, st, la); break;
-      case kModeRKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeRKL, true>), grid, dim3(kLogitThreads), 0, st, la); break;
-      case kModeLSE: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeLSE, true>), grid, dim3(kLogitThreads), 0, st, la); break;
-      default: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeJSD, true>), grid, dim3(kLogitThreads), 0, st, la); break;
-    }
-  } else {
-    switch (mode) {
-      case kModeFKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeFKL, false>), grid, dim3(kLogitThreads), 0, st, la); break;
-      case kModeRKL: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeRKL, false>), grid, dim3(kLogitThreads), 0, st, la); break;
-      case kModeLSE: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeLSE, false>), grid, dim3(kLogitThreads), 0, st, la); break;
-      default: hipLaunchKernelGGL((fwd_kernel<kBf16, kModeJSD, false>), grid, dim3(kLogitThreads), 0, st, la); break;
-    }
+// One logit-sweep kernel: the 64-token tile, the fp32 tile, or the bf16 tile,
+// whose pair 2 starts at ring position 1 when pair 1 (d_s) leaves one stage
+// past whole turns of the ring (the 152k-vocabulary workloads' d_s = 1024
+// and 2560), and otherwise both pairs run whole turns (the same stages when
+// d_s fills whole turns; at most three more per tile when it leaves two:
+// with pair 2 starting at position 2, the compiler again drained the ring
+// at the head of pair 1's loop).
+#define KD_LAUNCH_LOGIT(KERNEL)                                                                                  \
+  template <bool kBf16, int MODE>                                                                                \
+  hipError_t launch_##KERNEL(bool small, int r2, dim3 grid, const LogitArgs& la, hipStream_t st) {             \
+    if (small)                                                                                                   \
+      hipLaunchKernelGGL((KERNEL<kBf16, MODE, true, -1>), grid, dim3(kLogitThreads), 0, st, la);                \
+    else if (kBf16 && r2 == 1)                                                                                   \
+      hipLaunchKernelGGL((KERNEL<kBf16, MODE, false, (kBf16 ? 1 : -1)>), grid, dim3(kLogitThreads), 0, st, la); \
+    else                                                                                                         \
+      hipLaunchKernelGGL((KERNEL<kBf16, MODE, false, -1>), grid, dim3(kLogitThreads), 0, st, la);               \
+    return hipGetLastError();                                                                                    \
   }
-  return hipGetLastError();
+KD_LAUNCH_LOGIT(fwd_kernel)
+KD_LAUNCH_LOGIT(bwdg_kernel)
+#undef KD_LAUNCH_LOGIT
+
+// Pair 2's start position in the ring of the logit sweeps when pair 1 runs
+// exactly its stages.
+int logit_r2(const Plan& p) { return sweep_r2(p.d_s * p.esz, kLogitRB, kLogitBuf); }
+
+template <bool kBf16>
+hipError_t launch_fwd_mode(int mode, bool small, int r2, dim3 grid, const LogitArgs& la, hipStream_t st) {
+  switch (mode) {
+    case kModeFKL: return launch_fwd_kernel<kBf16, kModeFKL>(small, r2, grid, la, st);
+    case kModeRKL: return launch_fwd_kernel<kBf16, kModeRKL>(small, r2, grid, la, st);
+    case kModeLSE: return launch_fwd_kernel<kBf16, kModeLSE>(small, r2, grid, la, st);
+    default: return launch_fwd_kernel<kBf16, kModeJSD>(small, r2, grid, la, st);
+  }
 }
 
 template <bool kBf16>
-hipError_t launch_bwdg_mode(int mode, bool small, dim3 grid, const LogitArgs& la, hipStream_t st) {
-  if (small) {
-    switch (mode) {
-      case kModeFKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeFKL, true>), grid, dim3(kLogitThreads), 0, st, la); break;
-      case kModeRKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeRKL, true>), grid, dim3(kLogitThreads), 0, st, la); break;
-      default: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeJSD, true>), grid, dim3(kLogitThreads), 0, st, la); break;
-    }
-  } else {
-    switch (mode) {
-      case kModeFKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeFKL, false>), grid, dim3(kLogitThreads), 0, st, la); break;
-      case kModeRKL: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeRKL, false>), grid, dim3(kLogitThreads), 0, st, la); break;
-      default: hipLaunchKernelGGL((bwdg_kernel<kBf16, kModeJSD, false>), grid, dim3(kLogitThreads), 0, st, la); break;
-    }
+hipError_t launch_bwdg_mode(int mode, bool small, int r2, dim3 grid, const LogitArgs& la, hipStream_t st) {
+  switch (mode) {
+    case kModeFKL: return launch_bwdg_kernel<kBf16, kModeFKL>(small, r2, grid, la, st);
+    case kModeRKL: return launch_bwdg_kernel<kBf16, kModeRKL>(small, r2, grid, la, st);
+    default: return launch_bwdg_kernel<kBf16, kModeJSD>(small, r2, grid, la, st);
   }
-  return hipGetLastError();
 }
 
 LogitArgs logit_args(const Plan& p, const void* h_s, const void* W_s, const void* h_t, const void* W_t, float tau,
@@ -1247,17 +1254,18 @@ hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
   la.part = static_cast<float*>(io.workspace);
   const dim3 grid(xcd_grid(p.n_tok_tiles * p.n_splits));
   const bool small = p.N <= kSmallT;  // one token tile either way; the 64-row tile has a deeper ring
+  const int r2 = logit_r2(p);
   hipError_t e;
   if (io.beta == 0.f || io.beta == 1.f) {
     const int mode = io.beta == 1.f ? kModeRKL : kModeFKL;
-    e = p.bf16 ? launch_fwd_mode<true>(mode, small, grid, la, st) : launch_fwd_mode<false>(mode, small, grid, la, st);
+    e = p.bf16 ? launch_fwd_mode<true>(mode, small, r2, grid, la, st) : launch_fwd_mode<false>(mode, small, r2, grid, la, st);
     if (e != hipSuccess) return e;
     return mode == kModeRKL
                ? launch_merge<kModeRKL>(la.part, p.n_splits, p.N, la.inv_tau, io.loss, io.lse_s, io.lse_t, io.aux, st)
                : launch_merge<kModeFKL>(la.part, p.n_splits, p.N, la.inv_tau, io.loss, io.lse_s, io.lse_t, io.aux, st);
   }
   // 0 < beta < 1: sweep 1 -> LSEs, sweep 2 -> mixture sums.
-  e = p.bf16 ? launch_fwd_mode<true>(kModeLSE, small, grid, la, st) : launch_fwd_mode<false>(kModeLSE, small, grid, la, st);
+  e = p.bf16 ? launch_fwd_mode<true>(kModeLSE, small, r2, grid, la, st) : launch_fwd_mode<false>(kModeLSE, small, r2, grid, la, st);
   if (e != hipSuccess) return e;
   e = launch_merge<kModeLSE>(la.part, p.n_splits, p.N, la.inv_tau, io.loss, io.lse_s, io.lse_t, io.aux, st);
   if (e != hipSuccess) return e;
@@ -1266,7 +1274,7 @@ hipError_t run_fwd(const Plan& p, const FwdIO& io, hipStream_t st) {
       kFwdFields * (size_t)p.n_splits * (size_t)p.N * sizeof(float), 256));
   lj.lse_s = io.lse_s;
   lj.lse_t = io.lse_t;
-  e = p.bf16 ? launch_fwd_mode<true>(kModeJSD, small, grid, lj, st) : launch_fwd_mode<false>(kModeJSD, small, grid, lj, st);
+  e = p.bf16 ? launch_fwd_mode<true>(kModeJSD, small, r2, grid, lj, st) : launch_fwd_mode<false>(kModeJSD, small, r2, grid, lj, st);
   if (e != hipSuccess) return e;
   return launch_merge<kModeJSD>(lj.part, p.n_splits, p.N, la.inv_tau, io.loss, io.lse_s, io.lse_t, io.aux, st);
 }
@@ -1295,6 +1303,7 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
   // way); not with dW_s, whose transposed gradient copy must also zero the
   // token columns 64..127 of the 128-padded token extent.
   const bool small = p.N <= kSmallT && io.dW == nullptr;
+  const int r2 = logit_r2(p);
   la.lse_s = io.lse_s;
   la.lse_t = io.lse_t;
   la.aux = io.aux;
@@ -1343,7 +1352,7 @@ hipError_t run_bwd(const Plan& p, const BwdIO& io, hipStream_t st) {
     la.n_splits = (ctiles + la.tiles_per_split - 1) / la.tiles_per_split;
     la.g_col0 = c0;
     const dim3 grid(xcd_grid(p.n_tok_tiles * la.n_splits));
-    e = p.bf16 ? launch_bwdg_mode<true>(mode, small, grid, la, st) : launch_bwdg_mode<false>(mode, small, grid, la, st);
+    e = p.bf16 ? launch_bwdg_mode<true>(mode, small, r2, grid, la, st) : launch_bwdg_mode<false>(mode, small, r2, grid, la, st);
     if (e != hipSuccess) return e;
     if (io.dh) {
       // dh_s (+)= G . W_s[chunk], with the chunk of W_s transposed to [d_s][chunk]

@@ -73,6 +73,10 @@ struct RowFmt {
   __device__ static __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 3); }
 };
 
+// Ring position at which pair 2 starts when pair 1 runs exactly its stages
+// (the kR2 argument of sweep, chosen on the host from K1 in bytes).
+__host__ __device__ constexpr int sweep_r2(int kbytes1, int rb, int nbuf) { return ((kbytes1 + rb - 1) / rb) % nbuf; }
+
 template <int TM, int TN, int RB = 128>
 struct Ring {
   static constexpr int kBytes = (TM + TN) * RB;
@@ -200,7 +204,11 @@ struct RingLds {
 // MFMA blocks, MB = TM / (32 WM), NB = TN / (32 WN).
 // kDual = false: one operand pair only (p2 is ignored, the epilogue gets acc1
 // twice and no second accumulator is allocated).
-template <bool kBf16, int TM, int TN, int WM, int WN, int NBUF, int RB, bool kDual, class Epi>
+// kR2 >= 0 (two pairs only): pair 1 runs exactly its ceil(K1 / RB) stages,
+// which the caller guarantees to be kR2 modulo NBUF (sweep_r2 above), and
+// pair 2 is padded so that a tile is whole turns of the ring; kR2 = -1 pads
+// each pair to whole turns.
+template <bool kBf16, int TM, int TN, int WM, int WN, int NBUF, int RB, bool kDual, int kR2 = -1, class Epi>
 __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, int64_t b_row0, int a_tile_begin,
                                       int a_tile_end, const RingLds<NBUF>& lds, Epi&& epi) {
   static_assert(NBUF >= 2 && NBUF <= 4, "ring of two to four stage buffers");
@@ -221,16 +229,20 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
 #pragma unroll
   for (int j = 0; j < F::kSub; ++j) colx[j] = ((2 * j + (lane >> 5)) ^ F::swz(r32)) * 16;
 
-  // Stages per pair, rounded up to whole turns of the ring: the stages past a
+  // Stages per pair. A tile is whole turns of the ring, so every tile starts
+  // at ring position 0, and each pair starts at a position fixed at compile
+  // time (0, and kR2 for pair 2) with a tail of fixed length: each copy of
+  // the step loop has one history of outstanding loads. The stages past a
   // pair's K extent load nothing (every lane past the end writes zeros) and
-  // add exact zeros. So every pair starts at ring position 0 and the step
-  // loop has one shape. With a pair's start position and tail length known
-  // only at run time, the loop copies per start position were entered from
-  // several histories of outstanding loads, and the compiler, unable to tell
-  // which stage buffer those loads target, drained them all (vmcnt(0)) before
-  // the first fragment read of every ring turn in two of the three copies.
-  const int ks1 = ((p1.kbytes + RB - 1) / RB + NBUF - 1) / NBUF * NBUF;
-  const int ks2 = kDual ? ((p2.kbytes + RB - 1) / RB + NBUF - 1) / NBUF * NBUF : 0;
+  // add exact zeros. (With start positions and tail lengths known only at run
+  // time, the loop copies per start position were entered from several such
+  // histories, and the compiler, unable to tell which stage buffer the loads
+  // target, drained them all (vmcnt(0)) before the first fragment read of
+  // every ring turn in two of the three copies.)
+  static_assert(kR2 < NBUF && (kR2 < 0 || kDual), "pair 2 start position");
+  const int n1 = (p1.kbytes + RB - 1) / RB, n2 = kDual ? (p2.kbytes + RB - 1) / RB : 0;
+  const int ks1 = kR2 < 0 ? (n1 + NBUF - 1) / NBUF * NBUF : n1;
+  const int ks2 = kR2 < 0 ? (n2 + NBUF - 1) / NBUF * NBUF : n2 + (NBUF - (n1 + n2) % NBUF) % NBUF;
   if (a_tile_end <= a_tile_begin || ks1 == 0) return;
 
   // Load geometry: row group q (8 rows of 128 bytes) of the A tile is load
@@ -293,12 +305,22 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
                                             [&]() __attribute__((always_inline)) { issue(lds.b[(i + NBUF - 1) % NBUF]); });
     advance();
   };
-  // Run `ks` stages (whole turns of the ring) into `acc`; buffer indices are
-  // compile-time constants.
-  auto run = [&](floatx16(&acc)[MB][NB], int ks) __attribute__((always_inline)) {
-    for (int s = 0; s < ks; s += NBUF)
-      static_for<0, NBUF>([&](auto I) __attribute__((always_inline)) { step(acc, I); });
+  // Run `ks` stages into `acc` from ring position R, ending with T single
+  // steps (ks = T modulo NBUF); buffer indices are compile-time constants.
+  auto run = [&](floatx16(&acc)[MB][NB], int ks, auto R, auto T) __attribute__((always_inline)) {
+    constexpr int r = decltype(R)::value, t = decltype(T)::value;
+    int s = 0;
+    for (; s + NBUF <= ks; s += NBUF)
+      static_for<0, NBUF>([&](auto I) __attribute__((always_inline)) {
+        step(acc, std::integral_constant<int, (r + I) % NBUF>{});
+      });
+    static_for<0, t>([&](auto I) __attribute__((always_inline)) {
+      step(acc, std::integral_constant<int, (r + I) % NBUF>{});
+    });
   };
+  using I0 = std::integral_constant<int, 0>;
+  using IR2 = std::integral_constant<int, (kR2 < 0 ? 0 : kR2)>;
+  using IT2 = std::integral_constant<int, (kR2 < 0 ? 0 : (NBUF - kR2) % NBUF)>;
 
   floatx16 acc1[MB][NB], acc2[kDual ? MB : 1][kDual ? NB : 1];
   zero_acc(acc1);
@@ -314,9 +336,9 @@ __device__ __forceinline__ void sweep(const PairDesc& p1, const PairDesc& p2, in
   // an epilogue may use it as scratch after a barrier of its own (other waves
   // may still be reading their last fragments from it until then).
   for (int tile = a_tile_begin; tile < a_tile_end; ++tile) {
-    run(acc1, ks1);
+    run(acc1, ks1, I0{}, IR2{});
     if constexpr (kDual) {
-      if (ks2 > 0) run(acc2, ks2);
+      if (ks2 > 0) run(acc2, ks2, IR2{}, IT2{});
       epi(tile, acc1, acc2, lds.b[NBUF - 1]);
       zero_acc(acc2);
     } else {
