@@ -101,8 +101,11 @@ typedef uint32_t u32x16 __attribute__((__vector_size__(16 * sizeof(uint32_t))));
 // is then the student) and the LSE partials are written back in the usual
 // field order. kTwo: rank both models at once, the teacher into lists and
 // the student into lists2 (smaller candidate buffers, more merge rounds).
+// kPt1st: contract the pt pair first, when its stages leave one over whole
+// turns of the stage ring (a rank-256 teacher: 4 stages), so that a tile
+// needs no padding stages; the epilogue still gets (z_s, z_t).
 // ---------------------------------------------------------------------------
-template <bool kSep1, bool kTwo>
+template <bool kSep1, bool kTwo, bool kPt1st>
 __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a) {
   constexpr int TM = kTileV, TN = kTopkT, WM = kTopkWM, WN = kTopkWN, NW = WM * WN;
   constexpr int MB = TM / (32 * WM), NB = TN / (32 * WN);
@@ -349,7 +352,11 @@ __global__ __launch_bounds__(kTopkThreads, 1) void topk_sweep_kernel(TopkArgs a)
       if (!any) break;
     }
   };
-  sweep<true, TM, TN, WM, WN, 3, 128, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
+  if constexpr (kPt1st)
+    sweep<true, TM, TN, WM, WN, 3, 128, true, 1>(a.pt, a.ps, (int64_t)tt * TN, vt0, vt1, lds,
+                                                 [&](int vt, auto& z1, auto& z2, char* idle) { epi(vt, z2, z1, idle); });
+  else
+    sweep<true, TM, TN, WM, WN, 3, 128, true>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
   // the ring is drained: its first buffer holds the cross-wave LSE records
   float* red = reinterpret_cast<float*>(lds.b[0]);
   static_assert((WM - 1) * kTopkFields * TN * sizeof(float) <= Ring<TM, TN>::kBytes, "records fit one stage");
@@ -760,6 +767,17 @@ size_t topk_workspace_bytes(const Plan& p, int32_t k) {
          align_up((size_t)n_splits * p.N * k * sizeof(uint32_t), 256);
 }
 
+// The top-k sweep with the pt pair contracted first when that saves the
+// ring's padding stages (see topk_sweep_kernel).
+template <bool kSep1, bool kTwo>
+static hipError_t launch_topk_sweep(dim3 grid, const TopkArgs& a, hipStream_t st) {
+  if (sweep_r2(a.pt.kbytes, 128, 3) == 1)
+    hipLaunchKernelGGL((topk_sweep_kernel<kSep1, kTwo, true>), grid, dim3(kTopkThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((topk_sweep_kernel<kSep1, kTwo, false>), grid, dim3(kTopkThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
   TopkArgs a{};
   a.ps = PairDesc{static_cast<const char*>(io.W_s), static_cast<const char*>(io.h_s), (int64_t)p.d_s * 2,
@@ -781,11 +799,7 @@ hipError_t run_topk(const Plan& p, const TopkIO& io, hipStream_t st) {
                                         align_up((size_t)kTopkFields * a.n_splits * p.N * sizeof(float), 256));
   const bool sep1 = (io.labels != nullptr || io.lse_s1 != nullptr) && io.tau != 1.f;
   const dim3 grid(xcd_grid(a.n_tok_tiles * a.n_splits));
-  if (sep1)
-    hipLaunchKernelGGL((topk_sweep_kernel<true, false>), grid, dim3(kTopkThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL((topk_sweep_kernel<false, false>), grid, dim3(kTopkThreads), 0, st, a);
-  hipError_t e = hipGetLastError();
+  hipError_t e = sep1 ? launch_topk_sweep<true, false>(grid, a, st) : launch_topk_sweep<false, false>(grid, a, st);
   if (e != hipSuccess) return e;
   MergeArgs m{};
   m.h_s = static_cast<const uint16_t*>(io.h_s);
@@ -852,22 +866,22 @@ hipError_t run_tail(const Plan& p, const TailIO& io, hipStream_t st) {
   // one sweep: the teacher's list, the student's (the same sweep with the
   // two operand pairs exchanged) or both at once
   const bool rank_t = io.support & KD_SUPPORT_TEACHER, rank_s = io.support & KD_SUPPORT_STUDENT;
+  hipError_t e;
   if (rank_t && rank_s) {
     a.lists = lists_t;
     a.lists2 = lists_s;
-    hipLaunchKernelGGL((topk_sweep_kernel<false, true>), grid, dim3(kTopkThreads), 0, st, a);
+    e = launch_topk_sweep<false, true>(grid, a, st);
   } else if (rank_t) {
     a.lists = lists_t;
-    hipLaunchKernelGGL((topk_sweep_kernel<false, false>), grid, dim3(kTopkThreads), 0, st, a);
+    e = launch_topk_sweep<false, false>(grid, a, st);
   } else {
     TopkArgs b = a;
     b.ps = a.pt;
     b.pt = a.ps;
     b.swap = 1;
     b.lists = lists_s;
-    hipLaunchKernelGGL((topk_sweep_kernel<false, false>), grid, dim3(kTopkThreads), 0, st, b);
+    e = launch_topk_sweep<false, false>(grid, b, st);
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   TailArgs m{};
   m.h_s = static_cast<const uint16_t*>(io.h_s);
