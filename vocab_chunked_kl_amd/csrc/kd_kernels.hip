@@ -151,9 +151,14 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
   }
   const float beta = a.beta, omb = 1.f - a.beta;
 
-  auto epi = [&](int vt, auto& zs, auto& zt, char*) {
-    const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
-    const bool full = (int64_t)(vt + 1) * TM <= a.V;
+  // Epilogue of one vocabulary tile. Every tile but the vocabulary's last is
+  // whole, and its copy of the epilogue (kFull) carries no row test: a test
+  // per element (index, 64-bit compare, select) cost more instructions than
+  // the arithmetic it guards.
+  auto epi_tile = [&](auto kFull, int64_t vrow0, auto& zs, auto& zt) __attribute__((always_inline)) {
+    constexpr bool full = decltype(kFull)::value;
+    // rows of this wave's slice below V, relative to its first row (kFull: all)
+    const int vlim = full ? TM : (int)max<int64_t>(0, min<int64_t>(a.V - vrow0, TM));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       if constexpr (MODE == kModeJSD) {
@@ -162,7 +167,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const bool ok = full || (vrow0 + mb * 32 + acc_row(r, lane) < a.V);
+            const bool ok = full || (mb * 32 + acc_row(r, lane) < vlim);
             const float lq2 = fmaf(zs[mb][nb][r], c2, -Ls2[nb]);
             const float lp2 = fmaf(zt[mb][nb][r], c2, -Lt2[nb]);
             const float q = fast_exp2(lq2), p = fast_exp2(lp2);
@@ -182,8 +187,7 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const bool ok = full || (vrow0 + mb * 32 + acc_row(r, lane) < a.V);
-            if (ok) {
+            if (full || (mb * 32 + acc_row(r, lane) < vlim)) {
               mxs = fmaxf(mxs, zs[mb][nb][r]);
               mxt = fmaxf(mxt, zt[mb][nb][r]);
             }
@@ -198,11 +202,10 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const bool ok = full || (vrow0 + mb * 32 + acc_row(r, lane) < a.V);
             const float x = zs[mb][nb][r], y = zt[mb][nb][r];
             float es = fast_exp2(fmaf(x, c2, -ms_new));
             float et = fast_exp2(fmaf(y, c2, -mt_new));
-            if (!ok) es = et = 0.f;
+            if (!full && !(mb * 32 + acc_row(r, lane) < vlim)) es = et = 0.f;
             sl += es;
             tl += et;
             if (MODE == kModeRKL) sa = fmaf(es, x - y, sa);
@@ -216,6 +219,13 @@ __global__ __launch_bounds__(kLogitThreads, 1) void fwd_kernel(LogitArgs a) {
         mt[nb] = mt_new;
       }
     }
+  };
+  auto epi = [&](int vt, auto& zs, auto& zt, char*) {
+    const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
+    if ((int64_t)(vt + 1) * TM <= a.V)
+      epi_tile(std::true_type{}, vrow0, zs, zt);
+    else
+      epi_tile(std::false_type{}, vrow0, zs, zt);
   };
   sweep<kBf16, TM, TN, WM, WN, NBUF, kLogitRB, true, kR2>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 
@@ -415,7 +425,9 @@ __device__ __forceinline__ void store_g16(char* G, int64_t ldg, int64_t n, int64
   }
 }
 
-template <bool kBf16, int MODE, bool kSmall, int kR2>
+// kGT: also write the chunk transposed (a.GT, for dW_s); a compile-time
+// switch, so the loss-gradient-only kernel carries none of that code.
+template <bool kBf16, int MODE, bool kSmall, int kR2, bool kGT>
 __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
   constexpr int TM = kTileV, TN = kSmall ? kSmallT : kTileT, WM = kLogitWM, WN = kLogitWN;
   constexpr int NBUF = kSmall ? kSmallBuf : kLogitBuf;
@@ -452,8 +464,23 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
   for (int nb = 0; nb < NB; ++nb) es[nb] = 0.f;
   const bool fix = a.esum != nullptr;
 
+  // One vocabulary tile. The epilogue has no per-element row test: in the
+  // vocabulary's last tile, the rows past V (read as zeros) first get both
+  // logits set to -1e30, so that q = p = 0 there and every gradient formula
+  // below gives exactly 0 (and none passes the dominant-entry test). A second,
+  // test-free copy of the epilogue for whole tiles spilled registers.
   auto epi = [&](int vt, auto& zs, auto& zt, char*) {
     const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
+    if ((int64_t)(vt + 1) * TM > a.V) {
+      const int vlim = (int)max<int64_t>(0, min<int64_t>(a.V - vrow0, TM));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (mb * 32 + acc_row(r, lane) >= vlim) zs[mb][nb][r] = zt[mb][nb][r] = -1e30f;
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int64_t n = tok0 + nb * 32 + (lane & 31);
@@ -471,7 +498,6 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = rg * 4 + e;
-              const int64_t v = vrow0 + mb * 32 + acc_row(r, lane);
               const float x = zs[mb][nb][r], y = zt[mb][nb][r];
               const float lq2 = fmaf(x, c2, -Ls2[nb]);
               lqmax = fmaxf(lqmax, lq2);
@@ -486,9 +512,9 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
                 const float m = beta * fast_exp2(lp2) + omb * q;
                 g = (m > 1e-37f) ? omb * q * fmaf(lq2 - fast_log2(m), kLn2, -K1[nb]) : 0.f;
               }
-              g4[e] = (v < a.V) ? g * gsc[nb] : 0.f;
+              g4[e] = g * gsc[nb];
             }
-            if (a.GT && n < a.Np) {
+            if (kGT && n < a.Np) {
               // transposed copy for the weight gradient: token-contiguous rows;
               // tokens past N carry g = 0, so the padding columns are zeros
 #pragma unroll
@@ -524,12 +550,13 @@ __global__ __launch_bounds__(kLogitThreads, 1) void bwdg_kernel(LogitArgs a) {
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int64_t v = vrow0 + mb * 32 + acc_row(r, lane);
-            if (v < a.V && n < a.N && fmaf(zs[mb][nb][r], c2, -Ls2[nb]) > kBigLq2) a.big[n] = (int32_t)v;
+            if (n < a.N && fmaf(zs[mb][nb][r], c2, -Ls2[nb]) > kBigLq2)
+              a.big[n] = (int32_t)(vrow0 + mb * 32 + acc_row(r, lane));
           }
       }
     }
   };
+
   sweep<kBf16, TM, TN, WM, WN, NBUF, kLogitRB, true, kR2>(a.ps, a.pt, (int64_t)tt * TN, vt0, vt1, lds, epi);
 
   if (!fix) return;
@@ -1074,8 +1101,24 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const char* __restrict__
     return hipGetLastError();                                                                                    \
   }
 KD_LAUNCH_LOGIT(fwd_kernel)
-KD_LAUNCH_LOGIT(bwdg_kernel)
 #undef KD_LAUNCH_LOGIT
+
+template <bool kBf16, int MODE, bool kGT>
+hipError_t launch_bwdg_gt(bool small, int r2, dim3 grid, const LogitArgs& la, hipStream_t st) {
+  if (small)
+    hipLaunchKernelGGL((bwdg_kernel<kBf16, MODE, true, -1, kGT>), grid, dim3(kLogitThreads), 0, st, la);
+  else if (kBf16 && r2 == 1)
+    hipLaunchKernelGGL((bwdg_kernel<kBf16, MODE, false, (kBf16 ? 1 : -1), kGT>), grid, dim3(kLogitThreads), 0, st,
+                       la);
+  else
+    hipLaunchKernelGGL((bwdg_kernel<kBf16, MODE, false, -1, kGT>), grid, dim3(kLogitThreads), 0, st, la);
+  return hipGetLastError();
+}
+template <bool kBf16, int MODE>
+hipError_t launch_bwdg_kernel(bool small, int r2, dim3 grid, const LogitArgs& la, hipStream_t st) {
+  return la.GT ? launch_bwdg_gt<kBf16, MODE, true>(small, r2, grid, la, st)
+               : launch_bwdg_gt<kBf16, MODE, false>(small, r2, grid, la, st);
+}
 
 // Pair 2's start position in the ring of the logit sweeps when pair 1 runs
 // exactly its stages.
