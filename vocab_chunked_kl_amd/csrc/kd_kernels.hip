@@ -857,8 +857,20 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_g_kernel(DenseArgs a) 
       }
     }
   }
+  // No per-element row test: in the vocabulary's last tile the rows past V
+  // get the logit -1e30 first, so that q = r = 0 and G = 0 there.
   auto epi = [&](int vt, auto& zs, auto&, char*) {
     const int64_t vrow0 = (int64_t)vt * TM + wm * (TM / WM);
+    if ((int64_t)(vt + 1) * TM > a.V) {
+      const int vlim = (int)max<int64_t>(0, min<int64_t>(a.V - vrow0, TM));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (mb * 32 + acc_row(r, lane) >= vlim) zs[mb][nb][r] = -1e30f;
+    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int64_t n = tok0 + nb * 32 + (lane & 31);
@@ -873,11 +885,10 @@ __global__ __launch_bounds__(kDenseThreads, 1) void dense_g_kernel(DenseArgs a) 
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = (2 * pr + h) * 4 + e;
-              const int64_t v = vrow0 + mb * 32 + acc_row(r, lane);
               const float zb = __builtin_bit_cast(float, f32_to_bf16_bits(zs[mb][nb][r]) << 16);
               const float q = fast_exp2(fmaf(zb, a.c2, -Ls2[nb]));
               const float rr = kR ? fast_exp2(fmaf(zb, kLog2e, -L12[nb])) : q;
-              g4[e] = (v < a.V) ? fmaf(A[nb], q, C[nb] * rr) : 0.f;
+              g4[e] = fmaf(A[nb], q, C[nb] * rr);
             }
             w2[h].x = pack_bf16x2(g4[0], g4[1]);
             w2[h].y = pack_bf16x2(g4[2], g4[3]);
