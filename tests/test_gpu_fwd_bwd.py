@@ -101,6 +101,25 @@ def test_degenerate_shapes(N, V):
         run_case(kd, torch, arrays, beta, 1.0, chunk_V=256)
 
 
+@pytest.mark.parametrize("V", [257, 320, 321])
+def test_dominant_entry_on_the_last_vocabulary_row(V):
+    """The student's dominant entry (q near 1, the zero-sum path of the
+    backward) on the vocabulary's last row, inside the last 256-row tile, whose
+    rows past V the gradient sweep neutralises (each wave holds a 64-row
+    slice): V = 257 puts it alone at the start of the first slice, V = 320 at
+    the end of a full slice with every later slice past V, V = 321 alone at
+    the start of the second slice. Every row against the oracle, each beta."""
+    kd, torch = _kd()
+    h_s, W_s, h_t, W_t = kdsynth.small_case(23, 130, V, 32, 48, dtype="f32")
+    h_s[:, 0] = 4.0           # a hidden unit shared by every token
+    W_s[V - 1, :] = 0.0
+    W_s[V - 1, 0] = 5.0       # z_s = 20 on the last row for every token
+    arrays = tuple(kdsynth.f32_to_bf16_bits(x) for x in (h_s, W_s, h_t, W_t))
+    for beta in (0.0, 0.5, 1.0):
+        _say(f"dominant last row N=130 V={V} beta={beta}")
+        run_case(kd, torch, arrays, beta, 1.0, chunk_V=256)
+
+
 @pytest.mark.parametrize("beta", [0.0, 0.5, 1.0])
 def test_student_logits_offset_by_100(beta):
     """Student logits exact in bf16 and all near 100 (a hidden unit of 100
